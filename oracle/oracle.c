@@ -1,0 +1,330 @@
+/*
+ * Plain CPU oracle for the packed-weight product path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg load this library.  The HIP product path
+ * never includes, links or calls it, and it shares no source with that path.
+ *
+ * Every result is the plain definition written out in double precision from
+ * the f32 / int8 / binary16 inputs: no blocking, no fusion, no reordering
+ * beyond what the definition states.  The one exception is the f32 router
+ * logit (oracle_router_logits_f32): an f32 value that decides an integer (the
+ * chosen experts) is computed in f32, in the summation order the device uses,
+ * so both sides take that decision on identical bits.
+ *
+ * Sources (cortiq-engine docs.rs source pages):
+ *  - weights stay packed on the device and are decoded inside the product:
+ *    embryo_wide.wgsl (0.8.53), header comment;
+ *  - residual add + RMSNorm per position: nemotron_prefill.rs (0.8.50),
+ *    `pb_add_rms`; gemma_batch.rs (0.8.82), `g4_add_norm_b`;
+ *  - relu^2 activation on the finished product: nemotron_prefill.rs,
+ *    `pb_relu2` and the `act == 1` branch of `pb_q8_bank`;
+ *  - router, top-k selection (lower expert id wins an exact tie), per-expert
+ *    lists in ascending entry order: nemotron_prefill.rs, `pb_f32_mm`,
+ *    `pb_route`, `pb_lists`;
+ *  - routed expert FFN and the slot-ordered weighted sum into the residual:
+ *    nemotron_prefill.rs, `pb_q8_bank` and `pb_add_rms` (add == 2).
+ *
+ * The int8 block format (32 consecutive columns of a row share one f32 scale
+ * and one f32 bias, w = scale*q + bias) is this library's weight format; the
+ * pages' own q8_2f format (int8 body, f16 row scales, f16 column field) is a
+ * different encoding of the same idea.
+ *
+ * Parity status: every function here is pinned by the CPU test suite (closed
+ * forms, invariants, brute force, textbook routines); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define BLOCK 32
+
+/* ------------------------------------------------------------ binary16 */
+
+/* IEEE 754 binary16 decode: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+double oracle_f16_to_f64(uint16_t bits) {
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 31;
+    int m = bits & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);              /* subnormal: (m/1024) * 2^-14 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp(1024.0 + (double)m, e - 25);  /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------ dequant */
+
+static inline double q8_weight(const int8_t *q, const float *scale, const float *bias,
+                               int64_t cols, int64_t r, int64_t c) {
+    int64_t b = r * (cols / BLOCK) + c / BLOCK;
+    return (double)scale[b] * (double)q[r * cols + c] + (double)bias[b];
+}
+
+/* w[r][c] = scale[r][c/32] * q[r][c] + bias[r][c/32] */
+void oracle_dequant_q8(const int8_t *q, const float *scale, const float *bias,
+                       int64_t rows, int64_t cols, double *w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            w[r * cols + c] = q8_weight(q, scale, bias, cols, r, c);
+}
+
+static inline double act_apply(int act, double v) {
+    if (act == 1) {              /* relu^2: max(v, 0)^2 */
+        double t = v > 0.0 ? v : 0.0;
+        return t * t;
+    }
+    return v;
+}
+
+/* ------------------------------------------------------------ products */
+
+/* Y[b][r] = act( sum_c w[r][c] * X[b][c] ),  X [n][cols] f32, Y [n][rows] f64. */
+void oracle_gemm_q8(const int8_t *q, const float *scale, const float *bias,
+                    int64_t rows, int64_t cols, const float *X, int64_t n, int act,
+                    double *Y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * rows; ++i) {
+        int64_t b = i / rows, r = i % rows;
+        double acc = 0.0;
+        for (int64_t c = 0; c < cols; ++c)
+            acc += q8_weight(q, scale, bias, cols, r, c) * (double)X[b * cols + c];
+        Y[b * rows + r] = act_apply(act, acc);
+    }
+}
+
+/* Same product over a subset of output rows (for sampled checks of large
+ * matrices): Y[b][j] = act( sum_c w[row_idx[j]][c] * X[b][c] ). */
+void oracle_gemm_q8_rows(const int8_t *q, const float *scale, const float *bias,
+                         int64_t rows, int64_t cols, const int64_t *row_idx, int64_t nrows,
+                         const float *X, int64_t n, int act, double *Y) {
+    (void)rows;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * nrows; ++i) {
+        int64_t b = i / nrows, j = i % nrows, r = row_idx[j];
+        double acc = 0.0;
+        for (int64_t c = 0; c < cols; ++c)
+            acc += q8_weight(q, scale, bias, cols, r, c) * (double)X[b * cols + c];
+        Y[b * nrows + j] = act_apply(act, acc);
+    }
+}
+
+/* Y[b][r] = act( sum_c f16(W[r][c]) * X[b][c] ),  W as binary16 bits. */
+void oracle_gemm_f16(const uint16_t *W, int64_t rows, int64_t cols, const float *X,
+                     int64_t n, int act, double *Y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * rows; ++i) {
+        int64_t b = i / rows, r = i % rows;
+        double acc = 0.0;
+        for (int64_t c = 0; c < cols; ++c)
+            acc += oracle_f16_to_f64(W[r * cols + c]) * (double)X[b * cols + c];
+        Y[b * rows + r] = act_apply(act, acc);
+    }
+}
+
+/* ------------------------------------------------------------ add + RMSNorm */
+
+/* Per position b:  h'[i] = h[b][i] + delta[b*delta_stride + i]   (no add if delta is NULL)
+ *                  out[b][i] = w[i] * h'[i] / sqrt( (1/H) sum_i h'[i]^2 + eps ).
+ * h_out receives h'; both outputs in f64. */
+void oracle_add_rmsnorm(const float *h, const float *delta, int64_t delta_stride,
+                        const float *w, double eps, int64_t hidden, int64_t n,
+                        double *h_out, double *out) {
+    for (int64_t b = 0; b < n; ++b) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < hidden; ++i) {
+            double v = (double)h[b * hidden + i];
+            if (delta) v += (double)delta[b * delta_stride + i];
+            h_out[b * hidden + i] = v;
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)hidden + eps);
+        for (int64_t i = 0; i < hidden; ++i)
+            out[b * hidden + i] = (double)w[i] * h_out[b * hidden + i] * inv;
+    }
+}
+
+/* ------------------------------------------------------------ router */
+
+/* logits[b][e] = sum_c X[b][c] * Wr[e][c], in f64. */
+void oracle_router_logits_f64(const float *X, const float *Wr, int64_t n, int64_t H,
+                              int64_t E, double *logits) {
+    for (int64_t b = 0; b < n; ++b)
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < H; ++c)
+                acc += (double)X[b * H + c] * (double)Wr[e * H + c];
+            logits[b * E + e] = acc;
+        }
+}
+
+/* The same logit as an f32 value, summed in the order the device uses, so that
+ * the expert choice (an integer decided by f32 compares) is taken on the same
+ * bits on both sides.  Order: the row is cut into 4-column groups g; 64 partial
+ * sums p[l] each chain a single-rounding fused multiply-add over the groups
+ * g = l, l+64, l+128, ... and, inside a group, over its 4 columns in order;
+ * the 64 partials then fold pairwise, for s = 32, 16, 8, 4, 2, 1:
+ * p[l] = p[l] + p[l+s] for l < s.  The logit is p[0].  Requires H % 4 == 0. */
+void oracle_router_logits_f32(const float *X, const float *Wr, int64_t n, int64_t H,
+                              int64_t E, float *logits) {
+    int64_t groups = H / 4;
+    for (int64_t b = 0; b < n; ++b)
+        for (int64_t e = 0; e < E; ++e) {
+            float p[64];
+            for (int l = 0; l < 64; ++l) {
+                float acc = 0.0f;
+                for (int64_t g = l; g < groups; g += 64)
+                    for (int t = 0; t < 4; ++t)
+                        acc = fmaf(Wr[e * H + 4 * g + t], X[b * H + 4 * g + t], acc);
+                p[l] = acc;
+            }
+            for (int s = 32; s >= 1; s >>= 1)
+                for (int l = 0; l < s; ++l)
+                    p[l] = p[l] + p[l + s];
+            logits[b * E + e] = p[0];
+        }
+}
+
+/* Softmax over all E experts and top-k selection for each position.
+ * Selection follows the page's router: k rounds; each round takes the largest
+ * remaining score, the lower expert index winning an exact tie, then removes it.
+ * The score ranked is the f32 logit (softmax is strictly increasing in it, and
+ * ranking the logit avoids ties that rounding of probabilities would create).
+ * probs[b][e] = exp(l_e - max) / sum_e' exp(l_e' - max) in f64;
+ * rw[b][t] = probs[b][sel[b][t]], divided by sum_t probs[b][sel[b][t]] if renorm. */
+void oracle_route(const float *logits, int64_t n, int64_t E, int64_t k, int renorm,
+                  int32_t *sel, double *rw, double *probs) {
+    char *taken = (char *)malloc((size_t)E);
+    for (int64_t b = 0; b < n; ++b) {
+        const float *l = logits + b * E;
+        double mx = -INFINITY;
+        for (int64_t e = 0; e < E; ++e)
+            if ((double)l[e] > mx) mx = (double)l[e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; ++e) z += exp((double)l[e] - mx);
+        for (int64_t e = 0; e < E; ++e) probs[b * E + e] = exp((double)l[e] - mx) / z;
+
+        memset(taken, 0, (size_t)E);
+        double sum = 0.0;
+        for (int64_t t = 0; t < k; ++t) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;   /* strict: lower index keeps a tie */
+            }
+            taken[best] = 1;
+            sel[b * k + t] = (int32_t)best;
+            rw[b * k + t] = probs[b * E + best];
+            sum += probs[b * E + best];
+        }
+        if (renorm)
+            for (int64_t t = 0; t < k; ++t) rw[b * k + t] /= sum;
+    }
+    free(taken);
+}
+
+/* Per expert e, the entries j = b*k + t (ascending) whose selection is e.
+ * lists is [E][cap]; counts[e] = number of entries; entries past counts[e] are
+ * left untouched. */
+void oracle_group(const int32_t *sel, int64_t n, int64_t k, int64_t E, int64_t cap,
+                  int32_t *counts, int32_t *lists) {
+    for (int64_t e = 0; e < E; ++e) {
+        int32_t c = 0;
+        for (int64_t j = 0; j < n * k; ++j)
+            if (sel[j] == e) lists[e * cap + c++] = (int32_t)j;
+        counts[e] = c;
+    }
+}
+
+/* ------------------------------------------------------------ routed experts */
+
+/* One (position, slot) pair j = b*k + t with expert e = sel[j]:
+ *   u_j = relu^2( Up_e . X[b] )      [I]
+ *   d_j = Down_e . u_j               [H]
+ * Banks: up q [E][I][H], scale/bias [E][I][H/32]; down q [E][H][I], scale/bias [E][H][I/32]. */
+static void expert_pair(const float *X, int64_t H, int64_t I, int64_t b, int64_t e,
+                        const int8_t *up_q, const float *up_s, const float *up_b,
+                        const int8_t *dn_q, const float *dn_s, const float *dn_b,
+                        double *u, double *d) {
+    const int8_t *uq = up_q + e * I * H;
+    const float *us = up_s + e * I * (H / BLOCK), *ub = up_b + e * I * (H / BLOCK);
+    for (int64_t r = 0; r < I; ++r) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < H; ++c)
+            acc += q8_weight(uq, us, ub, H, r, c) * (double)X[b * H + c];
+        u[r] = act_apply(1, acc);
+    }
+    const int8_t *dq = dn_q + e * H * I;
+    const float *ds = dn_s + e * H * (I / BLOCK), *db = dn_b + e * H * (I / BLOCK);
+    for (int64_t r = 0; r < H; ++r) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < I; ++c)
+            acc += q8_weight(dq, ds, db, I, r, c) * u[c];
+        d[r] = acc;
+    }
+}
+
+/* Ungrouped: loop over the pairs in entry order.  U [n*k][I], D [n*k][H]. */
+void oracle_moe_experts_ungrouped(const float *X, int64_t n, int64_t H, int64_t I,
+                                  const int32_t *sel, int64_t k,
+                                  const int8_t *up_q, const float *up_s, const float *up_b,
+                                  const int8_t *dn_q, const float *dn_s, const float *dn_b,
+                                  double *U, double *D) {
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t j = 0; j < n * k; ++j)
+        expert_pair(X, H, I, j / k, sel[j], up_q, up_s, up_b, dn_q, dn_s, dn_b,
+                    U + j * I, D + j * H);
+}
+
+/* Grouped: loop over experts, and for each over its list of entries (the
+ * expert-major walk of the device).  Per pair the arithmetic is the ungrouped
+ * one, so both walks give the same bits. */
+void oracle_moe_experts_grouped(const float *X, int64_t n, int64_t H, int64_t I,
+                                int64_t E, int64_t k, const int32_t *counts,
+                                const int32_t *lists, int64_t cap,
+                                const int8_t *up_q, const float *up_s, const float *up_b,
+                                const int8_t *dn_q, const float *dn_s, const float *dn_b,
+                                double *U, double *D) {
+    (void)n;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t i = 0; i < counts[e]; ++i) {
+            int64_t j = lists[e * cap + i];
+            expert_pair(X, H, I, j / k, e, up_q, up_s, up_b, dn_q, dn_s, dn_b,
+                        U + j * I, D + j * H);
+        }
+}
+
+/* Combine into the residual and norm, per position b:
+ *   m[i] = sum_{t=0..k-1} rw[b][t] * D[b*k+t][i]   (slot order)
+ *   h'   = h[b] + m;   out[b] = w * h' / sqrt(mean(h'^2) + eps). */
+void oracle_moe_combine(const float *h, const double *D, const double *rw, int64_t n,
+                        int64_t k, int64_t H, const float *w, double eps,
+                        double *h_out, double *out) {
+    for (int64_t b = 0; b < n; ++b) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < H; ++i) {
+            double m = 0.0;
+            for (int64_t t = 0; t < k; ++t) m += rw[b * k + t] * D[(b * k + t) * H + i];
+            double v = (double)h[b * H + i] + m;
+            h_out[b * H + i] = v;
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t i = 0; i < H; ++i) out[b * H + i] = (double)w[i] * h_out[b * H + i] * inv;
+    }
+}
+
+/* Thread count the OpenMP loops above run with (1 when built without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

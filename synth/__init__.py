@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs shared by the HIP path's tests/benchmark and the CPU oracle.
+
+This module only draws numbers: it holds none of the products, norms or
+routing arithmetic.  Every tensor is drawn on the host with numpy's PCG64
+generators spawned from one ``SeedSequence``, in a fixed order per workload,
+so the GPU and the oracle see the same bytes.
+
+Distributions (the workloads' statement of their inputs):
+  * packed int8 weights: q uniform on the integers [-127, 127], in blocks of
+    32 consecutive columns of a row; each block has an f32 scale ~ U(1e-3, 1e-2)
+    and an f32 bias ~ N(0, 1e-3);
+  * f16 weights: N(0, 0.02) rounded to binary16 (the f16 bits are the input);
+  * activations and residuals: N(0, 1) f32;
+  * RMSNorm weights: U(0.5, 1.5) f32, eps = 1e-6;
+  * router weights: N(0, 0.02) f32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+BLOCK = 32
+EPS = 1e-6
+
+
+def streams(seed: int, count: int) -> list[np.random.Generator]:
+    """``count`` independent generators spawned from ``SeedSequence(seed)``."""
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(count)]
+
+
+@dataclass
+class Q8:
+    """A packed int8 matrix: q [rows][cols] int8, scale/bias [rows][cols/32] f32."""
+
+    q: np.ndarray
+    scale: np.ndarray
+    bias: np.ndarray
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[-2]
+
+    @property
+    def cols(self) -> int:
+        return self.q.shape[-1]
+
+    def nbytes(self) -> int:
+        return self.q.nbytes + self.scale.nbytes + self.bias.nbytes
+
+
+def q8(rng: np.random.Generator, rows: int, cols: int, lead: tuple = ()) -> Q8:
+    """Draw a q8 matrix (or a stack of them with leading shape ``lead``)."""
+    assert cols % BLOCK == 0
+    q = rng.integers(-127, 128, size=lead + (rows, cols), dtype=np.int8)
+    scale = rng.uniform(1e-3, 1e-2, size=lead + (rows, cols // BLOCK)).astype(np.float32)
+    bias = rng.normal(0.0, 1e-3, size=lead + (rows, cols // BLOCK)).astype(np.float32)
+    return Q8(q, scale, bias)
+
+
+def f16(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
+    """N(0, 0.02) weights rounded to binary16 (round to nearest even)."""
+    return rng.normal(0.0, 0.02, size=(rows, cols)).astype(np.float16)
+
+
+def normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def norm_weight(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.uniform(0.5, 1.5, size=n).astype(np.float32)
+
+
+def router_weight(rng: np.random.Generator, experts: int, hidden: int) -> np.ndarray:
+    return rng.normal(0.0, 0.02, size=(experts, hidden)).astype(np.float32)
+
+
+# ---------------------------------------------------------------- workloads
+# Each builder draws its tensors in the order written, one spawned stream per
+# tensor, so adding a tensor at the end never changes the earlier ones.
+
+def gemv_add_norm(seed: int = 0, rows: int = 1024, cols: int = 1024) -> dict:
+    """One q8 GEMV (rows x cols) whose output is added into a residual and RMS-normed."""
+    r = streams(seed, 4)
+    return {"W": q8(r[0], rows, cols), "x": normal(r[1], cols),
+            "h": normal(r[2], rows), "w": norm_weight(r[3], rows), "eps": EPS}
+
+
+def f16_gemv(seed: int = 0, rows: int = 4096, cols: int = 4096) -> dict:
+    r = streams(seed, 2)
+    return {"W": f16(r[0], rows, cols), "x": normal(r[1], cols)}
+
+
+@dataclass
+class FrameShape:
+    hidden: int = 4096
+    qkv: int = 6144
+    inter: int = 14336
+    vocab: int = 32000
+
+
+def frame_weights(seed: int = 0, shape: FrameShape = FrameShape()) -> dict:
+    """Weights of one layer frame: QKV, up, down, head (q8) and the two norm weights."""
+    r = streams(seed, 6)
+    H = shape.hidden
+    return {"qkv": q8(r[0], shape.qkv, H), "up": q8(r[1], shape.inter, H),
+            "down": q8(r[2], H, shape.inter), "head": q8(r[3], shape.vocab, H),
+            "w1": norm_weight(r[4], H), "w2": norm_weight(r[5], H), "eps": EPS}
+
+
+def frame_inputs(seed: int, n: int, hidden: int = 4096) -> dict:
+    """Per-position inputs of a frame: x0 (the matrix input) and h0 (the residual)."""
+    r = streams(seed + 1_000_003, 2)
+    return {"x0": normal(r[0], (n, hidden)), "h0": normal(r[1], (n, hidden))}
+
+
+@dataclass
+class MoEShape:
+    n: int = 64
+    hidden: int = 2688
+    inter: int = 1856
+    experts: int = 128
+    top_k: int = 6
+
+
+def moe(seed: int = 0, shape: MoEShape = MoEShape()) -> dict:
+    """A routed-MoE pass: input, residual, router, up/down expert banks, norm weight."""
+    r = streams(seed, 6)
+    n, H, I, E = shape.n, shape.hidden, shape.inter, shape.experts
+    return {"X": normal(r[0], (n, H)), "h": normal(r[1], (n, H)),
+            "Wr": router_weight(r[2], E, H),
+            "up": q8(r[3], I, H, lead=(E,)), "down": q8(r[4], H, I, lead=(E,)),
+            "w": norm_weight(r[5], H), "eps": EPS, "top_k": shape.top_k}

@@ -1,0 +1,439 @@
+"""Pins of the CPU oracle to things other than itself (runs without a GPU).
+
+Each oracle function is checked against what mathematics fixes independently of
+its code: exact rational arithmetic on tiny inputs, exact-integer special
+cases, closed forms, invariants, and textbook numpy/scipy routines.  The cases
+are chosen so that a plausible mistake (a dropped term, a wrong block index, a
+transposed operand, a wrong sign, a wrong tie rule) fails at least one of them;
+``test_planted_*`` show that on purpose-broken oracle calls.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import synth
+
+BLOCK = 32
+
+
+def _rand_q8(rng, rows, cols):
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    s = rng.uniform(1e-3, 1e-2, size=(rows, cols // BLOCK)).astype(np.float32)
+    b = rng.normal(0, 1e-3, size=(rows, cols // BLOCK)).astype(np.float32)
+    return q, s, b
+
+
+# ------------------------------------------------------------------ binary16
+
+def test_f16_decode_all_patterns(oracle):
+    """Every binary16 pattern decodes to numpy's float16 -> float64 value."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(v)) for v in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_f16_decode_closed_forms(oracle):
+    assert oracle.f16_to_f64(0x3C00) == 1.0
+    assert oracle.f16_to_f64(0xC000) == -2.0
+    assert oracle.f16_to_f64(0x7BFF) == 65504.0
+    assert oracle.f16_to_f64(0x0001) == 2.0 ** -24
+    assert oracle.f16_to_f64(0x0400) == 2.0 ** -14
+    assert oracle.f16_to_f64(0x3555) == 1365 / 4096
+
+
+# ------------------------------------------------------------------ dequant
+
+def test_dequant_special_cases(oracle):
+    rng = np.random.default_rng(1)
+    q, s, b = _rand_q8(rng, 3, 96)
+    w0 = oracle.dequant_q8(q, np.zeros_like(s), b)
+    assert np.array_equal(w0, np.repeat(b.astype(np.float64), BLOCK, axis=1))
+    w1 = oracle.dequant_q8(q, s, np.zeros_like(b))
+    # s*q with s f32 and |q| < 2^7 is exact in double
+    exact = np.array([[float(Fraction(float(s[r, c // BLOCK])) * int(q[r, c]))
+                       for c in range(96)] for r in range(3)])
+    assert np.array_equal(w1, exact)
+
+
+def test_dequant_block_index(oracle):
+    """Scale 2^-(r+blk), bias (r+1)*2^-(10+blk), q = column-dependent: catches a swapped
+    or misplaced block index (c % 32 instead of c // 32, rows for columns)."""
+    rows, cols = 4, 128
+    q = np.array([[(c % 7) - 3 for c in range(cols)] for _ in range(rows)], np.int8)
+    s = np.array([[2.0 ** -(r + k) for k in range(cols // BLOCK)] for r in range(rows)], np.float32)
+    b = np.array([[(r + 1) * 2.0 ** -(10 + k) for k in range(cols // BLOCK)] for r in range(rows)],
+                 np.float32)
+    w = oracle.dequant_q8(q, s, b)
+    for r in range(rows):
+        for c in range(cols):
+            k = c // BLOCK
+            assert w[r, c] == ((c % 7) - 3) * 2.0 ** -(r + k) + (r + 1) * 2.0 ** -(10 + k)
+
+
+def _affine_quant(w):
+    """Test-only affine quantizer of one 32-block: b = (max+min)/2, s = (max-min)/254,
+    q = clamp(round_half_even((w - b)/s), -127, 127)."""
+    lo, hi = float(np.min(w)), float(np.max(w))
+    b = np.float32((hi + lo) / 2)
+    s = np.float32((hi - lo) / 254) if hi > lo else np.float32(1.0)
+    q = np.clip(np.rint((w.astype(np.float64) - b) / s), -127, 127).astype(np.int8)
+    return q, s, b
+
+
+def test_dequant_round_trip(oracle):
+    rng = np.random.default_rng(2)
+    for trial in range(20):
+        rows, cols = 2, 64
+        w = rng.normal(0, 10.0 ** rng.uniform(-3, 2), size=(rows, cols))
+        q = np.empty((rows, cols), np.int8)
+        s = np.empty((rows, cols // BLOCK), np.float32)
+        b = np.empty((rows, cols // BLOCK), np.float32)
+        for r in range(rows):
+            for k in range(cols // BLOCK):
+                q[r, k * BLOCK:(k + 1) * BLOCK], s[r, k], b[r, k] = _affine_quant(
+                    w[r, k * BLOCK:(k + 1) * BLOCK])
+        deq = oracle.dequant_q8(q, s, b)
+        bound = np.repeat(s.astype(np.float64), BLOCK, axis=1) * (0.5 + 1e-5) + 1e-7 * np.abs(w)
+        assert np.all(np.abs(deq - w) <= bound), trial
+
+
+# ------------------------------------------------------------------ q8 products
+
+def test_gemm_q8_brute_force_fractions(oracle):
+    """Exact rational evaluation of the definition on a tiny 3x64 matrix, two positions."""
+    rng = np.random.default_rng(3)
+    q, s, b = _rand_q8(rng, 3, 64)
+    X = rng.standard_normal((2, 64)).astype(np.float32)
+    Y = oracle.gemm_q8(q, s, b, X)
+    for p in range(2):
+        for r in range(3):
+            acc = Fraction(0)
+            for c in range(64):
+                w = Fraction(float(s[r, c // BLOCK])) * int(q[r, c]) + Fraction(float(b[r, c // BLOCK]))
+                acc += w * Fraction(float(X[p, c]))
+            assert abs(Y[p, r] - float(acc)) <= 1e-13 * max(1.0, abs(float(acc)))
+
+
+def test_gemm_q8_exact_integer_case(oracle):
+    """s = 2^-3, b = 0, integer x: every partial sum is an exact dyadic, so the f64 result
+    equals the integer product exactly (also the case a device must match bit for bit)."""
+    rng = np.random.default_rng(4)
+    rows, cols, n = 37, 320, 5
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    s = np.full((rows, cols // BLOCK), 0.125, np.float32)
+    b = np.zeros((rows, cols // BLOCK), np.float32)
+    X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
+    Y = oracle.gemm_q8(q, s, b, X)
+    exact = (X.astype(np.int64) @ q.astype(np.int64).T) / 8
+    assert np.array_equal(Y, exact)
+
+
+def test_gemm_q8_two_term_identity(oracle):
+    """y_r = sum_blk s_rb (sum_{c in blk} q_rc x_c) + sum_blk b_rb X_blk with X_blk the block
+    sum of x: a dropped bias term, a misplaced scale or a transposed operand breaks it."""
+    rng = np.random.default_rng(5)
+    rows, cols, n = 50, 256, 3
+    q, s, b = _rand_q8(rng, rows, cols)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    Y = oracle.gemm_q8(q, s, b, X)
+    nb = cols // BLOCK
+    qb = q.astype(np.float64).reshape(rows, nb, BLOCK)
+    Xb = X.astype(np.float64).reshape(n, nb, BLOCK)
+    T = np.einsum("rkc,pkc->prk", qb, Xb)           # per-block integer-weight dots
+    two = np.einsum("prk,rk->pr", T, s.astype(np.float64)) + Xb.sum(-1) @ b.astype(np.float64).T
+    np.testing.assert_allclose(Y, two, rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_q8_textbook_numpy(oracle):
+    rng = np.random.default_rng(6)
+    rows, cols, n = 70, 192, 4
+    q, s, b = _rand_q8(rng, rows, cols)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    W = np.repeat(s.astype(np.float64), BLOCK, 1) * q + np.repeat(b.astype(np.float64), BLOCK, 1)
+    np.testing.assert_allclose(oracle.gemm_q8(q, s, b, X), X.astype(np.float64) @ W.T,
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_q8_act_and_rows(oracle):
+    rng = np.random.default_rng(7)
+    q, s, b = _rand_q8(rng, 40, 128)
+    X = rng.standard_normal((3, 128)).astype(np.float32)
+    Y0 = oracle.gemm_q8(q, s, b, X, act=0)
+    Y1 = oracle.gemm_q8(q, s, b, X, act=1)
+    assert np.array_equal(Y1, np.where(Y0 > 0, Y0 * Y0, 0.0))
+    idx = np.array([39, 0, 17, 17])
+    assert np.array_equal(oracle.gemm_q8_rows(q, s, b, idx, X, act=1), Y1[:, idx])
+    for p in range(3):
+        assert np.array_equal(oracle.gemm_q8(q, s, b, X[p]), Y0[p])
+
+
+def test_relu2_closed_form(oracle):
+    """relu^2 on outputs with known values: 3 -> 9, -2 -> 0, 0 -> 0."""
+    q = np.zeros((3, 32), np.int8)
+    q[0, 0], q[1, 0], q[2, 0] = 3, -2, 0
+    s = np.ones((3, 1), np.float32)
+    b = np.zeros((3, 1), np.float32)
+    x = np.zeros(32, np.float32)
+    x[0] = 1.0
+    assert list(oracle.gemm_q8(q, s, b, x, act=1)) == [9.0, 0.0, 0.0]
+
+
+# ------------------------------------------------------------------ f16 products
+
+def test_gemm_f16_textbook_and_exact(oracle):
+    rng = np.random.default_rng(8)
+    W = synth.f16(rng, 33, 96)
+    X = rng.standard_normal((2, 96)).astype(np.float32)
+    np.testing.assert_allclose(oracle.gemm_f16(W, X), X.astype(np.float64) @ W.astype(np.float64).T,
+                               rtol=1e-12, atol=1e-13)
+    Wi = (rng.integers(-64, 65, size=(9, 64)) / 16).astype(np.float16)   # exact dyadics
+    Xi = rng.integers(-5, 6, size=(3, 64)).astype(np.float32)
+    exact = (Xi.astype(np.int64) @ (Wi.astype(np.float64) * 16).astype(np.int64).T) / 16
+    assert np.array_equal(oracle.gemm_f16(Wi, Xi), exact)
+
+
+# ------------------------------------------------------------------ add + RMSNorm
+
+def test_rmsnorm_unit_weight_rms(oracle):
+    """w = 1: RMS(out) = sqrt(m / (m + eps)) with m = mean(h'^2)."""
+    rng = np.random.default_rng(9)
+    for H, eps in [(1024, 1e-6), (2688, 1e-6), (64, 0.5)]:
+        h = rng.standard_normal((3, H)).astype(np.float32)
+        d = rng.standard_normal((3, H)).astype(np.float32)
+        hp, out = oracle.add_rmsnorm(h, d, np.ones(H, np.float32), eps)
+        m = np.mean(hp * hp, axis=1)
+        np.testing.assert_allclose(np.sqrt(np.mean(out * out, axis=1)), np.sqrt(m / (m + eps)),
+                                   rtol=1e-13)
+
+
+def test_rmsnorm_add_and_stride(oracle):
+    rng = np.random.default_rng(10)
+    n, H, stride = 4, 256, 384
+    h = rng.standard_normal((n, H)).astype(np.float32)
+    wide = rng.standard_normal((n, stride)).astype(np.float32)
+    w = synth.norm_weight(rng, H)
+    hp, out = oracle.add_rmsnorm(h, wide, w, 1e-6, delta_stride=stride)
+    assert np.array_equal(hp, h.astype(np.float64) + wide[:, :H])     # exact in f64
+    hp0, out0 = oracle.add_rmsnorm(h, None, w, 1e-6)
+    assert np.array_equal(hp0, h.astype(np.float64))
+    ref = w * hp / np.sqrt(np.mean(hp * hp, axis=1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(out, ref, rtol=1e-13)
+
+
+def test_rmsnorm_special_cases(oracle):
+    H = 128
+    w = np.linspace(0.5, 1.5, H).astype(np.float32)
+    zero = np.zeros(H, np.float32)
+    hp, out = oracle.add_rmsnorm(zero, zero, w, 1e-6)
+    assert np.all(out == 0.0)
+    a, i = 3.0, 17
+    h = zero.copy()
+    h[i] = a
+    _, out = oracle.add_rmsnorm(h, None, w, 1e-6)
+    expect = np.zeros(H)
+    expect[i] = float(w[i]) * a / np.sqrt(a * a / H + 1e-6)
+    np.testing.assert_allclose(out, expect, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_scale_invariance(oracle):
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal(512).astype(np.float32)
+    w = synth.norm_weight(rng, 512)
+    _, o1 = oracle.add_rmsnorm(h, None, w, 1e-6)
+    _, o2 = oracle.add_rmsnorm(h * np.float32(64.0), None, w, 1e-6)
+    np.testing.assert_allclose(o1, o2, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ router
+
+def test_router_logits_f64_textbook(oracle):
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((5, 2688)).astype(np.float32)
+    Wr = synth.router_weight(rng, 128, 2688)
+    np.testing.assert_allclose(oracle.router_logits_f64(X, Wr),
+                               X.astype(np.float64) @ Wr.astype(np.float64).T, rtol=1e-12, atol=1e-13)
+
+
+def test_router_logits_f32_exact_integers(oracle):
+    """Small integers: every f32 partial sum is exact, so the f32 logit is the integer dot."""
+    rng = np.random.default_rng(13)
+    X = rng.integers(-9, 10, size=(4, 2688)).astype(np.float32)
+    Wr = rng.integers(-9, 10, size=(16, 2688)).astype(np.float32)
+    got = oracle.router_logits_f32(X, Wr)
+    assert np.array_equal(got.astype(np.float64), (X.astype(np.int64) @ Wr.astype(np.int64).T))
+
+
+def test_router_logits_f32_error_bound(oracle):
+    """|f32 - exact| <= gamma * sum|x w| with gamma for the longest chain plus tree depth."""
+    rng = np.random.default_rng(14)
+    H = 2688
+    X = rng.standard_normal((8, H)).astype(np.float32)
+    Wr = synth.router_weight(rng, 32, H)
+    f32 = oracle.router_logits_f32(X, Wr).astype(np.float64)
+    f64 = oracle.router_logits_f64(X, Wr)
+    depth = 4 * -(-(H // 4) // 64) + 6
+    u = 2.0 ** -24
+    gamma = depth * u / (1 - depth * u)
+    bound = gamma * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)).T)
+    assert np.all(np.abs(f32 - f64) <= bound)
+    assert np.any(f32 != f64)   # it really is an f32 computation
+
+
+def test_route_textbook_topk_and_softmax(oracle):
+    rng = np.random.default_rng(15)
+    n, E, k = 64, 128, 6
+    logits = (rng.standard_normal((n, E)) * 1.3).astype(np.float32)
+    sel, rw, probs = oracle.route(logits, k)
+    for b in range(n):
+        order = np.lexsort((np.arange(E), -logits[b].astype(np.float64)))
+        assert list(sel[b]) == list(order[:k])
+    np.testing.assert_allclose(probs, scipy.special.softmax(logits.astype(np.float64), axis=1),
+                               rtol=1e-13)
+    np.testing.assert_allclose(probs.sum(1), 1.0, rtol=1e-14)
+    assert np.array_equal(rw, np.take_along_axis(probs, sel.astype(np.int64), 1))
+    _, rwn, _ = oracle.route(logits, k, renorm=1)
+    np.testing.assert_allclose(rwn.sum(1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(rwn, rw / rw.sum(1, keepdims=True), rtol=1e-14)
+
+
+def test_route_tie_lower_index_wins(oracle):
+    """Duplicate router rows e1 < e2 give identical logits; e1 must rank first."""
+    rng = np.random.default_rng(16)
+    H, E = 256, 16
+    Wr = synth.router_weight(rng, E, H)
+    Wr[11] = Wr[3]
+    Wr[9] = Wr[3] * np.float32(4.0)      # strictly larger for positive logits
+    X = rng.standard_normal((32, H)).astype(np.float32)
+    L = oracle.router_logits_f32(X, Wr)
+    assert np.array_equal(L[:, 3], L[:, 11])
+    sel, _, _ = oracle.route(L, E)
+    for b in range(32):
+        pos = {int(e): t for t, e in enumerate(sel[b])}
+        assert pos[3] < pos[11]
+    # all-equal logits: selection is 0, 1, 2, ...
+    sel, rw, _ = oracle.route(np.zeros((2, 10), np.float32), 4)
+    assert sel.tolist() == [[0, 1, 2, 3]] * 2
+    np.testing.assert_allclose(rw, 0.1, rtol=1e-15)
+
+
+def test_group_textbook(oracle):
+    rng = np.random.default_rng(17)
+    n, k, E = 64, 6, 128
+    sel = np.stack([rng.permutation(E)[:k] for _ in range(n)]).astype(np.int32)
+    counts, lists = oracle.group(sel, E)
+    flat = sel.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    order = np.argsort(flat, kind="stable")
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    for e in range(E):
+        assert list(lists[e, :counts[e]]) == list(order[starts[e]:starts[e] + counts[e]])
+        assert np.all(lists[e, counts[e]:] == -1)
+    assert counts.sum() == n * k
+    seen = np.concatenate([lists[e, :counts[e]] for e in range(E)])
+    assert np.array_equal(np.sort(seen), np.arange(n * k))
+
+
+# ------------------------------------------------------------------ routed experts
+
+def _small_moe(seed, n=6, H=64, I=96, E=5, k=2):
+    rng = np.random.default_rng(seed)
+    up = synth.q8(rng, I, H, lead=(E,))
+    down = synth.q8(rng, H, I, lead=(E,))
+    X = rng.standard_normal((n, H)).astype(np.float32)
+    h = rng.standard_normal((n, H)).astype(np.float32)
+    Wr = synth.router_weight(rng, E, H)
+    w = synth.norm_weight(rng, H)
+    return up, down, X, h, Wr, w, k
+
+
+def test_moe_grouped_equals_ungrouped(oracle):
+    up, down, X, h, Wr, w, k = _small_moe(18)
+    sel, _, _ = oracle.route(oracle.router_logits_f32(X, Wr), k)
+    t_up, t_dn = (up.q, up.scale, up.bias), (down.q, down.scale, down.bias)
+    U0, D0 = oracle.moe_experts(X, sel, t_up, t_dn, grouped=False)
+    U1, D1 = oracle.moe_experts(X, sel, t_up, t_dn, grouped=True)
+    assert np.array_equal(U0, U1) and np.array_equal(D0, D1)
+
+
+def test_moe_single_expert_is_dense_ffn(oracle):
+    """k = 1 and every position routed to one expert: U = relu^2(Up x), D = Down U."""
+    up, down, X, h, Wr, w, _ = _small_moe(19, E=3)
+    n = X.shape[0]
+    sel = np.full((n, 1), 2, np.int32)
+    U, D = oracle.moe_experts(X, sel, (up.q, up.scale, up.bias), (down.q, down.scale, down.bias))
+    U_ref = oracle.gemm_q8(up.q[2], up.scale[2], up.bias[2], X, act=1)
+    assert np.array_equal(U, U_ref)
+    Wd = oracle.dequant_q8(down.q[2], down.scale[2], down.bias[2])
+    np.testing.assert_allclose(D, U_ref @ Wd.T, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_combine_textbook(oracle):
+    rng = np.random.default_rng(20)
+    n, k, H = 5, 3, 96
+    h = rng.standard_normal((n, H)).astype(np.float32)
+    D = rng.standard_normal((n * k, H))
+    rw = rng.uniform(0, 1, (n, k))
+    w = synth.norm_weight(rng, H)
+    hp, out = oracle.moe_combine(h, D, rw, w, 1e-6)
+    m = np.einsum("bt,bti->bi", rw, D.reshape(n, k, H))
+    np.testing.assert_allclose(hp, h + m, rtol=1e-14, atol=1e-14)
+    ref = w * hp / np.sqrt(np.mean(hp * hp, 1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(out, ref, rtol=1e-13)
+
+
+def test_moe_pass_stages_consistent(oracle):
+    up, down, X, h, Wr, w, k = _small_moe(21, n=8, E=6, k=3)
+    res = oracle.moe_pass(X, h, Wr, (up.q, up.scale, up.bias), (down.q, down.scale, down.bias),
+                          w, 1e-6, k)
+    assert res["counts"].sum() == 8 * 3
+    for j in range(8 * 3):
+        b, t = divmod(j, 3)
+        e = res["sel"][b, t]
+        np.testing.assert_allclose(res["U"][j], oracle.gemm_q8(up.q[e], up.scale[e], up.bias[e],
+                                                               X[b], act=1), rtol=0, atol=0)
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def test_planted_dropped_bias_is_caught(oracle):
+    """A mistake planted in the oracle call (the bias term dropped) fails the
+    two-term identity pin."""
+    rng = np.random.default_rng(22)
+    q, s, b = _rand_q8(rng, 20, 128)
+    X = rng.standard_normal((2, 128)).astype(np.float32)
+    bad = oracle.gemm_q8(q, s, np.zeros_like(b), X)
+    nb = 4
+    T = np.einsum("rkc,pkc->prk", q.astype(np.float64).reshape(20, nb, BLOCK),
+                  X.astype(np.float64).reshape(2, nb, BLOCK))
+    two = np.einsum("prk,rk->pr", T, s.astype(np.float64)) + \
+        X.astype(np.float64).reshape(2, nb, BLOCK).sum(-1) @ b.astype(np.float64).T
+    assert not np.allclose(bad, two, rtol=1e-9, atol=1e-9)
+
+
+def test_planted_transpose_is_caught(oracle):
+    """A transposed weight operand (square matrix, so the shapes still fit) fails the
+    exact rational brute force."""
+    rng = np.random.default_rng(23)
+    q, s, b = _rand_q8(rng, 64, 64)
+    x = rng.standard_normal(64).astype(np.float32)
+    W = oracle.dequant_q8(q, s, b)
+    qt = np.ascontiguousarray(q.T)
+    bad = oracle.gemm_q8(qt, s, b, x)
+    exact = np.array([float(sum(Fraction(W[r, c]) * Fraction(float(x[c])) for c in range(64)))
+                      for r in range(64)])
+    assert np.max(np.abs(bad - exact)) > 1e-3
+
+
+def test_planted_wrong_tie_rule_is_caught(oracle):
+    """Reversing the tie rule (higher index wins) fails the duplicate-row tie pin."""
+    L = np.zeros((1, 8), np.float32)
+    L[0, 2] = L[0, 6] = 1.0
+    sel, _, _ = oracle.route(L, 2)
+    assert sel.tolist() == [[2, 6]]
+    flipped = oracle.route(L[:, ::-1].copy(), 2)[0]
+    assert (7 - flipped).tolist() != [[2, 6]]   # the mirrored walk prefers the other copy
