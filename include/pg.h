@@ -1,0 +1,162 @@
+/*
+ * pg.h — packed-weight products for MI355X (gfx950): the C ABI of libpg.
+ *
+ * The library evaluates the data-parallel hot path of a portable LLM
+ * inference runtime (cortiq-engine's GPU frames, as described on its docs.rs
+ * source pages): products of packed weights with f32 activations, the decode
+ * matrix-vector product at one position, the batched prefill product over up
+ * to 64 positions with every weight read once per pass, the fused residual
+ * add + RMSNorm and relu^2 stages around them, and the routed-MoE step that
+ * groups (position, slot) pairs per expert so each selected expert is
+ * streamed once per pass.
+ *
+ * Conventions shared by every call
+ *  - Pointers named as tensors are DEVICE pointers owned by the caller.  The
+ *    library never allocates, frees or synchronizes; it enqueues kernels on
+ *    `stream` (a hipStream_t; NULL is the null stream) and returns.
+ *  - Return value: PG_OK, or a negative PG_E* code.  On any error other than
+ *    PG_ELAUNCH nothing has been enqueued.  PG_ELAUNCH reports a failed kernel
+ *    launch (hipGetLastError after the launch); faults during execution show
+ *    up at the caller's next synchronization of `stream`.
+ *  - q8 weight format ("q8 block"): q is int8 [rows][cols] row-major; every
+ *    32 consecutive columns of a row form a block with one f32 scale and one
+ *    f32 bias, stored [rows][cols/32] row-major; the weight is
+ *        w[r][c] = scale[r][c/32] * q[r][c] + bias[r][c/32].
+ *    cols % 32 == 0.  The pages' own int8 format (q8_2f: int8 body, f16 row
+ *    scales, f16 column field; nemotron_prefill.rs `pb_q8_bank`,
+ *    gemma_batch.rs `q8_2f_mm_r2`) folds its factors the same way: the column
+ *    factor into the staged activations, the row factor onto the finished sum.
+ *  - act: 0 = none, 1 = relu^2, y = max(y, 0)^2 on the finished product
+ *    (nemotron_prefill.rs, `pb_relu2` and `PqP.act`).
+ *  - Alignment: q, scale, bias, activation and output pointers must be
+ *    16-byte aligned (the kernels move 16 bytes per lane); PG_EINVAL if not.
+ *  - Calls are stateless and thread-safe; calls that share a workspace or
+ *    output buffer and overlap on different streams race.
+ */
+#ifndef PG_H
+#define PG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *pg_stream_t; /* a hipStream_t */
+
+enum {
+    PG_OK = 0,
+    PG_EINVAL = -1,        /* null pointer, non-positive size, misalignment, aliasing */
+    PG_EUNSUPPORTED = -2,  /* shape outside what the kernels handle (listed per call) */
+    PG_ELAUNCH = -3,       /* a kernel launch failed */
+    PG_EWORKSPACE = -4     /* workspace pointer NULL or smaller than the query returns */
+};
+
+/* Human-readable text of a PG_* code (static storage). */
+const char *pg_strerror(int code);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char *pg_version(void);
+
+/*
+ * gemv_q8 — decode matrix-vector product at one position:
+ *     y[r] = act( sum_c w[r][c] * x[c] ),  r < rows,
+ * with w the q8-block weight.  The weight stays packed in HBM and is decoded
+ * in registers as it streams (embryo_wide.wgsl, header comment: matrices stay
+ * in the file's form on the device, read in 16-byte loads).
+ *   q [rows][cols] int8, scale/bias [rows][cols/32] f32, x [cols] f32,
+ *   y [rows] f32 (written; must not overlap x).
+ * PG_EUNSUPPORTED: cols % 32 != 0, cols > 32768.
+ */
+int gemv_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+            int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
+
+/*
+ * gemv_f16 — the same product with binary16 weights, f32 accumulation:
+ *     y[r] = act( sum_c f16(w[r][c]) * x[c] )
+ * (embryo_wide.wgsl, header comment: f16 matrices are read in place.)
+ *   w [rows][cols] binary16 bits, x [cols] f32, y [rows] f32.
+ * PG_EUNSUPPORTED: cols % 8 != 0, cols > 32768.
+ */
+int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const float *x, float *y,
+             int32_t act, pg_stream_t stream);
+
+/*
+ * prefill_gemm_q8 — batched prefill product over one pass of n positions,
+ * every weight read from HBM once per pass (nemotron_prefill.rs, module doc:
+ * up to PB_MAX = 64 positions a pass; gemma_batch.rs, `encode_q82_mm`:
+ * y[nb][rows] = x[nb][cols] . W^T):
+ *     Y[b][r] = act( sum_c w[r][c] * X[b][c] ),  b < n, r < rows.
+ *   X [n][cols] f32, Y [n][rows] f32 (must not overlap X or the workspace).
+ *   workspace: device scratch of at least
+ *   prefill_gemm_q8_workspace_bytes(rows, cols, n) bytes (contents on entry
+ *   do not matter; the call overwrites them).
+ * Arithmetic: the weights enter the matrix cores as exact bf16 integers, the
+ * activations as an exact-to-2^-17 bf16 hi+lo pair, products accumulate in
+ * f32 per 32-column block, the block scale multiplies each block sum in f32
+ * and the bias term sum_blk bias[r][blk] * (sum_{c in blk} X[b][c]) is added.
+ * PG_EUNSUPPORTED: cols % 32 != 0, n < 1 or n > 64.
+ */
+int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                    int32_t cols, const float *X, int32_t n, float *Y, int32_t act,
+                    void *workspace, size_t workspace_bytes, pg_stream_t stream);
+size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n);
+
+/*
+ * add_rmsnorm — fused residual add + RMSNorm, per position b < n
+ * (nemotron_prefill.rs `pb_add_rms` with add = 1; gemma_batch.rs
+ * `g4_add_norm_b` without the layer scalar):
+ *     h[b][i] += delta[b * delta_stride + i]        (skipped if delta is NULL)
+ *     out[b][i] = w[i] * h[b][i] / sqrt( (1/hidden) sum_i h[b][i]^2 + eps )
+ *   h [n][hidden] f32, updated in place; delta rows delta_stride floats apart
+ *   (delta_stride >= hidden; it lets a wider product output, e.g. the first
+ *   `hidden` columns of a [n][6144] QKV result, be added in place);
+ *   w [hidden] f32; out [n][hidden] f32 (must not overlap h or delta).
+ * PG_EUNSUPPORTED: hidden % 4 != 0, hidden > 16384, delta_stride % 4 != 0.
+ */
+int add_rmsnorm(float *h, const float *delta, int32_t delta_stride, const float *w, float eps,
+                int32_t hidden, int32_t n, float *out, pg_stream_t stream);
+
+/*
+ * moe_grouped — one routed-MoE pass over n positions (nemotron_prefill.rs:
+ * `pb_f32_mm` router, `pb_route` top-k, `pb_lists` per-expert lists,
+ * `pb_q8_bank` expert banks with act = relu^2 on the up product, `pb_add_rms`
+ * with add = 2 for the slot-ordered weighted sum into the residual):
+ *     logits[b][e] = sum_c X[b][c] * Wr[e][c]                     (f32, order below)
+ *     p[b][.]      = softmax(logits[b][.]) over all E experts
+ *     sel[b][t]    = t-th largest logit (t < top_k), lower index wins a tie
+ *     route_w[b][t]= p[b][sel[b][t]]  (divided by sum_t p[b][sel[b][t]] if renorm)
+ *     counts[e], lists[e][0..counts[e]) = the entries j = b*top_k + t with
+ *                    sel[b][t] == e, in ascending j
+ *     u_j = relu^2( Up_e . X[b] ),  d_j = Down_e . u_j            (e = sel of j)
+ *     h[b] += sum_t route_w[b][t] * d_{b*top_k+t}                  (t ascending)
+ *     out[b] = w_norm * h[b] / sqrt(mean(h[b]^2) + eps)
+ * Each selected expert's weights are streamed from HBM once for all of its
+ * entries.  The logit is an f32 value in a fixed order: 64 partial sums, the
+ * l-th chaining fused multiply-adds over the 4-column groups l, l+64, ... (the
+ * 4 columns of a group in order), then folded pairwise for s = 32, 16, ..., 1
+ * (partial l += partial l+s).  Expert choice is taken on those bits.
+ *   X [n][H] f32 (the normed input), Wr [E][H] f32,
+ *   up_q [E][I][H] int8, up_scale/up_bias [E][I][H/32] f32,
+ *   down_q [E][H][I] int8, down_scale/down_bias [E][H][I/32] f32,
+ *   h [n][H] f32 in/out, w_norm [H] f32, out [n][H] f32,
+ *   logits [n][E] f32, sel [n][top_k] int32, route_w [n][top_k] f32,
+ *   counts [E] int32, lists [E][n] int32 (entries past counts[e] unspecified),
+ *   workspace of at least moe_grouped_workspace_bytes(n, H, I, E, top_k) bytes.
+ * PG_EUNSUPPORTED: n < 1 or n > 64, H % 32 or I % 32 != 0, H > 16384,
+ *   E < 1 or E > 1024, top_k < 1 or top_k > min(E, 16).
+ */
+int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
+                int32_t top_k, int32_t renorm, const int8_t *up_q, const float *up_scale,
+                const float *up_bias, int32_t I, const int8_t *down_q, const float *down_scale,
+                const float *down_bias, float *h, const float *w_norm, float eps, float *out,
+                float *logits, int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
+                void *workspace, size_t workspace_bytes, pg_stream_t stream);
+size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, int32_t E, int32_t top_k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PG_H */

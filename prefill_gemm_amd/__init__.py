@@ -1,0 +1,19 @@
+"""prefill_gemm_amd — packed-weight products for MI355X (gfx950).
+
+The hot path is hand-written HIP in ``csrc/`` behind the C ABI of
+``include/pg.h`` (built into ``libpg.so``); this package is its thin Python
+binding plus the layer-frame orchestration.  Importing it loads libpg and
+fails loudly if the library has not been built: there is no CPU fallback.
+"""
+from ._lib import (PG_EINVAL, PG_ELAUNCH, PG_EUNSUPPORTED, PG_EWORKSPACE, PG_OK, PGError,
+                   Q8Weight, add_rmsnorm, gemv_f16, gemv_q8, lib, moe_grouped,
+                   moe_grouped_workspace_bytes, prefill_gemm_q8, prefill_gemm_q8_workspace_bytes,
+                   strerror, version)
+from .frame import PB_MAX, Frame
+
+lib()
+
+__all__ = ["PG_OK", "PG_EINVAL", "PG_EUNSUPPORTED", "PG_ELAUNCH", "PG_EWORKSPACE", "PGError",
+           "Q8Weight", "gemv_q8", "gemv_f16", "prefill_gemm_q8", "prefill_gemm_q8_workspace_bytes",
+           "add_rmsnorm", "moe_grouped", "moe_grouped_workspace_bytes", "strerror", "version",
+           "lib", "Frame", "PB_MAX"]

@@ -1,0 +1,238 @@
+"""ctypes binding of libpg (include/pg.h): argument marshalling only.
+
+Every function takes device tensors (PyTorch-ROCm owns the memory and the
+stream), checks dtypes/shapes/contiguity, passes raw pointers and the current
+HIP stream to the C entry point of the same name, and raises ``PGError`` on a
+non-zero status.  All arithmetic happens in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpg.so")
+
+PG_OK, PG_EINVAL, PG_EUNSUPPORTED, PG_ELAUNCH, PG_EWORKSPACE = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class PGError(RuntimeError):
+    def __init__(self, name: str, code: int):
+        super().__init__(f"{name} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpg.  Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libpg.so is not built ({LIB_PATH}); run `python -m prefill_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def _declare(L):
+    L.pg_strerror.argtypes = [ctypes.c_int]
+    L.pg_strerror.restype = ctypes.c_char_p
+    L.pg_version.restype = ctypes.c_char_p
+    L.gemv_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
+    L.gemv_f16.argtypes = [_P, _i32, _i32, _P, _P, _i32, _P]
+    L.prefill_gemm_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
+    L.prefill_gemm_q8_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    L.prefill_gemm_q8_workspace_bytes.restype = _sz
+    L.add_rmsnorm.argtypes = [_P, _P, _i32, _P, _f, _i32, _i32, _P, _P]
+    L.moe_grouped.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _i32, _P, _P, _P, _i32, _P, _P, _P,
+                              _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
+    L.moe_grouped_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.moe_grouped_workspace_bytes.restype = _sz
+    for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped"):
+        getattr(L, name).restype = ctypes.c_int
+
+
+def strerror(code: int) -> str:
+    return lib().pg_strerror(code).decode()
+
+
+def version() -> str:
+    return lib().pg_version().decode()
+
+
+def _check(name: str, rc: int):
+    if rc != PG_OK:
+        raise PGError(name, rc)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclass
+class Q8Weight:
+    """A q8-block matrix on the device: q int8 [.., rows, cols], scale/bias f32 [.., rows, cols/32]."""
+
+    q: torch.Tensor
+    scale: torch.Tensor
+    bias: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[-2]
+
+    @property
+    def cols(self) -> int:
+        return self.q.shape[-1]
+
+    @staticmethod
+    def from_host(q, scale, bias, device="cuda") -> "Q8Weight":
+        return Q8Weight(torch.as_tensor(q).to(device), torch.as_tensor(scale).to(device),
+                        torch.as_tensor(bias).to(device))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.q, self.scale, self.bias))
+
+    def validate(self, name="W"):
+        _dev(self.q, torch.int8, name + ".q")
+        _dev(self.scale, torch.float32, name + ".scale")
+        _dev(self.bias, torch.float32, name + ".bias")
+        if self.scale.shape != self.q.shape[:-1] + (self.q.shape[-1] // 32,) or self.bias.shape != self.scale.shape:
+            raise ValueError(f"{name}: scale/bias must be [.., rows, cols/32]")
+
+
+def gemv_q8(W: Q8Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):
+    """y = act(W x) for one position; W is q8-block [rows][cols], x f32 [cols]."""
+    W.validate()
+    _dev(x, torch.float32, "x")
+    if x.numel() != W.cols:
+        raise ValueError("x length must equal W.cols")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    _check("gemv_q8", lib().gemv_q8(_ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols,
+                                    _ptr(x), _ptr(y), act, _stream(stream)))
+    return y
+
+
+def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):
+    """y = act(W x) with W float16 [rows][cols], x f32 [cols], f32 accumulation."""
+    _dev(W, torch.float16, "W")
+    _dev(x, torch.float32, "x")
+    rows, cols = W.shape
+    if y is None:
+        y = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    _check("gemv_f16", lib().gemv_f16(_ptr(W), rows, cols, _ptr(x), _ptr(y), act, _stream(stream)))
+    return y
+
+
+def prefill_gemm_q8_workspace_bytes(rows: int, cols: int, n: int) -> int:
+    return lib().prefill_gemm_q8_workspace_bytes(rows, cols, n)
+
+
+def prefill_gemm_q8(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor | None = None, act: int = 0,
+                    workspace: torch.Tensor | None = None, stream=None):
+    """Y [n][rows] = act(X [n][cols] . W^T) for one pass of n <= 64 positions."""
+    W.validate()
+    _dev(X, torch.float32, "X")
+    n = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != W.cols:
+        raise ValueError("X must be [n][W.cols]")
+    if Y is None:
+        Y = torch.empty(n, W.rows, dtype=torch.float32, device=X.device)
+    _dev(Y, torch.float32, "Y")
+    need = prefill_gemm_q8_workspace_bytes(W.rows, W.cols, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check("prefill_gemm_q8", lib().prefill_gemm_q8(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return Y
+
+
+def add_rmsnorm(h: torch.Tensor, delta: torch.Tensor | None, w: torch.Tensor, eps: float,
+                out: torch.Tensor | None = None, delta_stride: int | None = None, stream=None):
+    """h += delta (in place, rows ``delta_stride`` apart); returns out = rmsnorm(h) * w.
+
+    ``delta`` may be a strided view whose rows are contiguous (e.g. qkv[:, :hidden])."""
+    _dev(h, torch.float32, "h")
+    _dev(w, torch.float32, "w")
+    h2 = h.view(-1, h.shape[-1])
+    n, hidden = h2.shape
+    stride = hidden
+    if delta is not None:
+        if delta.dtype != torch.float32 or not delta.is_cuda or delta.stride(-1) != 1:
+            raise ValueError("delta must be a device f32 tensor with contiguous rows")
+        stride = delta_stride if delta_stride is not None else (delta.stride(0) if delta.dim() > 1 else hidden)
+    if out is None:
+        out = torch.empty_like(h)
+    _dev(out, torch.float32, "out")
+    _check("add_rmsnorm", lib().add_rmsnorm(_ptr(h), _ptr(delta), stride, _ptr(w), eps, hidden, n,
+                                            _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_grouped_workspace_bytes(n: int, H: int, I: int, E: int, top_k: int) -> int:
+    return lib().moe_grouped_workspace_bytes(n, H, I, E, top_k)
+
+
+def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight, h: torch.Tensor,
+                w_norm: torch.Tensor, eps: float, top_k: int, renorm: int = 0,
+                workspace: torch.Tensor | None = None, outputs: dict | None = None, stream=None) -> dict:
+    """One routed-MoE pass; updates ``h`` in place and returns the outputs
+    {out, logits, sel, route_w, counts, lists} (pre-allocated ones may be passed in ``outputs``)."""
+    _dev(X, torch.float32, "X")
+    _dev(Wr, torch.float32, "Wr")
+    _dev(h, torch.float32, "h")
+    _dev(w_norm, torch.float32, "w_norm")
+    up.validate("up")
+    down.validate("down")
+    n, H = X.shape
+    E = Wr.shape[0]
+    I = up.q.shape[-2]
+    if up.q.shape != (E, I, H) or down.q.shape != (E, H, I):
+        raise ValueError("expert banks must be up [E][I][H], down [E][H][I]")
+    dev = X.device
+    o = dict(outputs or {})
+    o.setdefault("out", torch.empty(n, H, dtype=torch.float32, device=dev))
+    o.setdefault("logits", torch.empty(n, E, dtype=torch.float32, device=dev))
+    o.setdefault("sel", torch.empty(n, top_k, dtype=torch.int32, device=dev))
+    o.setdefault("route_w", torch.empty(n, top_k, dtype=torch.float32, device=dev))
+    o.setdefault("counts", torch.empty(E, dtype=torch.int32, device=dev))
+    o.setdefault("lists", torch.empty(E, n, dtype=torch.int32, device=dev))
+    need = moe_grouped_workspace_bytes(n, H, I, E, top_k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("moe_grouped", lib().moe_grouped(
+        _ptr(X), n, H, _ptr(Wr), E, top_k, renorm, _ptr(up.q), _ptr(up.scale), _ptr(up.bias), I,
+        _ptr(down.q), _ptr(down.scale), _ptr(down.bias), _ptr(h), _ptr(w_norm), eps, _ptr(o["out"]),
+        _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o

@@ -1,0 +1,243 @@
+// Routed-MoE pass (moe_grouped).  nemotron_prefill.rs: `pb_f32_mm` (router
+// product over the pass), `pb_route` (top-k by k rounds of a workgroup max,
+// the lower expert index winning an exact tie, the winner masked),
+// `pb_lists` (per expert, the pass's entries j = position * k + slot that
+// chose it, ascending), `pb_q8_bank` (expert banks: workgroup per (row block,
+// expert), an expert with no entries returns at once), `pb_add_rms` with
+// add = 2 (the slot-ordered weighted sum into the residual, then the norm).
+// Differences from the page: the router scores are softmax probabilities of
+// the logits (ranking is done on the logits, which softmax preserves), and each
+// expert's weights stream through the matrix cores once for all its entries
+// instead of once per entry.
+#include <math.h>
+
+#include "mma_launch.h"
+#include "pg_device.h"
+#include "pg_host.h"
+
+namespace pg {
+
+int launch_moe_combine(float *h, const float *D, const float *rw, int n, int k, const float *w,
+                       float eps, int hidden, float *out, hipStream_t s);
+
+constexpr int kRouterPos = 8;  // positions per router workgroup
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+// logits[b][e] in the fixed f32 order: lane l chains fused multiply-adds over
+// the 4-column groups l, l+64, ...; the 64 lane sums fold pairwise for
+// s = 32, 16, ..., 1 (lane l += lane l+s); the logit is lane 0's value.
+// Grid (ceil(E / 4), ceil(n / 8)); wave -> expert, 8 positions per workgroup.
+__global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ X,
+                                                            const float *__restrict__ Wr, int n,
+                                                            int H, int E,
+                                                            float *__restrict__ logits) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E) return;
+    const int G4 = H >> 2;
+    const float4 *wr = reinterpret_cast<const float4 *>(Wr + (long long)e * H);
+    for (int bb = 0; bb < kRouterPos; ++bb) {
+        const int b = blockIdx.y * kRouterPos + bb;
+        if (b >= n) break;
+        const float4 *xr = reinterpret_cast<const float4 *>(X + (long long)b * H);
+        float acc = 0.0f;
+        for (int g = lane; g < G4; g += 64) {
+            const float4 w = wr[g], x = xr[g];
+            acc = fmaf(w.x, x.x, acc);
+            acc = fmaf(w.y, x.y, acc);
+            acc = fmaf(w.z, x.z, acc);
+            acc = fmaf(w.w, x.w, acc);
+        }
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const float o = __shfl_down(acc, s, kWave);
+            acc = acc + o;
+        }
+        if (lane == 0) logits[(long long)b * E + e] = acc;
+    }
+}
+
+// One wave per position: softmax over all E logits, then k rounds that take
+// the largest remaining logit (lower index on an exact tie) and mask it.
+__global__ __launch_bounds__(64) void route_kernel(const float *__restrict__ logits, int E, int k,
+                                                   int renorm, int32_t *__restrict__ sel,
+                                                   float *__restrict__ rw) {
+    constexpr int V = kMaxExperts / kWave;
+    const int b = blockIdx.x, lane = threadIdx.x;
+    float v[V];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? logits[(long long)b * E + e] : -INFINITY;
+        mx = fmaxf(mx, v[i]);
+    }
+    mx = wave_max(mx);
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        if (lane + 64 * i < E) z += expf(v[i] - mx);
+    z = wave_sum(z);
+
+    uint32_t taken = 0;
+    float psum = 0.0f;
+    for (int t = 0; t < k; ++t) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const float ov = __shfl_xor(bv, s, kWave);
+            const int oi = __shfl_xor(bi, s, kWave);
+            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        const float p = expf(bv - mx) / z;
+        psum += p;
+        if (lane == 0) {
+            sel[b * k + t] = bi;
+            rw[b * k + t] = p;
+        }
+    }
+    if (renorm && lane == 0)
+        for (int t = 0; t < k; ++t) rw[b * k + t] = rw[b * k + t] / psum;
+}
+
+// One wave per expert: walk the n*k entries in ascending order, 64 at a time,
+// and append the ones that chose this expert (ballot + prefix count).
+__global__ __launch_bounds__(256) void group_kernel(const int32_t *__restrict__ sel, int nk, int E,
+                                                    int cap, int32_t *__restrict__ counts,
+                                                    int32_t *__restrict__ lists) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E) return;
+    int base = 0;
+    for (int j0 = 0; j0 < nk; j0 += 64) {
+        const int j = j0 + lane;
+        const bool hit = j < nk && sel[j] == e;
+        const unsigned long long mask = __ballot(hit);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (hit && base + below < cap) lists[(long long)e * cap + base + below] = j;
+        base += __popcll(mask);
+    }
+    if (lane == 0) counts[e] = base;
+}
+
+struct MoeLayout {
+    size_t xp_x, xs_x, u, xp_u, xs_u, d, total;
+};
+
+static MoeLayout moe_layout(int n, int H, int I, int k) {
+    MoeLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += round_up(bytes, 256);
+        return at;
+    };
+    const int nk = n * k;
+    L.xp_x = take(stage_x_bytes(n, H));
+    L.xs_x = take(stage_s_bytes(n, H));
+    L.u = take((size_t)nk * I * sizeof(float));
+    L.xp_u = take(stage_x_bytes(nk, I));
+    L.xs_u = take(stage_s_bytes(nk, I));
+    L.d = take((size_t)nk * H * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace pg
+
+using namespace pg;
+
+extern "C" size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, int32_t E,
+                                              int32_t top_k) {
+    (void)E;
+    if (n <= 0 || H <= 0 || I <= 0 || top_k <= 0 || H % 32 || I % 32) return 0;
+    return moe_layout(n, H, I, top_k).total;
+}
+
+extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
+                           int32_t top_k, int32_t renorm, const int8_t *up_q,
+                           const float *up_scale, const float *up_bias, int32_t I,
+                           const int8_t *down_q, const float *down_scale, const float *down_bias,
+                           float *h, const float *w_norm, float eps, float *out, float *logits,
+                           int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
+                           void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+    if (!X || !Wr || !up_q || !up_scale || !up_bias || !down_q || !down_scale || !down_bias ||
+        !h || !w_norm || !out || !logits || !sel || !route_w || !counts || !lists)
+        return PG_EINVAL;
+    if (n <= 0 || H <= 0 || I <= 0 || E <= 0 || top_k <= 0) return PG_EINVAL;
+    if (!aligned16(X) || !aligned16(Wr) || !aligned16(up_q) || !aligned16(down_q) ||
+        !aligned16(h) || !aligned16(w_norm) || !aligned16(out))
+        return PG_EINVAL;
+    if (h == out) return PG_EINVAL;
+    if (n > 64 || H % 32 || I % 32 || H > 16384 || E > kMaxExperts || top_k > kMaxTopK ||
+        top_k > E)
+        return PG_EUNSUPPORTED;
+    const MoeLayout L = moe_layout(n, H, I, top_k);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return PG_EWORKSPACE;
+    hipStream_t s = as_stream(stream);
+    char *ws = static_cast<char *>(workspace);
+    const int nk = n * top_k;
+    float *U = reinterpret_cast<float *>(ws + L.u);
+    float *D = reinterpret_cast<float *>(ws + L.d);
+
+    int rc = launch_stage_x(X, n, H, ws + L.xp_x, ws + L.xs_x, s);
+    if (rc) return rc;
+    hipLaunchKernelGGL(router_logits_kernel, dim3(ceil_div(E, 4), ceil_div(n, kRouterPos)),
+                       dim3(256), 0, s, X, Wr, n, H, E, logits);
+    if ((rc = launch_status())) return rc;
+    hipLaunchKernelGGL(route_kernel, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel,
+                       route_w);
+    if ((rc = launch_status())) return rc;
+    hipLaunchKernelGGL(group_kernel, dim3(ceil_div(E, 4)), dim3(256), 0, s, sel, nk, E, n, counts,
+                       lists);
+    if ((rc = launch_status())) return rc;
+
+    MmaPanel up{};
+    up.q = up_q;
+    up.scale = up_scale;
+    up.bias = up_bias;
+    up.rows = I;
+    up.cols = H;
+    up.xp = reinterpret_cast<const uint4 *>(ws + L.xp_x);
+    up.xs = reinterpret_cast<const uint4 *>(ws + L.xs_x);
+    up.zero_row = n;
+    up.src_div = top_k;
+    up.out = U;
+    up.ldo = I;
+    up.act = 1;
+    if ((rc = launch_expert_bank(up, E, counts, lists, n, s))) return rc;
+
+    if ((rc = launch_stage_x(U, nk, I, ws + L.xp_u, ws + L.xs_u, s))) return rc;
+
+    MmaPanel dn{};
+    dn.q = down_q;
+    dn.scale = down_scale;
+    dn.bias = down_bias;
+    dn.rows = H;
+    dn.cols = I;
+    dn.xp = reinterpret_cast<const uint4 *>(ws + L.xp_u);
+    dn.xs = reinterpret_cast<const uint4 *>(ws + L.xs_u);
+    dn.zero_row = nk;
+    dn.src_div = 1;
+    dn.out = D;
+    dn.ldo = H;
+    dn.act = 0;
+    if ((rc = launch_expert_bank(dn, E, counts, lists, n, s))) return rc;
+
+    return launch_moe_combine(h, D, route_w, n, top_k, w_norm, eps, H, out, s);
+}

@@ -1,0 +1,89 @@
+// Device-side building blocks shared by the libpg kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 32;  // columns sharing one scale and one bias
+
+// Relu^2 on a finished product (act == 1), identity otherwise.
+__device__ __forceinline__ float apply_act(int act, float v) {
+    if (act == 1) {
+        float t = fmaxf(v, 0.0f);
+        return t * t;
+    }
+    return v;
+}
+
+// Sum over the 64 lanes of a wave; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, kWave));
+    return v;
+}
+
+// Two f32 values that are exact in bf16 (e.g. small integers): keep their high
+// halves, `lo` in bits 0..15 and `hi` in bits 16..31.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Sixteen int8 weights (one 16-byte load, columns c0..c0+15 of a row) as the
+// two bf16x8 matrix-core operands: columns c0..c0+7 and c0+8..c0+15.  Integers
+// in [-128, 127] are exact in bf16.
+__device__ __forceinline__ void q16_to_bf16(const uint4 w, bf16x8 &k0, bf16x8 &k1) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t p[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int v = (int)in[j];
+        const float f0 = (float)(int8_t)(v);
+        const float f1 = (float)(int8_t)(v >> 8);
+        const float f2 = (float)(int8_t)(v >> 16);
+        const float f3 = (float)(v >> 24);
+        p[2 * j] = pack_bf16_exact(f0, f1);
+        p[2 * j + 1] = pack_bf16_exact(f2, f3);
+    }
+    __builtin_memcpy(&k0, &p[0], 16);
+    __builtin_memcpy(&k1, &p[4], 16);
+}
+
+// Sixteen int8 as f32 into `f`, column order.
+__device__ __forceinline__ void q16_to_f32(const uint4 w, float f[16]) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int v = (int)in[j];
+        f[4 * j + 0] = (float)(int8_t)(v);
+        f[4 * j + 1] = (float)(int8_t)(v >> 8);
+        f[4 * j + 2] = (float)(int8_t)(v >> 16);
+        f[4 * j + 3] = (float)(v >> 24);
+    }
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, const f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+// Round-to-nearest-even bf16 of an f32 (the gfx950 packed converter).
+__device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
+
+}  // namespace pg
