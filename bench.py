@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Throughput of the packed-weight product path on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input:
+  * the q8 decode layer frame at one position (hidden 4096: QKV 4096->6144,
+    residual add + RMSNorm, up 4096->14336 with relu^2, down 14336->4096,
+    residual add + RMSNorm, head 4096->32000), and
+  * the same frame as one prefill pass over 64 positions.
+Two weight copies (2 x 342 MB, more than the 256 MB Infinity Cache) alternate
+between steps so the weights stream from HBM.  `value` is the decode frame's
+weight-stream rate (weight bytes per frame / frame time, GB/s); the prefill
+rate (positions/s) is reported beside it.  After the timed steps (not part of
+ms_per_step) the other workloads are measured: the 1024x1024 GEMV + add +
+RMSNorm, the 4096x4096 f16 GEMV over 16 rotated copies, the 420-position
+prompt as 6 x 64 + 36, and the routed-MoE pass.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-components", action="store_true", help="only the timed steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- helpers
+
+class Timer:
+    """Pairs of HIP events on torch's current stream (the stream libpg launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def total_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs)
+
+
+def file_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel_src):
+    """HBM bytes per launch of the decode GEMV from the committed counter summary,
+    or None if missing or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemv_q8_decode_frame_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    t = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != file_hash(kernel_src):
+        return None
+    return float(t.group(1))
+
+
+def to_dev(torch, a):
+    import numpy as np
+    return torch.as_tensor(np.ascontiguousarray(a)).to("cuda")
+
+
+def q8_dev(torch, pg, m):
+    return pg.Q8Weight(to_dev(torch, m.q), to_dev(torch, m.scale), to_dev(torch, m.bias))
+
+
+def make_frames(torch, pg, synth, n_list, copies=2):
+    frames = {n: [] for n in n_list}
+    nbytes = None
+    for c in range(copies):
+        f = synth.frame_weights(seed=c)
+        W = {k: q8_dev(torch, pg, f[k]) for k in ("qkv", "up", "down", "head")}
+        w1, w2 = to_dev(torch, f["w1"]), to_dev(torch, f["w2"])
+        for n in n_list:
+            frames[n].append(pg.Frame(W["qkv"], W["up"], W["down"], W["head"], w1, w2, f["eps"], n=n))
+        nbytes = sum(w.nbytes() for w in W.values())
+        del f
+    return frames, nbytes
+
+
+# ----------------------------------------------------------------- timed step
+
+def run_step(torch, dec, pre, inp, timers, gemv_timer):
+    """One decode frame + one 64-position prefill pass; events around each part
+    and around every decode GEMV launch."""
+    inp["h1"].copy_(inp["h1_0"])
+    inp["h64"].copy_(inp["h64_0"])
+    s = timers["decode"].start()
+    b = dec.buf
+    H = dec.hidden
+    for name, x, y, act, norm in (("qkv", inp["x1"], b["qkv"], 0, "w1"), ("up", b["x1"], b["u"], 1, None),
+                                  ("down", b["u"], b["d"], 0, "w2"), ("head", b["x2"], b["logits"], 0, None)):
+        g = gemv_timer.start()
+        dec._mm(name, x, y, act)
+        gemv_timer.stop(g)
+        if name == "qkv":
+            dec_norm(dec, inp["h1"], b["qkv"][:, :H], dec.w1, b["x1"], b["qkv"].shape[1])
+        elif name == "down":
+            dec_norm(dec, inp["h1"], b["d"], dec.w2, b["x2"], None)
+    timers["decode"].stop(s)
+    s = timers["prefill"].start()
+    pre.run(inp["x64"], inp["h64"])
+    timers["prefill"].stop(s)
+
+
+def dec_norm(fr, h, d, w, out, stride):
+    import prefill_gemm_amd as pg
+    pg.add_rmsnorm(h, d, w, fr.eps, out=out, delta_stride=stride)
+
+
+# ----------------------------------------------------------------- components
+
+def component_f16(torch, pg, synth, reps=100, copies=16):
+    rng = synth.streams(7, copies + 1)
+    Ws = [to_dev(torch, synth.f16(rng[i], 4096, 4096)) for i in range(copies)]
+    x = to_dev(torch, synth.normal(rng[copies], 4096))
+    y = torch.empty(4096, device="cuda")
+    for i in range(copies):
+        pg.gemv_f16(Ws[i], x, y)
+    t = Timer(torch)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for r in range(reps):
+        s = t.start()
+        pg.gemv_f16(Ws[r % copies], x, y)
+        t.stop(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = t.total_ms() / reps
+    nbytes = 4096 * 4096 * 2
+    return {"workload": "f16 GEMV 4096x4096, 100 reps over 16 rotated copies",
+            "us_per_gemv": round(per * 1e3, 3), "GB_s": round(nbytes / (per * 1e-3) / 1e9, 1),
+            "GB_s_wall": round(reps * nbytes / wall / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def component_gemv_norm(torch, pg, synth, reps=200):
+    c = synth.gemv_add_norm(0)
+    W = q8_dev(torch, pg, c["W"])
+    x, w = to_dev(torch, c["x"]), to_dev(torch, c["w"])
+    h = to_dev(torch, c["h"]).view(1, -1)
+    y = torch.empty(1024, device="cuda")
+    out = torch.empty(1, 1024, device="cuda")
+    for _ in range(5):
+        pg.gemv_q8(W, x, y)
+        pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
+    t = Timer(torch)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        s = t.start()
+        pg.gemv_q8(W, x, y)
+        pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
+        t.stop(s)
+    torch.cuda.synchronize()
+    return {"workload": "q8 GEMV 1024x1024 + add + RMSNorm (cache resident)",
+            "us_per_pair": round(t.total_ms() / reps * 1e3, 3)}
+
+
+def component_prompt(torch, frames, inp, reps=3):
+    """420 positions as 6 passes of 64 and one of 36."""
+    f64, f36 = frames[64][0], frames[36][0]
+    for _ in range(2):
+        f36.run(inp["x64"][:36].contiguous(), inp["h64"][:36].contiguous())
+    t = Timer(torch)
+    x36 = inp["x64"][:36].contiguous()
+    h36 = inp["h64"][:36].contiguous()
+    torch.cuda.synchronize()
+    for r in range(reps):
+        s = t.start()
+        for p in range(6):
+            frames[64][p % 2].run(inp["x64"], inp["h64"])
+        frames[36][r % 2].run(x36, h36)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.total_ms() / reps
+    return {"workload": "420-position prompt = 6 passes x 64 + 1 x 36, q8 frame",
+            "ms": round(ms, 3), "positions_per_s": round(420 / (ms * 1e-3), 1)}
+
+
+def component_moe(torch, pg, synth, reps=10):
+    c = synth.moe(0)
+    up, down = q8_dev(torch, pg, c["up"]), q8_dev(torch, pg, c["down"])
+    X, Wr, w = to_dev(torch, c["X"]), to_dev(torch, c["Wr"]), to_dev(torch, c["w"])
+    h0 = to_dev(torch, c["h"])
+    h = h0.clone()
+    n, H = c["X"].shape
+    I = c["up"].q.shape[1]
+    ws = torch.empty(pg.moe_grouped_workspace_bytes(n, H, I, Wr.shape[0], c["top_k"]), dtype=torch.uint8,
+                     device="cuda")
+    o = pg.moe_grouped(X, Wr, up, down, h, w, c["eps"], c["top_k"], workspace=ws)
+    torch.cuda.synchronize()
+    distinct = int((o["counts"] > 0).sum().item())
+    t = Timer(torch)
+    for _ in range(reps):
+        h.copy_(h0)
+        s = t.start()
+        pg.moe_grouped(X, Wr, up, down, h, w, c["eps"], c["top_k"], workspace=ws, outputs=o)
+        t.stop(s)
+    torch.cuda.synchronize()
+    ms = t.total_ms() / reps
+    per_expert = (I * H + H * I) * 1.25
+    nbytes = distinct * per_expert + Wr.numel() * 4
+    return {"workload": "routed MoE pass: 64 positions, hidden 2688, 128 experts 2688->1856->2688, top-6",
+            "distinct_experts": distinct, "ms": round(ms, 3),
+            "positions_per_s": round(n / (ms * 1e-3), 1),
+            "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(synth):
+    """The oracle (plain f64 C, OpenMP over outputs) on the decode frame's four
+    products at one position, repeated until about 10 s of CPU work."""
+    import numpy as np
+    import oracle
+    f = synth.frame_weights(seed=0)
+    rng = np.random.default_rng(0)
+    xs = {k: synth.normal(rng, f[k].cols) for k in ("qkv", "up", "down", "head")}
+    nbytes = sum(f[k].nbytes() for k in xs)
+    frames = 0
+    t0 = time.perf_counter()
+    while True:
+        for k, x in xs.items():
+            oracle.gemm_q8(f[k].q, f[k].scale, f[k].bias, x)
+        frames += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or frames >= 200:
+            break
+    return {"value": round(frames * nbytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{frames} decode frames (QKV, up, down, head q8 products at one position, "
+                      f"{nbytes / 1e6:.1f} MB of weights each) in {el:.1f} s"}
+
+
+# ----------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU part in this build "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        n = 1 << 28                      # 1 GiB f32 copy
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n * 4} bytes x3")
+        return
+    import prefill_gemm_amd as pg
+    import synth
+
+    log("building inputs ...")
+    frames, frame_bytes = make_frames(torch, pg, synth, (1, 64, 36))
+    rng = synth.streams(11, 4)
+    inp = {"x1": to_dev(torch, synth.normal(rng[0], (1, 4096))),
+           "h1_0": to_dev(torch, synth.normal(rng[1], (1, 4096))),
+           "x64": to_dev(torch, synth.normal(rng[2], (64, 4096))),
+           "h64_0": to_dev(torch, synth.normal(rng[3], (64, 4096)))}
+    inp["h1"] = inp["h1_0"].clone()
+    inp["h64"] = inp["h64_0"].clone()
+
+    log(f"warmup {args.warmup} steps ...")
+    for i in range(args.warmup):
+        run_step(torch, frames[1][i % 2], frames[64][i % 2], inp,
+                 {"decode": Timer(torch), "prefill": Timer(torch)}, Timer(torch))
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps ...")
+    timers = {"decode": Timer(torch), "prefill": Timer(torch)}
+    gemv_t = Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(torch, frames[1][i % 2], frames[64][i % 2], inp, timers, gemv_t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    K = args.steps
+    dec_ms = timers["decode"].total_ms() / K
+    pre_ms = timers["prefill"].total_ms() / K
+    gemv_launches = 4 * K
+    gemv_avg_ms = gemv_t.total_ms() / gemv_launches
+    gemv_bytes_per_launch = frame_bytes / 4
+    achieved = gemv_bytes_per_launch / (gemv_avg_ms * 1e-3) / 1e9
+    value = frame_bytes / (dec_ms * 1e-3) / 1e9
+    flops_pass = 2 * 64 * sum(w.rows * w.cols for w in frames[64][0].W.values())
+    traffic = recorded_traffic(os.path.join(ROOT, "prefill_gemm_amd", "csrc", "gemv.hip"))
+
+    result = {
+        "metric": "weight-stream HBM GB/s (q8 GEMV decode) + prefill positions/s at B=64",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 weights (q8 block), f32 activations, f32 accumulate",
+        "data": "synthetic (seeded numpy: q8 U[-127,127], scale U(1e-3,1e-2), bias N(0,1e-3); x,h N(0,1))",
+        "config": {"workload": "q8 layer frame, hidden 4096 (QKV 6144, up 14336 relu^2, down, head 32000, "
+                               "2x add+RMSNorm): decode at 1 position + prefill pass at 64 positions",
+                   "decode_batch": 1, "prefill_batch": 64, "weight_copies_rotated": 2,
+                   "frame_weight_bytes": frame_bytes},
+        "decode_frame_us": round(dec_ms * 1e3, 2),
+        "decode_tokens_per_s": round(1.0 / (dec_ms * 1e-3), 1),
+        "prefill_pass_us": round(pre_ms * 1e3, 2),
+        "prefill_positions_per_s": round(64 / (pre_ms * 1e-3), 1),
+        "prefill_frac_hbm_peak": round(frame_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "prefill_frac_mfma_bf16_peak": round(flops_pass / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": "gemv_q8_kernel (decode GEMV, 4 launches a frame)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(gemv_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": gemv_bytes_per_launch},
+    }
+    if not args.no_components:
+        log("components ...")
+        comp = {"gemv_add_norm_1024": component_gemv_norm(torch, pg, synth),
+                "f16_gemv_4096": component_f16(torch, pg, synth),
+                "prompt_420": component_prompt(torch, frames, inp)}
+        del frames
+        torch.cuda.empty_cache()
+        comp["moe_pass"] = component_moe(torch, pg, synth)
+        result["components"] = comp
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(synth)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,8 +16,11 @@ LIB = os.path.join(HERE, "libpg.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed f32 vector arithmetic is generated (v_pk_*_f32).
+# -amdgpu-mfma-vgpr-form: matrix-core results stay in VGPRs, where the vector
+# ALU applies the block scales (no copies through the accumulation registers).
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 

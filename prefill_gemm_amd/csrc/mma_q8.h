@@ -22,6 +22,8 @@
 // each wave streams its own weights straight from HBM, 16 bytes a lane.
 #pragma once
 
+#include <utility>
+
 #include "pg_device.h"
 
 namespace pg {
@@ -33,13 +35,18 @@ namespace pg {
 //  xs: 64 bytes per (row, group g of 16 blocks): [h][part][8 bf16], element i of half h is
 //      the sum of the row's X over block 16 g + 8 h + i (zero past the last block).
 //  The row after the last is all zeros; tile rows past the valid count read it.
+//  This "row" layout serves gathered A rows (expert entries).  The dense pass
+//  (A row m = position m) uses the "fragment" layout instead, in which the 64
+//  lanes of one matrix-core fragment are contiguous (one 1 KB load a fragment):
+//  xp: [blk][mt][fi = part * 2 + ks][lane = m % 32 + 32 h] 16 bytes each;
+//  xs: [g][mt][part][lane = m % 32 + 32 h] 16 bytes each; rows past n are zero.
 struct MmaPanel {
     const int8_t *q;
     const float *scale;
     const float *bias;
     int rows, cols;
-    const uint4 *xp;
-    const uint4 *xs;
+    const u32x4 *xp;
+    const u32x4 *xs;
     int zero_row;
     const int32_t *src_list;  // A row m reads staged row src_list[m] / src_div (NULL: row m)
     int src_div;
@@ -48,7 +55,19 @@ struct MmaPanel {
     long long ldo;
     const int32_t *out_list;  // orow(m) = out_list[m] (NULL: m)
     int act;
+    int frag;                 // 1: fragment layout (dense rows, MT tiles staged), 0: row layout
 };
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that f can
+// index register arrays with a compile-time constant.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kPanelRows = 128;
 constexpr int kChunk = 4;
@@ -58,9 +77,20 @@ __device__ __forceinline__ int lds_index(int buf, int kbl, int mt, int fi, int l
     return (((buf * kChunk + kbl) * MT + mt) * 4 + fi) * 64 + lane;
 }
 
-template <int MT>
+// One workgroup's share of the product: weight rows [r_base, r_base + 128),
+// blocks [kb0, kb1), all A rows.  Software pipeline, per chunk c of kChunk blocks:
+//   - the A fragments of chunk c+1 (in registers since two chunks ago) go to
+//     LDS buffer (c+1) & 1 and chunk c+3 is requested into the freed registers;
+//   - chunk c is contracted from LDS buffer c & 1 and the weight registers of
+//     ring slot c % WCH, which are then refilled with chunk c + WCH;
+//   - one barrier closes the chunk.
+// Every load is unconditional (block index clamped into the range, so the
+// loads past the end re-read the last block) and every register array is
+// indexed by compile-time constants, so nothing leaves the register file.
+template <int MT, int WCH>
 __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, const int kb0,
-                                          const int kb1, uint4 *lds) {
+                                          const int kb1, u32x4 *lds) {
+    static_assert(WCH % 2 == 0, "the ring walk keeps the LDS buffer parity static");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -78,12 +108,89 @@ __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, c
     }
 
     // The weight row this lane feeds to the matrix core and owns in the output.
-    const int r = r_base + wave * 32 + ml;
+    // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane
+    // offset, so the per-block address arithmetic stays off the vector ALU.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int row_base = r_base + wave_u * 32;
+    const int r = row_base + ml;
     const bool r_ok = r < P.rows;
-    const long long rl = r_ok ? r : P.rows - 1;
-    const int8_t *qrow = P.q + rl * P.cols + 16 * h;
-    const float *scrow = P.scale + rl * nb;
-    const float *birow = P.bias + rl * nb;
+    const int rl = r_ok ? r : P.rows - 1;
+    const int q_off = (rl - row_base) * P.cols + 16 * h;
+    const int s_off = (rl - row_base) * nb;
+    const int8_t *q_wave = P.q + (long long)row_base * P.cols;
+    const float *sc_wave = P.scale + (long long)row_base * nb;
+    const float *birow = P.bias + (long long)rl * nb;
+
+    // This lane's A fragment of tile mt and block blk is
+    //   a_base + blk * a_step + mt * a_mt + a_off[mt]   (a_off: lane part),
+    // its block-sum fragment of group g and part p is
+    //   P.xs + g * s_step + p * s_part + s_lane[mt].
+    long long a_step, a_mt, s_step;
+    int s_part;
+    int a_off[MT], s_lane[MT];
+    const u32x4 *a_base;
+    if (P.frag) {
+        a_base = P.xp + wave_u * 64;
+        a_step = MT * 4 * 64;
+        a_mt = 4 * 64;
+        s_step = MT * 2 * 64;
+        s_part = 64;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            a_off[mt] = lane;
+            s_lane[mt] = mt * 2 * 64 + lane;
+        }
+    } else {
+        a_base = P.xp + wave_u;
+        a_step = 8;
+        a_mt = 0;
+        s_step = 4;
+        s_part = 1;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            a_off[mt] = (srow[mt] * nb * 2 + h) * 4;
+            s_lane[mt] = srow[mt] * ng * 4 + 2 * h;
+        }
+    }
+
+    const int nblk = kb1 - kb0;
+    const int nchunks = (nblk + kChunk - 1) / kChunk;
+    auto blk_of = [&](int c, int kbl) __attribute__((always_inline)) { return min(kb0 + c * kChunk + kbl, kb1 - 1); };
+
+    u32x4 wq[WCH][kChunk];
+    float ws[WCH][kChunk];
+    u32x4 st[2][kChunk * MT];
+
+    auto load_w = [&](int c, u32x4 (&q)[kChunk], float (&s)[kChunk]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kbl = 0; kbl < kChunk; ++kbl) {
+            const int b = blk_of(c, kbl);
+            q[kbl] = *reinterpret_cast<const u32x4 *>(q_wave + (long long)b * 32 + q_off);
+            s[kbl] = sc_wave[(long long)b + s_off];
+        }
+    };
+    auto load_a = [&](int c, u32x4 (&dst)[kChunk * MT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kChunk * MT; ++i) {
+            const int kbl = i / MT, mt = i % MT;
+            const u32x4 *base = a_base + (long long)blk_of(c, kbl) * a_step + mt * a_mt;
+            dst[i] = base[a_off[mt]];
+        }
+    };
+    auto store_a = [&](int buf, const u32x4 (&src)[kChunk * MT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kChunk * MT; ++i)
+            lds[lds_index<MT>(buf, i / MT, i % MT, wave, lane)] = src[i];
+    };
+
+    // Prologue: weights of the first WCH chunks, A of chunk 0 in LDS, A of
+    // chunks 1 and 2 on their way.
+#pragma unroll
+    for (int u = 0; u < WCH; ++u) load_w(u, wq[u], ws[u]);
+    load_a(0, st[0]);
+    store_a(0, st[0]);
+    load_a(1, st[1]);
+    load_a(2, st[0]);
 
     f32x16 acc[MT];
 #pragma unroll
@@ -97,93 +204,48 @@ __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, c
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int blk = 16 * g + 8 * h + i;
-            const float v = (blk >= kb0 && blk < kb1) ? birow[blk] : 0.0f;
-            bb[i] = to_bf16(v);
+            const bool in = blk >= kb0 && blk < kb1;
+            const float v = birow[in ? blk : kb0];
+            bb[i] = to_bf16(in ? v : 0.0f);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const uint4 *xr = P.xs + ((long long)srow[mt] * ng + g) * 4 + 2 * h;
-            acc[mt] = mfma_bf16(as_bf16x8(xr[0]), bb, acc[mt]);
-            acc[mt] = mfma_bf16(as_bf16x8(xr[1]), bb, acc[mt]);
+            const u32x4 *xr = P.xs + g * s_step;
+            acc[mt] = mfma_bf16(as_bf16x8(xr[s_lane[mt]]), bb, acc[mt]);
+            acc[mt] = mfma_bf16(as_bf16x8(xr[s_lane[mt] + s_part]), bb, acc[mt]);
         }
     }
-
-    // Main contraction.  Thread `tid` stages, for every (block, tile) of a
-    // chunk, the fragment of type fi = wave (hi/lo x k-step) for its lane.
-    const int nblk = kb1 - kb0;
-    const int nchunks = (nblk + kChunk - 1) / kChunk;
-    uint4 st[kChunk * MT];
-    uint4 wq[kChunk], wq_n[kChunk];
-    float ws[kChunk], ws_n[kChunk];
-
-    auto load_a = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < kChunk * MT; ++i) {
-            const int kbl = i / MT, mt = i % MT;
-            const int blk = kb0 + c * kChunk + kbl;
-            if (blk < kb1)
-                st[i] = P.xp[(((long long)srow[mt] * nb + blk) * 2 + h) * 4 + wave];
-        }
-    };
-    auto store_a = [&](int c, int buf) {
-#pragma unroll
-        for (int i = 0; i < kChunk * MT; ++i) {
-            const int kbl = i / MT, mt = i % MT;
-            const int blk = kb0 + c * kChunk + kbl;
-            if (blk < kb1) lds[lds_index<MT>(buf, kbl, mt, wave, lane)] = st[i];
-        }
-    };
-    auto load_w = [&](int c, uint4 *q, float *s) {
-#pragma unroll
-        for (int kbl = 0; kbl < kChunk; ++kbl) {
-            const int blk = kb0 + c * kChunk + kbl;
-            if (blk < kb1) {
-                q[kbl] = *reinterpret_cast<const uint4 *>(qrow + blk * 32);
-                s[kbl] = scrow[blk];
-            }
-        }
-    };
-
-    load_a(0);
-    load_w(0, wq, ws);
-    store_a(0, 0);
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        const bool more = c + 1 < nchunks;
-        if (more) {
-            load_a(c + 1);
-            load_w(c + 1, wq_n, ws_n);
-        }
+
+    auto chunk_step = [&](auto uc, const int c0) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        const int c = c0 + u;
+        if (c < nchunks) {
+            store_a((u + 1) & 1, st[(u + 1) & 1]);
+            load_a(c + 3, st[(u + 1) & 1]);
+            // A block past kb1 (last chunk only) re-reads the last block and is
+            // weighted by zero, which keeps the chunk one branch-free stretch.
 #pragma unroll
-        for (int kbl = 0; kbl < kChunk; ++kbl) {
-            const int blk = kb0 + c * kChunk + kbl;
-            if (blk < kb1) {
+            for (int kbl = 0; kbl < kChunk; ++kbl) {
                 bf16x8 b0, b1;
-                q16_to_bf16(wq[kbl], b0, b1);
+                q16_to_bf16(wq[u][kbl], b0, b1);
+                const float s = kb0 + c * kChunk + kbl < kb1 ? ws[u][kbl] : 0.0f;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const uint4 *f = lds + lds_index<MT>(buf, kbl, mt, 0, lane);
+                    const u32x4 *f = lds + lds_index<MT>(u & 1, kbl, mt, 0, lane);
                     f32x16 t = mfma_bf16(as_bf16x8(f[0]), b0, zero);
                     t = mfma_bf16(as_bf16x8(f[64]), b1, t);
                     t = mfma_bf16(as_bf16x8(f[128]), b0, t);
                     t = mfma_bf16(as_bf16x8(f[192]), b1, t);
-                    const float s = ws[kbl];
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[mt][v] = fmaf(s, t[v], acc[mt][v]);
                 }
             }
-        }
-        if (more) {
-            store_a(c + 1, buf ^ 1);
-#pragma unroll
-            for (int kbl = 0; kbl < kChunk; ++kbl) {
-                wq[kbl] = wq_n[kbl];
-                ws[kbl] = ws_n[kbl];
-            }
+            load_w(c + WCH, wq[u], ws[u]);
         }
         __syncthreads();
-    }
+    };
+    for (int c0 = 0; c0 < nchunks; c0 += WCH) static_for<WCH>([&](auto uc) __attribute__((always_inline)) { chunk_step(uc, c0); });
 
     // Output: element v of tile mt is A row 32 mt + 8 (v / 4) + 4 h + (v % 4), column r.
     if (r_ok) {

@@ -13,6 +13,8 @@
 
 namespace pg {
 
+constexpr int kWch = 2;  // weight chunks in flight per wave
+
 // One thread per (row, 16-column half block), over rows + 1 rows (the last is
 // the zero row) and 16 * ng blocks per row (blocks past the last give zeros in xs).
 __global__ __launch_bounds__(256) void stage_x_kernel(const float *__restrict__ X, int rows,
@@ -68,6 +70,61 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const float *__restrict__ 
     }
 }
 
+// Fragment layout for the dense pass (see mma_q8.h): one thread per (row m,
+// 16-column half block) over mts * 32 rows (rows >= n are zero) and 16 * ng blocks.
+__global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
+                                                           int cols, int mts, u32x4 *__restrict__ xp,
+                                                           __bf16 *__restrict__ xs) {
+    const int nb = cols >> 5;
+    const int ng = (nb + 15) >> 4;
+    const int per_row = ng * 32;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int m = (int)(t / per_row);
+    const int hb = (int)(t % per_row);
+    const int blk = hb >> 1, h = hb & 1;
+    if (m >= mts * 32) return;
+    const int mt = m >> 5, lane = (m & 31) + 32 * h;
+    const bool live = m < n && blk < nb;
+    float v[16];
+    if (live) {
+        const float4 *src = reinterpret_cast<const float4 *>(X + (long long)m * cols + 32 * blk + 16 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = src[j];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    __bf16 hi[16], lo[16];
+    float half_sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        hi[i] = to_bf16(v[i]);
+        lo[i] = to_bf16(v[i] - (float)hi[i]);
+        half_sum += v[i];
+    }
+    if (blk < nb) {
+        u32x4 rec[4];
+        __builtin_memcpy(&rec[0], &hi[0], 16);
+        __builtin_memcpy(&rec[1], &hi[8], 16);
+        __builtin_memcpy(&rec[2], &lo[0], 16);
+        __builtin_memcpy(&rec[3], &lo[8], 16);
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) xp[(((long long)blk * mts + mt) * 4 + fi) * 64 + lane] = rec[fi];
+    }
+    const float block_sum = half_sum + __shfl_xor(half_sum, 1, kWave);
+    if (h == 0) {
+        const __bf16 s_hi = to_bf16(block_sum);
+        const __bf16 s_lo = to_bf16(block_sum - (float)s_hi);
+        const int g = blk >> 4, hh = (blk >> 3) & 1, i = blk & 7;
+        const int sl = (m & 31) + 32 * hh;
+        xs[((((long long)g * mts + mt) * 2 + 0) * 64 + sl) * 8 + i] = s_hi;
+        xs[((((long long)g * mts + mt) * 2 + 1) * 64 + sl) * 8 + i] = s_lo;
+    }
+}
+
 int launch_stage_x(const float *X, int rows, int cols, void *xp, void *xs, hipStream_t s) {
     const int nb = cols / 32, ng = (nb + 15) / 16;
     const long long threads = (long long)(rows + 1) * ng * 32;
@@ -84,7 +141,7 @@ int launch_stage_x(const float *X, int rows, int cols, void *xp, void *xs, hipSt
 template <int MT>
 __global__ __launch_bounds__(256) void mma_dense_kernel(MmaPanel P, int splits, int bps,
                                                         float *partials, long long plane) {
-    __shared__ uint4 lds[2 * kChunk * MT * 4 * 64];
+    __shared__ u32x4 lds[2 * kChunk * MT * 4 * 64];
     const int id = blockIdx.x;
     const int split = id % splits, panel = id / splits;
     const int nb = P.cols >> 5;
@@ -94,7 +151,7 @@ __global__ __launch_bounds__(256) void mma_dense_kernel(MmaPanel P, int splits, 
         P.out = partials + (long long)split * plane;
         P.act = 0;
     }
-    mma_panel<MT>(P, panel * kPanelRows, kb0, kb1, lds);
+    mma_panel<MT, kWch>(P, panel * kPanelRows, kb0, kb1, lds);
 }
 
 // Y[i] = act( sum_{s < splits} parts[s][i] ), the splits added in order.
@@ -113,7 +170,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 __global__ __launch_bounds__(256) void mma_expert_kernel(MmaPanel P, const int32_t *counts,
                                                          const int32_t *lists, int cap,
                                                          long long q_stride, long long s_stride) {
-    __shared__ uint4 lds[2 * kChunk * 2 * 4 * 64];
+    __shared__ u32x4 lds[2 * kChunk * 2 * 4 * 64];
     const int e = blockIdx.y;
     const int cnt = min(counts[e], min(cap, 64));
     if (cnt <= 0) return;
@@ -125,9 +182,9 @@ __global__ __launch_bounds__(256) void mma_expert_kernel(MmaPanel P, const int32
     P.m_valid = cnt;
     const int nb = P.cols >> 5;
     if (cnt > 32)
-        mma_panel<2>(P, blockIdx.x * kPanelRows, 0, nb, lds);
+        mma_panel<2, kWch>(P, blockIdx.x * kPanelRows, 0, nb, lds);
     else
-        mma_panel<1>(P, blockIdx.x * kPanelRows, 0, nb, lds);
+        mma_panel<1, kWch>(P, blockIdx.x * kPanelRows, 0, nb, lds);
 }
 
 int launch_expert_bank(const MmaPanel &P, int experts, const int32_t *counts,
@@ -155,9 +212,15 @@ int dense_splits(int rows, int cols) {
 
 using namespace pg;
 
+// Fragment-layout staging sizes of n rows (mts tiles of 32 rows).
+static size_t frag_x_bytes(int n, int cols) { return (size_t)ceil_div(n, 32) * cols * 128; }
+static size_t frag_s_bytes(int n, int cols) {
+    return (size_t)ceil_div(n, 32) * ceil_div(cols / 32, 16) * 2048;
+}
+
 extern "C" size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n) {
     if (rows <= 0 || cols <= 0 || n <= 0 || cols % 32) return 0;
-    size_t bytes = round_up(stage_x_bytes(n, cols), 256) + round_up(stage_s_bytes(n, cols), 256);
+    size_t bytes = round_up(frag_x_bytes(n, cols), 256) + round_up(frag_s_bytes(n, cols), 256);
     const int s = dense_splits(rows, cols);
     if (s > 1) bytes += (size_t)s * n * rows * sizeof(float);
     return bytes;
@@ -178,11 +241,19 @@ extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float 
 
     char *ws = static_cast<char *>(workspace);
     void *xp = ws;
-    void *xs = ws + round_up(stage_x_bytes(n, cols), 256);
-    float *parts = reinterpret_cast<float *>(ws + round_up(stage_x_bytes(n, cols), 256) +
-                                             round_up(stage_s_bytes(n, cols), 256));
-    int rc = launch_stage_x(X, n, cols, xp, xs, s);
-    if (rc) return rc;
+    void *xs = ws + round_up(frag_x_bytes(n, cols), 256);
+    float *parts = reinterpret_cast<float *>(ws + round_up(frag_x_bytes(n, cols), 256) +
+                                             round_up(frag_s_bytes(n, cols), 256));
+    const int mts = ceil_div(n, 32);
+    {
+        const int nb = cols / 32, ng = (nb + 15) / 16;
+        const long long threads = (long long)mts * 32 * ng * 32;
+        hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           X, n, cols, mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs));
+        int rc = launch_status();
+        if (rc) return rc;
+    }
+    int rc = PG_OK;
 
     MmaPanel P{};
     P.q = q;
@@ -190,9 +261,10 @@ extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float 
     P.bias = bias;
     P.rows = rows;
     P.cols = cols;
-    P.xp = reinterpret_cast<const uint4 *>(xp);
-    P.xs = reinterpret_cast<const uint4 *>(xs);
+    P.xp = reinterpret_cast<const u32x4 *>(xp);
+    P.xs = reinterpret_cast<const u32x4 *>(xs);
     P.zero_row = n;
+    P.frag = 1;
     P.src_list = nullptr;
     P.src_div = 1;
     P.m_valid = n;

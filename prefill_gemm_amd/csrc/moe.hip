@@ -213,13 +213,14 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     up.bias = up_bias;
     up.rows = I;
     up.cols = H;
-    up.xp = reinterpret_cast<const uint4 *>(ws + L.xp_x);
-    up.xs = reinterpret_cast<const uint4 *>(ws + L.xs_x);
+    up.xp = reinterpret_cast<const u32x4 *>(ws + L.xp_x);
+    up.xs = reinterpret_cast<const u32x4 *>(ws + L.xs_x);
     up.zero_row = n;
     up.src_div = top_k;
     up.out = U;
     up.ldo = I;
     up.act = 1;
+    up.frag = 0;
     if ((rc = launch_expert_bank(up, E, counts, lists, n, s))) return rc;
 
     if ((rc = launch_stage_x(U, nk, I, ws + L.xp_u, ws + L.xs_u, s))) return rc;
@@ -230,13 +231,14 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     dn.bias = down_bias;
     dn.rows = H;
     dn.cols = I;
-    dn.xp = reinterpret_cast<const uint4 *>(ws + L.xp_u);
-    dn.xs = reinterpret_cast<const uint4 *>(ws + L.xs_u);
+    dn.xp = reinterpret_cast<const u32x4 *>(ws + L.xp_u);
+    dn.xs = reinterpret_cast<const u32x4 *>(ws + L.xs_u);
     dn.zero_row = nk;
     dn.src_div = 1;
     dn.out = D;
     dn.ldo = H;
     dn.act = 0;
+    dn.frag = 0;
     if ((rc = launch_expert_bank(dn, E, counts, lists, n, s))) return rc;
 
     return launch_moe_combine(h, D, route_w, n, top_k, w_norm, eps, H, out, s);

@@ -8,6 +8,8 @@ namespace pg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector (HIP's uint4 is a struct whose copies become memcpy).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 32;  // columns sharing one scale and one bias
@@ -43,7 +45,7 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
 // Sixteen int8 weights (one 16-byte load, columns c0..c0+15 of a row) as the
 // two bf16x8 matrix-core operands: columns c0..c0+7 and c0+8..c0+15.  Integers
 // in [-128, 127] are exact in bf16.
-__device__ __forceinline__ void q16_to_bf16(const uint4 w, bf16x8 &k0, bf16x8 &k1) {
+__device__ __forceinline__ void q16_to_bf16(const u32x4 w, bf16x8 &k0, bf16x8 &k1) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
     uint32_t p[8];
 #pragma unroll
@@ -61,7 +63,7 @@ __device__ __forceinline__ void q16_to_bf16(const uint4 w, bf16x8 &k0, bf16x8 &k
 }
 
 // Sixteen int8 as f32 into `f`, column order.
-__device__ __forceinline__ void q16_to_f32(const uint4 w, float f[16]) {
+__device__ __forceinline__ void q16_to_f32(const u32x4 w, float f[16]) {
     const uint32_t in[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -77,11 +79,7 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, cons
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 v) {
-    bf16x8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Round-to-nearest-even bf16 of an f32 (the gfx950 packed converter).
 __device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
