@@ -78,28 +78,50 @@ __device__ __forceinline__ int lds_index(int buf, int kbl, int mt, int fi, int l
 }
 
 // One workgroup's share of the product: weight rows [r_base, r_base + 128),
-// blocks [kb0, kb1), all A rows.  Software pipeline, per chunk c of kChunk blocks:
-//   - the A fragments of chunk c+1 (in registers since two chunks ago) go to
-//     LDS buffer (c+1) & 1 and chunk c+3 is requested into the freed registers;
-//   - chunk c is contracted from LDS buffer c & 1 and the weight registers of
-//     ring slot c % WCH, which are then refilled with chunk c + WCH;
-//   - one barrier closes the chunk.
-// Every load is unconditional (block index clamped into the range, so the
-// loads past the end re-read the last block) and every register array is
-// indexed by compile-time constants, so nothing leaves the register file.
+// blocks [kb0, kb1), all A rows.  The workgroup is 4 row groups x kKSplit
+// consumer waves plus one producer wave:
+//  - the producer copies the A fragments of chunk c+1 from global memory
+//    straight into LDS buffer (c+1) & 1 (global_load_lds_dwordx4, no
+//    registers) while the consumers work on chunk c;
+//  - consumer (g, k) owns the 32 weight rows of row group g and, inside every
+//    chunk, the blocks k, k + kKSplit, ...; it streams those weights through a
+//    register ring WCH chunks deep and contracts them against LDS buffer c & 1;
+//  - after the last chunk the kKSplit partial sums of a row group meet in LDS
+//    and the k = 0 wave adds them (in order k = 0, 1, ...) and stores.
+// Splitting K inside the workgroup puts two consumer waves on every SIMD, so
+// one wave's matrix-core chain overlaps the other's vector work, without
+// reading any weight or activation twice.  Consumers issue only weight loads,
+// so their in-order vmcnt waits cover just the weights they are about to use;
+// the producer waits for its own copies before each barrier.  Producer and
+// consumers run separate loops that pass the same number of barriers (one per
+// chunk, plus one before the first and one before the reduction).  Every load
+// address is clamped into range (blocks past kb1 re-read the last block and
+// are weighted by zero) and register arrays are indexed by compile-time
+// constants only.
+constexpr int kKSplit = 2;
+constexpr int kRowGroups = 4;
+constexpr int kConsumers = kRowGroups * kKSplit;
+constexpr int kMmaThreads = (kConsumers + 1) * 64;
+
 template <int MT, int WCH>
 __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, const int kb0,
                                           const int kb1, u32x4 *lds) {
-    static_assert(WCH % 2 == 0, "the ring walk keeps the LDS buffer parity static");
+    static_assert(kChunk % kKSplit == 0, "a chunk splits evenly between the K halves");
+    constexpr int kPer = kChunk / kKSplit;  // blocks per chunk per consumer
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nb = P.cols >> 5;
     const int ng = (nb + 15) >> 4;
     const int ml = lane & 31;
     const int h = lane >> 5;
+    const int nblk = kb1 - kb0;
+    const int nchunks = (nblk + kChunk - 1) / kChunk;
+    auto blk_of = [&](int c, int kbl) __attribute__((always_inline)) {
+        return min(kb0 + c * kChunk + kbl, kb1 - 1);
+    };
 
-    // Staged row behind A-tile row m = 32 mt + ml (the rows this lane loads).
+    // Staged row behind A-tile row m = 32 mt + ml.
     int srow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -107,11 +129,44 @@ __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, c
         srow[mt] = m < P.m_valid ? (P.src_list ? P.src_list[m] / P.src_div : m) : P.zero_row;
     }
 
+    if (wave == kConsumers) {
+        // ---------------- producer: A fragments into LDS, one chunk ahead
+        auto copy_chunk = [&](int c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kbl = 0; kbl < kChunk; ++kbl) {
+                const long long b = blk_of(c, kbl);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int fi = 0; fi < 4; ++fi) {
+                        const u32x4 *src = P.frag
+                            ? P.xp + ((b * MT + mt) * 4 + fi) * 64 + lane
+                            : P.xp + (((long long)srow[mt] * nb + b) * 2 + h) * 4 + fi;
+                        __builtin_amdgcn_global_load_lds(
+                            (const void *)src,
+                            (__attribute__((address_space(3))) void *)(lds + lds_index<MT>(buf, kbl, mt, fi, 0)),
+                            16, 0, 0);
+                    }
+            }
+        };
+        copy_chunk(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (c + 1 < nchunks) copy_chunk(c + 1, (c + 1) & 1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        __syncthreads();  // the consumers' reduction barrier
+        return;
+    }
+
+    // ---------------- consumers
+    const int rg = wave % kRowGroups;
+    const int kh = wave / kRowGroups;
     // The weight row this lane feeds to the matrix core and owns in the output.
-    // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane
-    // offset, so the per-block address arithmetic stays off the vector ALU.
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int row_base = r_base + wave_u * 32;
+    // Addresses are a wave-uniform base (scalar registers) plus a 32-bit lane offset.
+    const int row_base = r_base + rg * 32;
     const int r = row_base + ml;
     const bool r_ok = r < P.rows;
     const int rl = r_ok ? r : P.rows - 1;
@@ -121,98 +176,46 @@ __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, c
     const float *sc_wave = P.scale + (long long)row_base * nb;
     const float *birow = P.bias + (long long)rl * nb;
 
-    // This lane's A fragment of tile mt and block blk is
-    //   a_base + blk * a_step + mt * a_mt + a_off[mt]   (a_off: lane part),
-    // its block-sum fragment of group g and part p is
-    //   P.xs + g * s_step + p * s_part + s_lane[mt].
-    long long a_step, a_mt, s_step;
-    int s_part;
-    int a_off[MT], s_lane[MT];
-    const u32x4 *a_base;
-    if (P.frag) {
-        a_base = P.xp + wave_u * 64;
-        a_step = MT * 4 * 64;
-        a_mt = 4 * 64;
-        s_step = MT * 2 * 64;
-        s_part = 64;
+    u32x4 wq[WCH][kPer];
+    float ws[WCH][kPer];
+    auto load_w = [&](int c, u32x4 (&q)[kPer], float (&s)[kPer]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            a_off[mt] = lane;
-            s_lane[mt] = mt * 2 * 64 + lane;
-        }
-    } else {
-        a_base = P.xp + wave_u;
-        a_step = 8;
-        a_mt = 0;
-        s_step = 4;
-        s_part = 1;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            a_off[mt] = (srow[mt] * nb * 2 + h) * 4;
-            s_lane[mt] = srow[mt] * ng * 4 + 2 * h;
-        }
-    }
-
-    const int nblk = kb1 - kb0;
-    const int nchunks = (nblk + kChunk - 1) / kChunk;
-    auto blk_of = [&](int c, int kbl) __attribute__((always_inline)) { return min(kb0 + c * kChunk + kbl, kb1 - 1); };
-
-    u32x4 wq[WCH][kChunk];
-    float ws[WCH][kChunk];
-    u32x4 st[2][kChunk * MT];
-
-    auto load_w = [&](int c, u32x4 (&q)[kChunk], float (&s)[kChunk]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kbl = 0; kbl < kChunk; ++kbl) {
-            const int b = blk_of(c, kbl);
-            q[kbl] = *reinterpret_cast<const u32x4 *>(q_wave + (long long)b * 32 + q_off);
-            s[kbl] = sc_wave[(long long)b + s_off];
+        for (int j = 0; j < kPer; ++j) {
+            const int b = blk_of(c, kh + kKSplit * j);
+            q[j] = *reinterpret_cast<const u32x4 *>(q_wave + (long long)b * 32 + q_off);
+            s[j] = sc_wave[(long long)b + s_off];
         }
     };
-    auto load_a = [&](int c, u32x4 (&dst)[kChunk * MT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kChunk * MT; ++i) {
-            const int kbl = i / MT, mt = i % MT;
-            const u32x4 *base = a_base + (long long)blk_of(c, kbl) * a_step + mt * a_mt;
-            dst[i] = base[a_off[mt]];
-        }
-    };
-    auto store_a = [&](int buf, const u32x4 (&src)[kChunk * MT]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < kChunk * MT; ++i)
-            lds[lds_index<MT>(buf, i / MT, i % MT, wave, lane)] = src[i];
-    };
-
-    // Prologue: weights of the first WCH chunks, A of chunk 0 in LDS, A of
-    // chunks 1 and 2 on their way.
 #pragma unroll
     for (int u = 0; u < WCH; ++u) load_w(u, wq[u], ws[u]);
-    load_a(0, st[0]);
-    store_a(0, st[0]);
-    load_a(1, st[1]);
-    load_a(2, st[0]);
 
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
     const f32x16 zero{};
 
-    // Bias term over the blocks [kb0, kb1): K = 16 blocks a step, blocks of
-    // the step outside the range contribute a zero bias.
-    for (int g = kb0 >> 4; g * 16 < kb1; ++g) {
-        bf16x8 bb;
+    // Bias term over the blocks [kb0, kb1) (k = 0 waves): K = 16 blocks a step,
+    // blocks of the step outside the range contribute a zero bias.  Block-sum
+    // fragment of group g, part p for tile mt: row layout
+    // xs[(srow * ng + g) * 4 + 2 h + p], fragment layout xs[((g * MT + mt) * 2 + p) * 64 + lane].
+    if (kh == 0) {
+        for (int g = kb0 >> 4; g * 16 < kb1; ++g) {
+            bf16x8 bb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int blk = 16 * g + 8 * h + i;
-            const bool in = blk >= kb0 && blk < kb1;
-            const float v = birow[in ? blk : kb0];
-            bb[i] = to_bf16(in ? v : 0.0f);
-        }
+            for (int i = 0; i < 8; ++i) {
+                const int blk = 16 * g + 8 * h + i;
+                const bool in = blk >= kb0 && blk < kb1;
+                const float v = birow[in ? blk : kb0];
+                bb[i] = to_bf16(in ? v : 0.0f);
+            }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x4 *xr = P.xs + g * s_step;
-            acc[mt] = mfma_bf16(as_bf16x8(xr[s_lane[mt]]), bb, acc[mt]);
-            acc[mt] = mfma_bf16(as_bf16x8(xr[s_lane[mt] + s_part]), bb, acc[mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+                const long long i0 = P.frag ? (((long long)g * MT + mt) * 2) * 64 + lane
+                                            : ((long long)srow[mt] * ng + g) * 4 + 2 * h;
+                const long long i1 = P.frag ? i0 + 64 : i0 + 1;
+                acc[mt] = mfma_bf16(as_bf16x8(P.xs[i0]), bb, acc[mt]);
+                acc[mt] = mfma_bf16(as_bf16x8(P.xs[i1]), bb, acc[mt]);
+            }
         }
     }
     __syncthreads();
@@ -221,31 +224,55 @@ __device__ __forceinline__ void mma_panel(const MmaPanel &P, const int r_base, c
         constexpr int u = decltype(uc)::value;
         const int c = c0 + u;
         if (c < nchunks) {
-            store_a((u + 1) & 1, st[(u + 1) & 1]);
-            load_a(c + 3, st[(u + 1) & 1]);
-            // A block past kb1 (last chunk only) re-reads the last block and is
-            // weighted by zero, which keeps the chunk one branch-free stretch.
 #pragma unroll
-            for (int kbl = 0; kbl < kChunk; ++kbl) {
+            for (int j = 0; j < kPer; ++j) {
+                const int kbl = kh + kKSplit * j;
+                const u32x4 *f = lds + lds_index<MT>(c & 1, kbl, 0, 0, lane);
                 bf16x8 b0, b1;
-                q16_to_bf16(wq[u][kbl], b0, b1);
-                const float s = kb0 + c * kChunk + kbl < kb1 ? ws[u][kbl] : 0.0f;
+                q16_to_bf16(wq[u][j], b0, b1);
+                f32x16 t[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const u32x4 *f = lds + lds_index<MT>(u & 1, kbl, mt, 0, lane);
-                    f32x16 t = mfma_bf16(as_bf16x8(f[0]), b0, zero);
-                    t = mfma_bf16(as_bf16x8(f[64]), b1, t);
-                    t = mfma_bf16(as_bf16x8(f[128]), b0, t);
-                    t = mfma_bf16(as_bf16x8(f[192]), b1, t);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[mt][v] = fmaf(s, t[v], acc[mt][v]);
+                    const u32x4 *fm = f + mt * 4 * 64;
+                    t[mt] = mfma_bf16(as_bf16x8(fm[0]), b0, zero);
+                    t[mt] = mfma_bf16(as_bf16x8(fm[64]), b1, t[mt]);
+                    t[mt] = mfma_bf16(as_bf16x8(fm[128]), b0, t[mt]);
+                    t[mt] = mfma_bf16(as_bf16x8(fm[192]), b1, t[mt]);
                 }
+                // A block past kb1 (last chunk only) re-reads the last block and is
+                // weighted by zero, which keeps the chunk one branch-free stretch.
+                const float s = kb0 + c * kChunk + kbl < kb1 ? ws[u][j] : 0.0f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mt][v] = fmaf(s, t[mt][v], acc[mt][v]);
             }
             load_w(c + WCH, wq[u], ws[u]);
+            __syncthreads();
         }
-        __syncthreads();
     };
-    for (int c0 = 0; c0 < nchunks; c0 += WCH) static_for<WCH>([&](auto uc) __attribute__((always_inline)) { chunk_step(uc, c0); });
+    for (int c0 = 0; c0 < nchunks; c0 += WCH)
+        static_for<WCH>([&](auto uc) __attribute__((always_inline)) { chunk_step(uc, c0); });
+
+    // Partial sums of the K halves meet in LDS (the stage buffers are free now):
+    // slot [rg][k-1][mt][v][lane] for k >= 1.
+    float *red = reinterpret_cast<float *>(lds);
+    if (kh > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[((((rg * (kKSplit - 1) + kh - 1) * MT + mt) * 16 + v) * 64) + lane] = acc[mt][v];
+    }
+    __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (int k = 1; k < kKSplit; ++k)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[mt][v] += red[((((rg * (kKSplit - 1) + k - 1) * MT + mt) * 16 + v) * 64) + lane];
 
     // Output: element v of tile mt is A row 32 mt + 8 (v / 4) + 4 h + (v % 4), column r.
     if (r_ok) {

@@ -139,7 +139,7 @@ int launch_stage_x(const float *X, int rows, int cols, void *xp, void *xs, hipSt
 // read the same activation blocks land on the same XCD (ids are dealt to the
 // 8 XCDs round robin).
 template <int MT>
-__global__ __launch_bounds__(256) void mma_dense_kernel(MmaPanel P, int splits, int bps,
+__global__ __launch_bounds__(kMmaThreads) void mma_dense_kernel(MmaPanel P, int splits, int bps,
                                                         float *partials, long long plane) {
     __shared__ u32x4 lds[2 * kChunk * MT * 4 * 64];
     const int id = blockIdx.x;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 
 // Grouped expert bank: workgroup (panel of 128 rows, expert e).  An expert no
 // position chose returns at once (nemotron_prefill.rs, `pb_q8_bank`: cnt == 0).
-__global__ __launch_bounds__(256) void mma_expert_kernel(MmaPanel P, const int32_t *counts,
+__global__ __launch_bounds__(kMmaThreads) void mma_expert_kernel(MmaPanel P, const int32_t *counts,
                                                          const int32_t *lists, int cap,
                                                          long long q_stride, long long s_stride) {
     __shared__ u32x4 lds[2 * kChunk * 2 * 4 * 64];
@@ -192,7 +192,7 @@ int launch_expert_bank(const MmaPanel &P, int experts, const int32_t *counts,
     const long long q_stride = (long long)P.rows * P.cols;
     const long long s_stride = (long long)P.rows * (P.cols / 32);
     dim3 grid(ceil_div(P.rows, kPanelRows), experts);
-    hipLaunchKernelGGL(mma_expert_kernel, grid, dim3(256), 0, s, P, counts, lists, cap, q_stride,
+    hipLaunchKernelGGL(mma_expert_kernel, grid, dim3(kMmaThreads), 0, s, P, counts, lists, cap, q_stride,
                        s_stride);
     return launch_status();
 }
@@ -280,9 +280,9 @@ extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float 
     const int grid = ceil_div(rows, kPanelRows) * used;
     const long long plane = (long long)n * rows;
     if (n > 32)
-        hipLaunchKernelGGL(mma_dense_kernel<2>, dim3(grid), dim3(256), 0, s, P, used, bps, parts, plane);
+        hipLaunchKernelGGL(mma_dense_kernel<2>, dim3(grid), dim3(kMmaThreads), 0, s, P, used, bps, parts, plane);
     else
-        hipLaunchKernelGGL(mma_dense_kernel<1>, dim3(grid), dim3(256), 0, s, P, used, bps, parts, plane);
+        hipLaunchKernelGGL(mma_dense_kernel<1>, dim3(grid), dim3(kMmaThreads), 0, s, P, used, bps, parts, plane);
     rc = launch_status();
     if (rc || used == 1) return rc;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256), 0, s,
