@@ -73,6 +73,56 @@ int gemv_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows
             int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
 
 /*
+ * gemv_q8_addnorm — the residual add + RMSNorm that precedes a projection,
+ * fused into the decode product (nemotron_prefill.rs `pb_add_rms` with
+ * add = 1 feeding the next matrix stage; embryo_wide.wgsl header comment:
+ * stages are fused because every dispatch boundary costs microseconds):
+ *     h'[c]  = h[c] + delta[c]                       (delta NULL: h' = h)
+ *     x[c]   = w[c] * h'[c] / sqrt( (1/cols) sum_c h'[c]^2 + eps )
+ *     y[r]   = act( sum_c wq[r][c] * x[c] ),  r < rows, wq the q8-block weight
+ * Each workgroup stages w * h' together with sum h'^2 (the same order in
+ * every workgroup) and multiplies its finished dot products by the scalar
+ * 1/rms, so no separate pass over the activations is made.
+ *   q/scale/bias as gemv_q8 (cols = the hidden size); h, delta, w [cols] f32;
+ *   h_out [cols] f32 receives h' (NULL: not written); x_out [cols] f32
+ *   receives x (NULL: not written); y [rows] f32.  h_out, x_out and y must not
+ *   overlap each other or h, delta, w (PG_EINVAL): workgroups read the whole
+ *   of h, delta and w while others write.
+ * PG_EINVAL also for eps < 0 or NaN.  PG_EUNSUPPORTED: cols % 32 != 0, cols > 32768.
+ */
+int gemv_q8_addnorm(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                    int32_t cols, const float *h, const float *delta, const float *w, float eps,
+                    float *h_out, float *x_out, float *y, int32_t act, pg_stream_t stream);
+
+/*
+ * gemv_q8_residual / gemv_q8_normed — the residual add + RMSNorm between two
+ * decode products, split so that neither call makes an extra pass over the
+ * activations (nemotron_prefill.rs `pb_add_rms`, add = 1, between the matrix
+ * stages; embryo_wide.wgsl header comment on fusing stages to save dispatch
+ * boundaries):
+ *   gemv_q8_residual: y[r] = act( sum_c wq[r][c] * x[c] ), r < rows, and for
+ *     r < hidden:  h_out[r] = h[r] + y[r],   xw[r] = w[r] * h_out[r],
+ *     and parts[j] = sum of h_out[r]^2 over r in [8j, 8j + 8) ∩ [0, hidden),
+ *     j < ceil(hidden / 8) (f32).
+ *   gemv_q8_normed: y[r] = act( (sum_c wq[r][c] * xw[c]) / sqrt( sum_j parts[j] / cols + eps ) ),
+ *     j < ceil(cols / 8), the parts summed in the same fixed order by every
+ *     workgroup.  With xw and parts from gemv_q8_residual (cols = hidden) this
+ *     is the product of W with rmsnorm(h + y[:hidden]) * w.
+ *   x [cols] f32; y [rows] f32; h, w [hidden] f32 (hidden <= rows); h_out
+ *   [hidden] f32 (NULL: not written; h_out == h updates the residual in
+ *   place); xw [hidden] f32; parts [ceil(hidden / 8)] f32.  Outputs may not
+ *   overlap each other or the inputs (other than h_out == h): PG_EINVAL.
+ * PG_EINVAL also for eps < 0 or NaN.  PG_EUNSUPPORTED: cols % 32 != 0, cols > 32768.
+ */
+int gemv_q8_residual(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                     int32_t cols, const float *x, float *y, int32_t act, const float *h,
+                     const float *w, int32_t hidden, float *h_out, float *xw, float *parts,
+                     pg_stream_t stream);
+int gemv_q8_normed(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                   int32_t cols, const float *xw, const float *parts, float eps, float *y,
+                   int32_t act, pg_stream_t stream);
+
+/*
  * gemv_f16 — the same product with binary16 weights, f32 accumulation:
  *     y[r] = act( sum_c f16(w[r][c]) * x[c] )
  * (embryo_wide.wgsl, header comment: f16 matrices are read in place.)
@@ -102,6 +152,28 @@ int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias, int3
                     int32_t cols, const float *X, int32_t n, float *Y, int32_t act,
                     void *workspace, size_t workspace_bytes, pg_stream_t stream);
 size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n);
+
+/*
+ * prefill_gemm_q8_addnorm — prefill_gemm_q8 on rmsnorm(H + delta) * w, the
+ * add + norm done per position while the activations are staged for the
+ * matrix cores (nemotron_prefill.rs `pb_add_rms`, add = 1, then the product):
+ *     H'[b][c] = H[b][c] + delta[b * delta_stride + c]   (delta NULL: H' = H)
+ *     X[b][c]  = w[c] * H'[b][c] / sqrt( (1/cols) sum_c H'[b][c]^2 + eps )
+ *     Y[b][r]  = act( sum_c wq[r][c] * X[b][c] ),  b < n, r < rows
+ *   H [n][cols] f32; delta rows delta_stride floats apart (delta_stride >=
+ *   cols, a multiple of 4); w [cols] f32; H_out [n][cols] receives H' (NULL:
+ *   not written; H_out == H updates the residual in place); X_out [n][cols]
+ *   receives X (NULL: not written); Y [n][rows]; workspace as prefill_gemm_q8
+ *   (prefill_gemm_q8_workspace_bytes(rows, cols, n)).  Other overlaps among
+ *   H_out, X_out, H, delta, w, Y and the workspace: PG_EINVAL.
+ * Arithmetic of the product as prefill_gemm_q8.
+ * PG_EUNSUPPORTED: cols % 32 != 0, cols > 16384, n < 1 or n > 64.
+ */
+int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                            int32_t cols, const float *H, const float *delta, int32_t delta_stride,
+                            const float *w, float eps, int32_t n, float *H_out, float *X_out,
+                            float *Y, int32_t act, void *workspace, size_t workspace_bytes,
+                            pg_stream_t stream);
 
 /*
  * add_rmsnorm — fused residual add + RMSNorm, per position b < n

@@ -59,7 +59,13 @@ def _declare(L):
                               _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     L.moe_grouped_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     L.moe_grouped_workspace_bytes.restype = _sz
-    for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped"):
+    L.gemv_q8_addnorm.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _P, _f, _P, _P, _P, _i32, _P]
+    L.prefill_gemm_q8_addnorm.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P, _f, _i32, _P, _P, _P,
+                                          _i32, _P, _sz, _P]
+    L.gemv_q8_residual.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P, _P, _P]
+    L.gemv_q8_normed.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _f, _P, _i32, _P]
+    for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+                 "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed"):
         getattr(L, name).restype = ctypes.c_int
 
 
@@ -141,6 +147,95 @@ def gemv_q8(W: Q8Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: in
     return y
 
 
+def _rows_view(delta: torch.Tensor | None, cols: int, name: str):
+    """Row stride of a device f32 tensor whose rows are contiguous (a view such as qkv[:, :hidden])."""
+    if delta is None:
+        return cols
+    if delta.dtype != torch.float32 or not delta.is_cuda or delta.stride(-1) != 1:
+        raise ValueError(f"{name} must be a device f32 tensor with contiguous rows")
+    if delta.shape[-1] != cols:
+        raise ValueError(f"{name} rows must have {cols} columns")
+    return delta.stride(0) if delta.dim() > 1 else cols
+
+
+def gemv_q8_addnorm(W: Q8Weight, h: torch.Tensor, delta: torch.Tensor | None, w: torch.Tensor, eps: float,
+                    y: torch.Tensor | None = None, act: int = 0, h_out: torch.Tensor | None = None,
+                    x_out: torch.Tensor | None = None, stream=None):
+    """y = act(W . (rmsnorm(h + delta) * w)) at one position; h_out/x_out receive h + delta and the
+    normed vector when given.  ``delta`` may be a view with contiguous data (e.g. qkv[:hidden])."""
+    W.validate()
+    _dev(h, torch.float32, "h")
+    _dev(w, torch.float32, "w")
+    if h.numel() != W.cols or w.numel() != W.cols:
+        raise ValueError("h and w must have W.cols elements")
+    if delta is not None:
+        if delta.dtype != torch.float32 or not delta.is_cuda or not delta.is_contiguous():
+            raise ValueError("delta must be a contiguous device f32 tensor")
+        if delta.numel() != W.cols:
+            raise ValueError("delta must have W.cols elements")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=h.device)
+    _dev(y, torch.float32, "y")
+    for t, nm in ((h_out, "h_out"), (x_out, "x_out")):
+        if t is not None:
+            _dev(t, torch.float32, nm)
+            if t.numel() != W.cols:
+                raise ValueError(f"{nm} must have W.cols elements")
+    _check("gemv_q8_addnorm", lib().gemv_q8_addnorm(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(h), _ptr(delta), _ptr(w), eps,
+        _ptr(h_out), _ptr(x_out), _ptr(y), act, _stream(stream)))
+    return y
+
+
+def norm_parts(hidden: int) -> int:
+    """Length of the sum-of-squares parts gemv_q8_residual writes for ``hidden`` rows."""
+    return -(-hidden // 8)
+
+
+def gemv_q8_residual(W: Q8Weight, x: torch.Tensor, h: torch.Tensor, w: torch.Tensor, xw: torch.Tensor,
+                     parts: torch.Tensor, y: torch.Tensor | None = None, act: int = 0,
+                     h_out: torch.Tensor | None = None, stream=None):
+    """y = act(W x); for the first len(h) rows h_out = h + y (h_out may be h), xw = w * h_out and
+    parts = sums of h_out^2 over groups of 8 rows (the input of gemv_q8_normed)."""
+    W.validate()
+    for t, nm in ((x, "x"), (h, "h"), (w, "w"), (xw, "xw"), (parts, "parts")):
+        _dev(t, torch.float32, nm)
+    hidden = h.numel()
+    if x.numel() != W.cols or w.numel() != hidden or xw.numel() != hidden or hidden > W.rows:
+        raise ValueError("x must have W.cols elements; w and xw len(h) <= W.rows")
+    if parts.numel() != norm_parts(hidden):
+        raise ValueError(f"parts must have {norm_parts(hidden)} elements")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    if h_out is not None:
+        _dev(h_out, torch.float32, "h_out")
+        if h_out.numel() != hidden:
+            raise ValueError("h_out must have len(h) elements")
+    _check("gemv_q8_residual", lib().gemv_q8_residual(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(x), _ptr(y), act, _ptr(h), _ptr(w), hidden,
+        _ptr(h_out), _ptr(xw), _ptr(parts), _stream(stream)))
+    return y
+
+
+def gemv_q8_normed(W: Q8Weight, xw: torch.Tensor, parts: torch.Tensor, eps: float, y: torch.Tensor | None = None,
+                   act: int = 0, stream=None):
+    """y = act(W xw / sqrt(sum(parts) / W.cols + eps)): the product on the RMS-normed residual that
+    gemv_q8_residual prepared."""
+    W.validate()
+    _dev(xw, torch.float32, "xw")
+    _dev(parts, torch.float32, "parts")
+    if xw.numel() != W.cols or parts.numel() != norm_parts(W.cols):
+        raise ValueError("xw must have W.cols elements and parts norm_parts(W.cols)")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=xw.device)
+    _dev(y, torch.float32, "y")
+    _check("gemv_q8_normed", lib().gemv_q8_normed(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(xw), _ptr(parts), eps, _ptr(y), act,
+        _stream(stream)))
+    return y
+
+
 def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):
     """y = act(W x) with W float16 [rows][cols], x f32 [cols], f32 accumulation."""
     _dev(W, torch.float16, "W")
@@ -174,6 +269,39 @@ def prefill_gemm_q8(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor | None = None,
     _check("prefill_gemm_q8", lib().prefill_gemm_q8(
         _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return Y
+
+
+def prefill_gemm_q8_addnorm(W: Q8Weight, H: torch.Tensor, delta: torch.Tensor | None, w: torch.Tensor,
+                            eps: float, Y: torch.Tensor | None = None, act: int = 0,
+                            H_out: torch.Tensor | None = None, X_out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None):
+    """Y [n][rows] = act((rmsnorm(H + delta) * w) . W^T) for one pass of n <= 64 positions;
+    H_out (may be H itself) and X_out receive H + delta and the normed rows when given."""
+    W.validate()
+    _dev(H, torch.float32, "H")
+    _dev(w, torch.float32, "w")
+    if H.dim() != 2 or H.shape[1] != W.cols or w.numel() != W.cols:
+        raise ValueError("H must be [n][W.cols] and w [W.cols]")
+    n = H.shape[0]
+    stride = _rows_view(delta, W.cols, "delta")
+    if delta is not None and (delta.dim() != 2 or delta.shape[0] != n):
+        raise ValueError("delta must be [n][W.cols] (rows may be strided)")
+    if Y is None:
+        Y = torch.empty(n, W.rows, dtype=torch.float32, device=H.device)
+    _dev(Y, torch.float32, "Y")
+    for t, nm in ((H_out, "H_out"), (X_out, "X_out")):
+        if t is not None:
+            _dev(t, torch.float32, nm)
+            if t.shape != H.shape:
+                raise ValueError(f"{nm} must be [n][W.cols]")
+    need = prefill_gemm_q8_workspace_bytes(W.rows, W.cols, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    _check("prefill_gemm_q8_addnorm", lib().prefill_gemm_q8_addnorm(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(H), _ptr(delta), stride, _ptr(w), eps, n,
+        _ptr(H_out), _ptr(X_out), _ptr(Y), act, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return Y
 
 

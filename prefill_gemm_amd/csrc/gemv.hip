@@ -21,6 +21,30 @@ namespace pg {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 
+// What a q8 GEMV does around its product (template argument MODE):
+//  kPlain    y = act(W x)
+//  kAddNorm  y = act(W x), x = rmsnorm(h + delta) * w built while staging;
+//            every workgroup forms the same sum of squares in the same order
+//            and multiplies its finished dot products by the scalar 1/rms
+//  kResid    y = act(W x); then for rows r < n: h_out[r] = h[r] + y[r],
+//            x_out[r] = w[r] * h_out[r], and parts[j] = the sum of h_out^2
+//            over the rows 8j .. 8j + 7 (the rows of workgroup j)
+//  kScaled   y = act((W x) / sqrt(sum_j parts[j] / cols + eps)), j < n: the
+//            consumer of a kResid product (x = its x_out), which completes
+//            the RMSNorm without another pass over the activations
+enum GemvMode { kPlain = 0, kAddNorm = 1, kResid = 2, kScaled = 3 };
+
+struct Fuse {
+    const float *h;      // residual [cols] (kAddNorm) or [n] (kResid)
+    const float *delta;  // kAddNorm: added to h first (NULL: nothing)
+    const float *w;      // norm weight
+    float eps;
+    float *h_out;        // kAddNorm / kResid: h + delta or h + y (NULL: not written)
+    float *x_out;        // kAddNorm: the normed x; kResid: w * h_out (NULL: not written)
+    float *parts;        // kResid: written; kScaled: read
+    int n;               // kResid: rows feeding the residual; kScaled: number of parts
+};
+
 // x staging: segment s (16 columns for q8, 8 for f16) of `per` float4 goes to
 // slot ((s / 64) * per + j) * 64 + (s % 64): lane l of step i reads slots
 // (i * per + j) * 64 + l, consecutive across the wave.
@@ -35,11 +59,14 @@ __device__ __forceinline__ int xslot(int s, int j) {
 // before the activation is staged), from clamped in-bounds addresses; a
 // segment past the end of the row meets zeros in the staged activation, so
 // it adds nothing.
-template <int RW, int U>
+// What happens around the product is MODE (GemvMode above).
+template <int RW, int U, int MODE>
 __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ scale, const float *__restrict__ bias,
-    int rows, int cols, const float *__restrict__ x, float *__restrict__ y, int act) {
+    int rows, int cols, const float *__restrict__ x, float *__restrict__ y, int act, Fuse nm) {
+    constexpr bool NORM = MODE == kAddNorm;
     extern __shared__ float4 sx[];
+    __shared__ float red[kGemvWaves];
     const int nseg = cols >> 4;
     const int steps = (nseg + 63) >> 6;
     const int nb = cols >> 5;
@@ -76,19 +103,69 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
     };
     load(0, wa, sa, ba);
 
+    float ss = 0.0f;
     for (int s = threadIdx.x; s < steps * 64; s += kGemvThreads) {
         float4 a[4];
         float sum = 0.0f;
+        if (NORM) {
+            // This workgroup writes h + delta (and later x) for its share of segments.
+            const bool mine = (unsigned)s % gridDim.x == blockIdx.x;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            a[j] = s < nseg ? reinterpret_cast<const float4 *>(x)[4 * s + j] : make_float4(0, 0, 0, 0);
-            sum += (a[j].x + a[j].y) + (a[j].z + a[j].w);
+            for (int j = 0; j < 4; ++j) {
+                float4 v = make_float4(0, 0, 0, 0);
+                if (s < nseg) {
+                    v = reinterpret_cast<const float4 *>(nm.h)[4 * s + j];
+                    if (nm.delta) {
+                        const float4 d = reinterpret_cast<const float4 *>(nm.delta)[4 * s + j];
+                        v.x += d.x; v.y += d.y; v.z += d.z; v.w += d.w;
+                    }
+                    if (nm.h_out && mine) reinterpret_cast<float4 *>(nm.h_out)[4 * s + j] = v;
+                    const float4 g = reinterpret_cast<const float4 *>(nm.w)[4 * s + j];
+                    ss += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+                    v = make_float4(g.x * v.x, g.y * v.y, g.z * v.z, g.w * v.w);
+                }
+                a[j] = v;
+                sum += (v.x + v.y) + (v.z + v.w);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = s < nseg ? reinterpret_cast<const float4 *>(x)[4 * s + j] : make_float4(0, 0, 0, 0);
+                sum += (a[j].x + a[j].y) + (a[j].z + a[j].w);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) sx[xslot<4>(s, j)] = a[j];
         seg_sum[s] = sum;
     }
+    if (MODE == kScaled) {
+        for (int j = threadIdx.x; j < nm.n; j += kGemvThreads) ss += nm.parts[j];
+    }
+    if (NORM || MODE == kScaled) {
+        ss = wave_sum(ss);
+        if (lane == 0) red[wave] = ss;
+    }
     __syncthreads();
+    float inv = 1.0f;
+    if (NORM || MODE == kScaled) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kGemvWaves; ++i) t += red[i];
+        inv = rsqrtf(t / (float)cols + nm.eps);
+    }
+    if (NORM) {
+        if (nm.x_out) {
+            for (int s = threadIdx.x; s < nseg; s += kGemvThreads) {
+                if ((unsigned)s % gridDim.x != blockIdx.x) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 a = sx[xslot<4>(s, j)];
+                    reinterpret_cast<float4 *>(nm.x_out)[4 * s + j] =
+                        make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+                }
+            }
+        }
+    }
 
     float acc[RW];
 #pragma unroll
@@ -128,10 +205,31 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
         load(i0 + 2 * U, wa, sa, ba);
         compute(i0 + U, wb, sb, bb);
     }
+    float sq = 0.0f;
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
-        const float v = wave_sum(acc[rr]);
-        if (lane == rr && r0 + rr < rows) y[r0 + rr] = apply_act(act, v);
+        const float v = apply_act(act, wave_sum(acc[rr]) * inv);
+        const int r = r0 + rr;
+        if (lane == rr && r < rows) y[r] = v;
+        if (MODE == kResid && r < nm.n) {
+            const float hp = nm.h[r] + v;
+            if (lane == rr) {
+                if (nm.h_out) nm.h_out[r] = hp;
+                if (nm.x_out) nm.x_out[r] = nm.w[r] * hp;
+            }
+            sq += hp * hp;
+        }
+    }
+    if (MODE == kResid) {
+        // The workgroup's 4 * RW rows (waves in order) make one part.
+        if (lane == 0) red[wave] = sq;
+        __syncthreads();
+        if (threadIdx.x == 0 && blockIdx.x * kGemvWaves * RW < nm.n) {
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kGemvWaves; ++i) t += red[i];
+            nm.parts[blockIdx.x] = t;
+        }
     }
 }
 
@@ -210,13 +308,46 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_f16_kernel(
 
 constexpr int kQ8Rw = 2, kQ8U = 2;
 constexpr int kF16Rw = 2, kF16U = 4;
-constexpr int kMaxLds = 160 * 1024;
 
 static int gemv_grid(int rows, int rw) { return ceil_div(rows, kGemvWaves * rw); }
 
 }  // namespace pg
 
 using namespace pg;
+
+// Dynamic LDS of the q8 kernel: staged x (16 bytes per float4, 4 per segment)
+// and one segment sum per segment, for ceil(cols / 1024) steps of 64 segments.
+static size_t gemv_q8_lds(int cols) {
+    const int steps = ceil_div(cols / 16, 64);
+    return (size_t)steps * 4 * 64 * sizeof(float4) + (size_t)steps * 64 * sizeof(float);
+}
+
+// Allow the largest dynamic LDS a kernel can ask for (cols = 32768); the
+// static reduction slots come on top, within the 160 KB of a compute unit.
+static int allow_lds(const void *kernel, size_t bytes) {
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess)
+        return PG_OK;
+    (void)hipGetLastError();  // do not leave the error for a later launch check to find
+    return PG_ELAUNCH;
+}
+
+template <int MODE>
+static int launch_mode(const int8_t *q, const float *scale, const float *bias, int rows, int cols,
+                       const float *x, float *y, int act, const Fuse &nm, pg_stream_t stream) {
+    static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q8_kernel<kQ8Rw, kQ8U, MODE>),
+                                    gemv_q8_lds(32768));
+    if (ok != PG_OK) return PG_ELAUNCH;
+    hipLaunchKernelGGL((gemv_q8_kernel<kQ8Rw, kQ8U, MODE>), dim3(gemv_grid(rows, kQ8Rw)), dim3(kGemvThreads),
+                       gemv_q8_lds(cols), as_stream(stream), q, scale, bias, rows, cols, x, y, act, nm);
+    return launch_status();
+}
+
+// [a, a + an) and [b, b + bn) bytes overlap.
+static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    if (!a || !b) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + bn && pb < pa + an;
+}
 
 extern "C" int gemv_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows,
                        int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream) {
@@ -225,18 +356,73 @@ extern "C" int gemv_q8(const int8_t *q, const float *scale, const float *bias, i
     if (!aligned16(q) || !aligned16(x) || !aligned16(y)) return PG_EINVAL;
     if (act != 0 && act != 1) return PG_EINVAL;
     if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
-    const int steps = ceil_div(cols / 16, 64);
-    const size_t lds = (size_t)steps * 4 * 64 * sizeof(float4) + (size_t)steps * 64 * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_q8_kernel<kQ8Rw, kQ8U>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        attr = true;
+    return launch_mode<kPlain>(q, scale, bias, rows, cols, x, y, act, Fuse{}, stream);
+}
+
+extern "C" int gemv_q8_addnorm(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                               int32_t cols, const float *h, const float *delta, const float *w,
+                               float eps, float *h_out, float *x_out, float *y, int32_t act,
+                               pg_stream_t stream) {
+    if (!q || !scale || !bias || !h || !w || !y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || !(eps >= 0.0f)) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(h) || !aligned16(w) || !aligned16(y)) return PG_EINVAL;
+    if ((delta && !aligned16(delta)) || (h_out && !aligned16(h_out)) || (x_out && !aligned16(x_out)))
+        return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
+    // Outputs are written while other workgroups still read h, delta and w.
+    const size_t vb = (size_t)cols * sizeof(float), yb = (size_t)rows * sizeof(float);
+    const void *ins[3] = {h, delta, w};
+    for (const void *in : ins) {
+        if (overlaps(h_out, vb, in, vb) || overlaps(x_out, vb, in, vb) || overlaps(y, yb, in, vb))
+            return PG_EINVAL;
     }
-    hipLaunchKernelGGL((gemv_q8_kernel<kQ8Rw, kQ8U>), dim3(gemv_grid(rows, kQ8Rw)),
-                       dim3(kGemvThreads), lds, as_stream(stream), q, scale, bias, rows, cols, x,
-                       y, act);
-    return launch_status();
+    if (overlaps(h_out, vb, x_out, vb) || overlaps(h_out, vb, y, yb) || overlaps(x_out, vb, y, yb))
+        return PG_EINVAL;
+    const Fuse nm{h, delta, w, eps, h_out, x_out, nullptr, 0};
+    return launch_mode<kAddNorm>(q, scale, bias, rows, cols, nullptr, y, act, nm, stream);
+}
+
+extern "C" int gemv_q8_residual(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                                int32_t cols, const float *x, float *y, int32_t act, const float *h,
+                                const float *w, int32_t hidden, float *h_out, float *xw, float *parts,
+                                pg_stream_t stream) {
+    if (!q || !scale || !bias || !x || !y || !h || !w || !xw || !parts) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || hidden <= 0 || hidden > rows) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(x) || !aligned16(y)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
+    // Row r's residual is read and written by one lane, so h_out may be h; nothing
+    // else may overlap (x is read by every workgroup while the others write).
+    const size_t hb = (size_t)hidden * sizeof(float), yb = (size_t)rows * sizeof(float);
+    const size_t pb = (size_t)ceil_div(hidden, kGemvWaves * kQ8Rw) * sizeof(float);
+    const size_t xb = (size_t)cols * sizeof(float);
+    struct Span { const void *p; size_t n; };
+    const Span sp[7] = {{x, xb}, {y, yb}, {h, hb}, {w, hb}, {h_out, hb}, {xw, hb}, {parts, pb}};
+    for (int i = 0; i < 7; ++i)
+        for (int j = i + 1; j < 7; ++j) {
+            if (i == 2 && j == 4 && h_out == h) continue;    // in place
+            if (i <= 3 && j <= 3 && i != 1 && j != 1) continue;  // inputs may share memory
+            if (overlaps(sp[i].p, sp[i].n, sp[j].p, sp[j].n)) return PG_EINVAL;
+        }
+    const Fuse nm{h, nullptr, w, 0.0f, h_out, xw, parts, hidden};
+    return launch_mode<kResid>(q, scale, bias, rows, cols, x, y, act, nm, stream);
+}
+
+extern "C" int gemv_q8_normed(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                              int32_t cols, const float *xw, const float *parts, float eps, float *y,
+                              int32_t act, pg_stream_t stream) {
+    if (!q || !scale || !bias || !xw || !parts || !y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || !(eps >= 0.0f)) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(xw) || !aligned16(y)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
+    const int nparts = ceil_div(cols, kGemvWaves * kQ8Rw);
+    const size_t yb = (size_t)rows * sizeof(float);
+    if (overlaps(y, yb, xw, (size_t)cols * sizeof(float)) || overlaps(y, yb, parts, (size_t)nparts * sizeof(float)))
+        return PG_EINVAL;
+    const Fuse nm{nullptr, nullptr, nullptr, eps, nullptr, nullptr, const_cast<float *>(parts), nparts};
+    return launch_mode<kScaled>(q, scale, bias, rows, cols, xw, y, act, nm, stream);
 }
 
 extern "C" int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const float *x, float *y,
@@ -246,14 +432,10 @@ extern "C" int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const flo
     if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return PG_EINVAL;
     if (act != 0 && act != 1) return PG_EINVAL;
     if (cols % 8 || cols > 32768) return PG_EUNSUPPORTED;
-    const int steps = ceil_div(cols / 8, 64);
-    const size_t lds = (size_t)steps * 2 * 64 * sizeof(float4);
-    static bool attr = false;
-    if (!attr) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(gemv_f16_kernel<kF16Rw, kF16U>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
-        attr = true;
-    }
+    const size_t lds = (size_t)ceil_div(cols / 8, 64) * 2 * 64 * sizeof(float4);
+    static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_f16_kernel<kF16Rw, kF16U>),
+                                    (size_t)ceil_div(32768 / 8, 64) * 2 * 64 * sizeof(float4));
+    if (ok != PG_OK) return PG_ELAUNCH;
     hipLaunchKernelGGL((gemv_f16_kernel<kF16Rw, kF16U>), dim3(gemv_grid(rows, kF16Rw)),
                        dim3(kGemvThreads), lds, as_stream(stream), w, rows, cols, x, y, act);
     return launch_status();

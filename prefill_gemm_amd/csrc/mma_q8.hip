@@ -70,33 +70,12 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const float *__restrict__ 
     }
 }
 
-// Fragment layout for the dense pass (see mma_q8.h): one thread per (row m,
-// 16-column half block) over mts * 32 rows (rows >= n are zero) and 16 * ng blocks.
-__global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
-                                                           int cols, int mts, u32x4 *__restrict__ xp,
-                                                           __bf16 *__restrict__ xs) {
-    const int nb = cols >> 5;
-    const int ng = (nb + 15) >> 4;
-    const int per_row = ng * 32;
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const int m = (int)(t / per_row);
-    const int hb = (int)(t % per_row);
-    const int blk = hb >> 1, h = hb & 1;
-    if (m >= mts * 32) return;
+// Fragment-layout record of one half block (16 columns, half h of block blk)
+// of A row m: the hi/lo bf16 pair of each value, and (h == 0 lane) the
+// block's sum.  Lanes 2i and 2i + 1 hold the two halves of one block.
+__device__ __forceinline__ void put_frag_half(const float v[16], int m, int blk, int h, int nb, int mts,
+                                              u32x4 *__restrict__ xp, __bf16 *__restrict__ xs) {
     const int mt = m >> 5, lane = (m & 31) + 32 * h;
-    const bool live = m < n && blk < nb;
-    float v[16];
-    if (live) {
-        const float4 *src = reinterpret_cast<const float4 *>(X + (long long)m * cols + 32 * blk + 16 * h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 a = src[j];
-            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-    }
     __bf16 hi[16], lo[16];
     float half_sum = 0.0f;
 #pragma unroll
@@ -122,6 +101,100 @@ __global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restri
         const int sl = (m & 31) + 32 * hh;
         xs[((((long long)g * mts + mt) * 2 + 0) * 64 + sl) * 8 + i] = s_hi;
         xs[((((long long)g * mts + mt) * 2 + 1) * 64 + sl) * 8 + i] = s_lo;
+    }
+}
+
+// Fragment layout for the dense pass (see mma_q8.h): one thread per (row m,
+// 16-column half block) over mts * 32 rows (rows >= n are zero) and 16 * ng blocks.
+__global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
+                                                           int cols, int mts, u32x4 *__restrict__ xp,
+                                                           __bf16 *__restrict__ xs) {
+    const int nb = cols >> 5;
+    const int ng = (nb + 15) >> 4;
+    const int per_row = ng * 32;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int m = (int)(t / per_row);
+    const int hb = (int)(t % per_row);
+    const int blk = hb >> 1, h = hb & 1;
+    if (m >= mts * 32) return;
+    const bool live = m < n && blk < nb;
+    float v[16];
+    if (live) {
+        const float4 *src = reinterpret_cast<const float4 *>(X + (long long)m * cols + 32 * blk + 16 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = src[j];
+            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    put_frag_half(v, m, blk, h, nb, mts, xp, xs);
+}
+
+// Residual add + RMSNorm fused into the fragment staging (nemotron_prefill.rs,
+// `pb_add_rms` with add = 1, ahead of the next product): workgroup m holds A
+// row m, kStageNormIter half blocks per thread in registers:
+//     h' = H[m] + delta[m];  X[m] = w * h' / sqrt(mean(h'^2) + eps)
+// H_out[m] = h' and X_out[m] = X[m] are written if given.  Rows m >= n stage zeros.
+constexpr int kStageNormIter = 4;  // cols <= 4 * 256 * 16 = 16384
+
+__global__ __launch_bounds__(256) void stage_norm_frag_kernel(
+    const float *__restrict__ H, const float *__restrict__ delta, int dstride, const float *__restrict__ w,
+    float eps, int n, int cols, int mts, float *__restrict__ H_out, float *__restrict__ X_out,
+    u32x4 *__restrict__ xp, __bf16 *__restrict__ xs) {
+    __shared__ float red[4];
+    const int nb = cols >> 5;
+    const int ng = (nb + 15) >> 4;
+    const int per_row = ng * 32;
+    const int m = blockIdx.x;
+    const bool row_live = m < n;
+    float v[kStageNormIter][16];
+    float ss = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kStageNormIter; ++it) {
+        const int hb = threadIdx.x + 256 * it;
+        const int c0 = 16 * hb;
+        const bool live = row_live && c0 < cols;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 a = make_float4(0, 0, 0, 0);
+            if (live) {
+                a = reinterpret_cast<const float4 *>(H + (long long)m * cols + c0)[j];
+                if (delta) {
+                    const float4 d = reinterpret_cast<const float4 *>(delta + (long long)m * dstride + c0)[j];
+                    a.x += d.x; a.y += d.y; a.z += d.z; a.w += d.w;
+                }
+                if (H_out) reinterpret_cast<float4 *>(H_out + (long long)m * cols + c0)[j] = a;
+                ss += (a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w);
+            }
+            v[it][4 * j] = a.x; v[it][4 * j + 1] = a.y; v[it][4 * j + 2] = a.z; v[it][4 * j + 3] = a.w;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float inv = rsqrtf((((red[0] + red[1]) + red[2]) + red[3]) / (float)cols + eps);
+#pragma unroll
+    for (int it = 0; it < kStageNormIter; ++it) {
+        const int hb = threadIdx.x + 256 * it;
+        if (hb >= per_row) break;  // uniform across each pair of lanes (per_row is even)
+        const int c0 = 16 * hb;
+        if (row_live && c0 < cols) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 g = reinterpret_cast<const float4 *>(w + c0)[j];
+                v[it][4 * j] = g.x * (v[it][4 * j] * inv);
+                v[it][4 * j + 1] = g.y * (v[it][4 * j + 1] * inv);
+                v[it][4 * j + 2] = g.z * (v[it][4 * j + 2] * inv);
+                v[it][4 * j + 3] = g.w * (v[it][4 * j + 3] * inv);
+                if (X_out)
+                    reinterpret_cast<float4 *>(X_out + (long long)m * cols + c0)[j] =
+                        make_float4(v[it][4 * j], v[it][4 * j + 1], v[it][4 * j + 2], v[it][4 * j + 3]);
+            }
+        }
+        put_frag_half(v[it], m, hb >> 1, hb & 1, nb, mts, xp, xs);
     }
 }
 
@@ -226,34 +299,46 @@ extern "C" size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, in
     return bytes;
 }
 
-extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias,
-                               int32_t rows, int32_t cols, const float *X, int32_t n, float *Y,
-                               int32_t act, void *workspace, size_t workspace_bytes,
-                               pg_stream_t stream) {
-    if (!q || !scale || !bias || !X || !Y) return PG_EINVAL;
-    if (rows <= 0 || cols <= 0 || n <= 0) return PG_EINVAL;
-    if (!aligned16(q) || !aligned16(X) || !aligned16(Y)) return PG_EINVAL;
-    if (act != 0 && act != 1) return PG_EINVAL;
-    if (cols % 32 || n > 64) return PG_EUNSUPPORTED;
-    const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
-    hipStream_t s = as_stream(stream);
+// Residual add + RMSNorm ahead of a prefill product (stage_norm_frag_kernel).
+struct StageNorm {
+    const float *H;
+    const float *delta;
+    int dstride;
+    const float *w;
+    float eps;
+    float *H_out;
+    float *X_out;
+};
 
+static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    if (!a || !b) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + bn && pb < pa + an;
+}
+
+// Staging (plain or normed) into the workspace, then the dense matrix-core pass
+// [+ the ordered split-K reduction].  Arguments are checked by the callers.
+static int prefill_run(const int8_t *q, const float *scale, const float *bias, int rows, int cols,
+                       const float *X, const StageNorm *nm, int n, float *Y, int act, void *workspace,
+                       hipStream_t s) {
     char *ws = static_cast<char *>(workspace);
     void *xp = ws;
     void *xs = ws + round_up(frag_x_bytes(n, cols), 256);
     float *parts = reinterpret_cast<float *>(ws + round_up(frag_x_bytes(n, cols), 256) +
                                              round_up(frag_s_bytes(n, cols), 256));
     const int mts = ceil_div(n, 32);
-    {
+    if (nm) {
+        hipLaunchKernelGGL(stage_norm_frag_kernel, dim3(mts * 32), dim3(256), 0, s, nm->H, nm->delta,
+                           nm->dstride, nm->w, nm->eps, n, cols, mts, nm->H_out, nm->X_out,
+                           reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs));
+    } else {
         const int nb = cols / 32, ng = (nb + 15) / 16;
         const long long threads = (long long)mts * 32 * ng * 32;
         hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                            X, n, cols, mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs));
-        int rc = launch_status();
-        if (rc) return rc;
     }
-    int rc = PG_OK;
+    int rc = launch_status();
+    if (rc) return rc;
 
     MmaPanel P{};
     P.q = q;
@@ -288,4 +373,53 @@ extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float 
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256), 0, s,
                        parts, used, plane, Y, act);
     return launch_status();
+}
+
+extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias,
+                               int32_t rows, int32_t cols, const float *X, int32_t n, float *Y,
+                               int32_t act, void *workspace, size_t workspace_bytes,
+                               pg_stream_t stream) {
+    if (!q || !scale || !bias || !X || !Y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || n <= 0) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(X) || !aligned16(Y)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || n > 64) return PG_EUNSUPPORTED;
+    const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
+    return prefill_run(q, scale, bias, rows, cols, X, nullptr, n, Y, act, workspace, as_stream(stream));
+}
+
+extern "C" int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bias,
+                                       int32_t rows, int32_t cols, const float *H, const float *delta,
+                                       int32_t delta_stride, const float *w, float eps, int32_t n,
+                                       float *H_out, float *X_out, float *Y, int32_t act,
+                                       void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+    if (!q || !scale || !bias || !H || !w || !Y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || n <= 0 || !(eps >= 0.0f)) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(H) || !aligned16(w) || !aligned16(Y)) return PG_EINVAL;
+    if ((delta && !aligned16(delta)) || (H_out && !aligned16(H_out)) || (X_out && !aligned16(X_out)))
+        return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (delta && (delta_stride < cols || delta_stride % 4)) return PG_EINVAL;
+    if (cols % 32 || cols > 16384 || n > 64) return PG_EUNSUPPORTED;
+    const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
+    // H_out and X_out are written while other rows of H and delta are still read
+    // (H_out == H is allowed: each element is read and then written by one thread);
+    // Y is written after the staging has finished.
+    const size_t mb = (size_t)n * cols * sizeof(float);
+    const size_t db = delta ? ((size_t)(n - 1) * delta_stride + cols) * sizeof(float) : 0;
+    const void *outs[2] = {H_out, X_out};
+    for (const void *o : outs)
+        if ((o != H && overlaps(o, mb, H, mb)) || overlaps(o, mb, delta, db) ||
+            overlaps(o, mb, w, cols * sizeof(float)))
+            return PG_EINVAL;
+    if (X_out && X_out == H) return PG_EINVAL;
+    if (overlaps(H_out, mb, X_out, mb)) return PG_EINVAL;
+    const size_t yb = (size_t)n * rows * sizeof(float);
+    if (overlaps(Y, yb, workspace, need) || overlaps(H_out, mb, workspace, need) ||
+        overlaps(X_out, mb, workspace, need))
+        return PG_EINVAL;
+    const StageNorm nm{H, delta, delta_stride, w, eps, H_out, X_out};
+    return prefill_run(q, scale, bias, rows, cols, nullptr, &nm, n, Y, act, workspace, as_stream(stream));
 }

@@ -10,16 +10,22 @@ product stand in for the mixer output added into the residual.
     u   = relu^2(W_up x1)     d  = W_down u
     h2  = h1 + d;  x2 = rmsnorm(h2) w2                     logits = W_head x2
 
-Every stage is one libpg call on the current stream; ``capture()`` records the
-whole frame once into a HIP graph (through torch.cuda.CUDAGraph) so replays
-pay one launch for the frame (nemotron_prefill.rs builds its bind groups once
-and keeps the pass size in a device buffer for the same reason).
+The two residual + norm sites run inside the products around them, so a
+frame is four product calls.  Decode: the QKV and down GEMVs add their output
+into the residual and leave w * h and partial sums of squares
+(gemv_q8_residual); the up and head GEMVs apply 1/rms to their dot products
+(gemv_q8_normed) -- four GEMV launches back to back.  Prefill: the up and head
+products stage rmsnorm(h + delta) * w themselves (prefill_gemm_q8_addnorm).  ``capture()`` records
+the whole frame once into a HIP graph (through torch.cuda.CUDAGraph) so
+replays pay one launch for the frame (nemotron_prefill.rs builds its bind
+groups once and keeps the pass size in a device buffer for the same reason).
 """
 from __future__ import annotations
 
 import torch
 
-from ._lib import Q8Weight, add_rmsnorm, gemv_q8, prefill_gemm_q8, prefill_gemm_q8_workspace_bytes
+from ._lib import (Q8Weight, gemv_q8, gemv_q8_normed, gemv_q8_residual, norm_parts, prefill_gemm_q8,
+                   prefill_gemm_q8_addnorm, prefill_gemm_q8_workspace_bytes)
 
 PB_MAX = 64
 
@@ -36,9 +42,13 @@ class Frame:
         self.hidden = qkv.cols
         dev = qkv.q.device
         f32 = dict(dtype=torch.float32, device=dev)
-        self.buf = {"qkv": torch.empty(n, qkv.rows, **f32), "x1": torch.empty(n, self.hidden, **f32),
-                    "u": torch.empty(n, up.rows, **f32), "d": torch.empty(n, self.hidden, **f32),
-                    "x2": torch.empty(n, self.hidden, **f32), "logits": torch.empty(n, head.rows, **f32)}
+        self.buf = {"qkv": torch.empty(n, qkv.rows, **f32), "u": torch.empty(n, up.rows, **f32),
+                    "d": torch.empty(n, self.hidden, **f32), "logits": torch.empty(n, head.rows, **f32)}
+        if n == 1:   # decode: w * h and the sum-of-squares parts handed between GEMVs
+            for k in ("xw1", "xw2"):
+                self.buf[k] = torch.empty(self.hidden, **f32)
+            for k in ("p1", "p2"):
+                self.buf[k] = torch.empty(norm_parts(self.hidden), **f32)
         if n > 1:
             need = max(prefill_gemm_q8_workspace_bytes(w.rows, w.cols, n) for w in self.W.values())
             self.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -53,17 +63,33 @@ class Frame:
         else:
             prefill_gemm_q8(self.W[name], x, y, act, workspace=self.workspace)
 
-    def run(self, x0: torch.Tensor, h: torch.Tensor) -> torch.Tensor:
-        """Run the frame on x0 [n][hidden]; h [n][hidden] is the residual, updated in place."""
+    def stages(self, x0: torch.Tensor, h: torch.Tensor):
+        """The frame as its four product calls (zero-argument callables, in order)."""
         b = self.buf
         H = self.hidden
-        self._mm("qkv", x0, b["qkv"])
-        add_rmsnorm(h, b["qkv"][:, :H], self.w1, self.eps, out=b["x1"], delta_stride=b["qkv"].shape[1])
-        self._mm("up", b["x1"], b["u"], act=1)
-        self._mm("down", b["u"], b["d"])
-        add_rmsnorm(h, b["d"], self.w2, self.eps, out=b["x2"])
-        self._mm("head", b["x2"], b["logits"])
-        return b["logits"]
+        W = self.W
+        if self.n == 1:
+            hv = h.view(-1)
+            return [lambda: gemv_q8_residual(W["qkv"], x0.view(-1), hv, self.w1, b["xw1"], b["p1"],
+                                             y=b["qkv"].view(-1), h_out=hv),
+                    lambda: gemv_q8_normed(W["up"], b["xw1"], b["p1"], self.eps, y=b["u"].view(-1), act=1),
+                    lambda: gemv_q8_residual(W["down"], b["u"].view(-1), hv, self.w2, b["xw2"], b["p2"],
+                                             y=b["d"].view(-1), h_out=hv),
+                    lambda: gemv_q8_normed(W["head"], b["xw2"], b["p2"], self.eps, y=b["logits"].view(-1))]
+        ws = self.workspace
+        return [lambda: prefill_gemm_q8(W["qkv"], x0, b["qkv"], workspace=ws),
+                lambda: prefill_gemm_q8_addnorm(W["up"], h, b["qkv"][:, :H], self.w1, self.eps, Y=b["u"], act=1,
+                                                H_out=h, workspace=ws),
+                lambda: prefill_gemm_q8(W["down"], b["u"], b["d"], workspace=ws),
+                lambda: prefill_gemm_q8_addnorm(W["head"], h, b["d"], self.w2, self.eps, Y=b["logits"], H_out=h,
+                                                workspace=ws)]
+
+    def run(self, x0: torch.Tensor, h: torch.Tensor) -> torch.Tensor:
+        """Run the frame on x0 [n][hidden]; h [n][hidden] is the residual, updated in place
+        (h ends as h + qkv[:, :hidden] + d)."""
+        for st in self.stages(x0, h):
+            st()
+        return self.buf["logits"]
 
     def capture(self, x0: torch.Tensor, h: torch.Tensor):
         """Record run(x0, h) into a graph; replay() then reruns it on the same buffers."""

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(pg):
     names = declared_functions()
     assert {"gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
             "pg_strerror", "pg_version", "prefill_gemm_q8_workspace_bytes",
-            "moe_grouped_workspace_bytes"} <= set(names)
+            "moe_grouped_workspace_bytes", "gemv_q8_addnorm", "prefill_gemm_q8_addnorm"} <= set(names)
     L = pg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -83,3 +83,59 @@ def test_argument_checks_return_before_launch(pg):
     assert L.moe_grouped(*args(4, 64, 2000, 2, 64)) == pg.PG_EUNSUPPORTED
     assert L.moe_grouped(*args(4, 64, 8, 17, 64)) == pg.PG_EUNSUPPORTED
     assert L.moe_grouped(*args(4, 64, 8, 0, 64)) == pg.PG_EINVAL
+
+
+def test_fused_norm_argument_checks(pg):
+    L = pg.lib()
+    f = ctypes.c_float
+    A, B, C, D, E = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000))
+    # gemv_q8_addnorm(q, scale, bias, rows, cols, h, delta, w, eps, h_out, x_out, y, act, stream)
+    g = lambda h, d, w, eps, ho, xo, y, rows=8, cols=64, act=0: L.gemv_q8_addnorm(
+        FAKE, FAKE, FAKE, rows, cols, h, d, w, f(eps), ho, xo, y, act, None)
+    assert g(None, None, B, 1e-6, None, None, C) == pg.PG_EINVAL
+    assert g(A, None, B, -1.0, None, None, C) == pg.PG_EINVAL
+    assert g(A, None, B, float("nan"), None, None, C) == pg.PG_EINVAL
+    assert g(A, ODD, B, 1e-6, None, None, C) == pg.PG_EINVAL
+    assert g(A, None, B, 1e-6, None, None, C, cols=48) == pg.PG_EUNSUPPORTED
+    assert g(A, None, B, 1e-6, A, None, C) == pg.PG_EINVAL          # h_out aliases h
+    assert g(A, D, B, 1e-6, ctypes.c_void_p(0x400010), None, C) == pg.PG_EINVAL   # h_out overlaps delta
+    assert g(A, None, B, 1e-6, None, B, C) == pg.PG_EINVAL          # x_out aliases w
+    assert g(A, None, B, 1e-6, D, D, C) == pg.PG_EINVAL             # h_out aliases x_out
+    assert g(A, None, B, 1e-6, None, None, A) == pg.PG_EINVAL       # y aliases h
+    assert g(A, None, B, 1e-6, None, None, C, act=3) == pg.PG_EINVAL
+    # prefill_gemm_q8_addnorm(q, scale, bias, rows, cols, H, delta, stride, w, eps, n, H_out, X_out, Y, act, ws, wsb, s)
+    big = ctypes.c_size_t(1 << 30)
+    WS = ctypes.c_void_p(0x10000000)
+    p = lambda H, d, st, w, n, Ho, Xo, Y, cols=64, wsb=big, ws=WS: L.prefill_gemm_q8_addnorm(
+        FAKE, FAKE, FAKE, 8, cols, H, d, st, w, f(1e-6), n, Ho, Xo, Y, 0, ws, wsb, None)
+    assert p(A, None, 0, B, 65, None, None, C) == pg.PG_EUNSUPPORTED
+    assert p(A, None, 0, B, 4, None, None, C, cols=32768) == pg.PG_EUNSUPPORTED
+    assert p(A, D, 32, B, 4, None, None, C) == pg.PG_EINVAL          # stride < cols
+    assert p(A, D, 66, B, 4, None, None, C) == pg.PG_EINVAL          # stride % 4
+    assert p(A, None, 0, B, 4, None, None, C, wsb=ctypes.c_size_t(16)) == pg.PG_EWORKSPACE
+    assert p(A, None, 0, B, 4, ctypes.c_void_p(0x100100), None, C) == pg.PG_EINVAL   # H_out overlaps H, not equal
+    assert p(A, None, 0, B, 4, None, A, C) == pg.PG_EINVAL           # X_out aliases H
+    assert p(A, None, 0, B, 4, D, D, C) == pg.PG_EINVAL              # H_out aliases X_out
+    assert p(A, None, 0, B, 4, None, None, WS) == pg.PG_EINVAL       # Y inside the workspace
+
+
+def test_residual_pair_argument_checks(pg):
+    L = pg.lib()
+    f = ctypes.c_float
+    X, Y, H, Wn, HO, XW, PT = (ctypes.c_void_p(a) for a in
+                               (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000))
+    r = lambda rows=16, cols=64, hidden=8, x=X, y=Y, h=H, ho=HO, xw=XW, pt=PT, act=0: L.gemv_q8_residual(
+        FAKE, FAKE, FAKE, rows, cols, x, y, act, h, Wn, hidden, ho, xw, pt, None)
+    assert r(hidden=17) == pg.PG_EINVAL                 # hidden > rows
+    assert r(xw=None) == pg.PG_EINVAL
+    assert r(cols=48) == pg.PG_EUNSUPPORTED
+    assert r(y=X) == pg.PG_EINVAL                       # y aliases x
+    assert r(ho=ctypes.c_void_p(0x300010)) == pg.PG_EINVAL   # h_out overlaps h without being h
+    assert r(xw=PT) == pg.PG_EINVAL                     # xw aliases parts
+    assert r(pt=ctypes.c_void_p(0x200004)) == pg.PG_EINVAL   # parts overlaps y
+    n = lambda cols=64, xw=XW, pt=PT, y=Y, eps=1e-6: L.gemv_q8_normed(FAKE, FAKE, FAKE, 16, cols, xw, pt, f(eps), y, 0,
+                                                                      None)
+    assert n(eps=-1.0) == pg.PG_EINVAL
+    assert n(y=XW) == pg.PG_EINVAL
+    assert n(y=PT) == pg.PG_EINVAL
+    assert n(cols=40) == pg.PG_EUNSUPPORTED

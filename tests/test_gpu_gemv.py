@@ -128,3 +128,139 @@ def test_gemv_errors_on_device(pg):
     with pytest.raises(pg.PGError) as e:
         pg.gemv_q8(W, torch.zeros(48, device="cuda"))
     assert e.value.code == pg.PG_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ add + RMSNorm fused into the GEMV
+
+@pytest.mark.parametrize("rows,cols,delta,outs", [(1024, 1024, True, True), (37, 96, False, True),
+                                                  (133, 2688, True, False), (6, 32768, True, True),
+                                                  (14336, 4096, True, True), (1, 32, True, True)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_gemv_q8_addnorm(pg, oracle, rows, cols, delta, outs, act):
+    """y = act(W (rmsnorm(h + delta) w)) in one launch, against the oracle's norm then product."""
+    _case(f"gemv_q8_addnorm {rows}x{cols} delta={delta} outs={outs} act={act}")
+    rng = np.random.default_rng(rows * 13 + cols + act)
+    m = synth.q8(rng, rows, cols)
+    h = synth.normal(rng, cols)
+    d = synth.normal(rng, cols) if delta else None
+    w = synth.norm_weight(rng, cols)
+    h_ref, x_ref = oracle.add_rmsnorm(h, d, w, 1e-6)
+    y_ref = oracle.gemm_q8(m.q, m.scale, m.bias, x_ref, act=act)
+    hd = to_dev(h, torch)
+    ho = torch.full((cols,), float("nan"), device="cuda") if outs else None
+    xo = torch.full((cols,), float("nan"), device="cuda") if outs else None
+    y = pg.gemv_q8_addnorm(q8_dev(m, torch), hd, None if d is None else to_dev(d, torch), to_dev(w, torch),
+                           1e-6, act=act, h_out=ho, x_out=xo)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y.cpu().numpy(), y_ref) <= TOL_Q8
+    assert np.array_equal(hd.cpu().numpy(), h)            # the input residual is left alone
+    if outs:
+        assert oracle.rel_err(ho.cpu().numpy(), h_ref) <= TOL_F32
+        assert oracle.rel_err(xo.cpu().numpy(), x_ref) <= TOL_F32
+
+
+def test_gemv_q8_addnorm_matches_two_calls(pg):
+    """The fused call and add_rmsnorm followed by gemv_q8 agree (same inputs, f32 both ways)."""
+    _case("gemv_q8_addnorm vs add_rmsnorm + gemv_q8")
+    rng = np.random.default_rng(5)
+    m = synth.q8(rng, 6144, 4096)
+    W = q8_dev(m, torch)
+    h = to_dev(synth.normal(rng, 4096), torch)
+    d = to_dev(synth.normal(rng, 4096), torch)
+    w = to_dev(synth.norm_weight(rng, 4096), torch)
+    y = pg.gemv_q8_addnorm(W, h, d, w, 1e-6, act=1)
+    h2 = h.clone().view(1, -1)
+    x = pg.add_rmsnorm(h2, d.view(1, -1), w, 1e-6)
+    y2 = pg.gemv_q8(W, x.view(-1), act=1)
+    assert float((y - y2).abs().max() / y2.pow(2).mean().sqrt()) <= 1e-5
+
+
+def test_gemv_q8_addnorm_exact(pg, oracle):
+    """Exact case: integer residual with sum of squares = cols (rms 1), unit weights,
+    eps 0, scale 2^-3, bias 0, so every step is exact and the result is bit for bit."""
+    _case("gemv_q8_addnorm exact")
+    rng = np.random.default_rng(21)
+    rows, cols = 300, 2048
+    m = exact_q8(rng, rows, cols)
+    h = rng.choice(np.array([-1.0, 1.0], np.float32), size=cols)
+    y = pg.gemv_q8_addnorm(q8_dev(m, torch), to_dev(h, torch), None, torch.ones(cols, device="cuda"), 0.0)
+    ref = oracle.gemm_q8(m.q, m.scale, m.bias, h)
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+# ------------------------------------------------------------------ add + RMSNorm split across two GEMVs
+
+def _parts(hp):
+    """Sums of squares over groups of 8 (the contract of gemv_q8_residual), in f64."""
+    hp = np.asarray(hp, np.float64)
+    pad = np.zeros(-(-hp.size // 8) * 8)
+    pad[:hp.size] = hp
+    return (pad.reshape(-1, 8) ** 2).sum(1)
+
+
+@pytest.mark.parametrize("rows,cols,hidden,inplace", [(6144, 4096, 4096, True), (4096, 14336, 4096, False),
+                                                      (100, 96, 37, True), (1024, 1024, 1024, False),
+                                                      (8, 32768, 3, True)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_gemv_q8_residual(pg, oracle, rows, cols, hidden, inplace, act):
+    _case(f"gemv_q8_residual {rows}x{cols} hidden={hidden} inplace={inplace} act={act}")
+    rng = np.random.default_rng(rows + cols + hidden + act)
+    m = synth.q8(rng, rows, cols)
+    x = synth.normal(rng, cols)
+    h = synth.normal(rng, hidden)
+    w = synth.norm_weight(rng, hidden)
+    y_ref = oracle.gemm_q8(m.q, m.scale, m.bias, x, act=act)
+    h_ref, _ = oracle.add_rmsnorm(h, y_ref[:hidden].astype(np.float32), w, 1e-6)
+    hd = to_dev(h, torch)
+    ho = hd if inplace else torch.full((hidden,), float("nan"), device="cuda")
+    xw = torch.full((hidden,), float("nan"), device="cuda")
+    parts = torch.full((pg.norm_parts(hidden),), float("nan"), device="cuda")
+    y = pg.gemv_q8_residual(q8_dev(m, torch), to_dev(x, torch), hd, to_dev(w, torch), xw, parts, act=act,
+                            h_out=ho)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y.cpu().numpy(), y_ref) <= TOL_Q8
+    assert oracle.rel_err(ho.cpu().numpy(), h_ref) <= TOL_Q8
+    assert oracle.rel_err(xw.cpu().numpy(), w.astype(np.float64) * h_ref) <= TOL_Q8
+    assert oracle.rel_err(parts.cpu().numpy(), _parts(h_ref)) <= TOL_Q8
+    if not inplace:
+        assert np.array_equal(hd.cpu().numpy(), h)
+
+
+@pytest.mark.parametrize("rows,cols", [(14336, 4096), (32000, 4096), (77, 1056)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_gemv_q8_normed(pg, oracle, rows, cols, act):
+    """Stage-isolated: fed w * h' and the parts of the oracle's h', the product equals the
+    oracle's product on rmsnorm(h') * w."""
+    _case(f"gemv_q8_normed {rows}x{cols} act={act}")
+    rng = np.random.default_rng(rows * 3 + cols + act)
+    m = synth.q8(rng, rows, cols)
+    h = synth.normal(rng, cols)
+    d = synth.normal(rng, cols)
+    w = synth.norm_weight(rng, cols)
+    h_ref, x_ref = oracle.add_rmsnorm(h, d, w, 1e-6)
+    xw = (w.astype(np.float64) * h_ref).astype(np.float32)
+    parts = _parts(h_ref).astype(np.float32)
+    y = pg.gemv_q8_normed(q8_dev(m, torch), to_dev(xw, torch), to_dev(parts, torch), 1e-6, act=act)
+    torch.cuda.synchronize()
+    idx = np.unique(rng.choice(rows, min(rows, 500), replace=False))
+    ref = oracle.gemm_q8_rows(m.q, m.scale, m.bias, idx, x_ref, act=act)[0]
+    assert oracle.rel_err(y.cpu().numpy()[idx], ref) <= TOL_Q8
+
+
+def test_gemv_q8_residual_then_normed(pg, oracle):
+    """The pair end to end: W2 . (rmsnorm(h + W1 x) w) against the oracle chain."""
+    _case("gemv_q8_residual -> gemv_q8_normed")
+    rng = np.random.default_rng(44)
+    m1, m2 = synth.q8(rng, 1536, 1024), synth.q8(rng, 2000, 1024)
+    x, h, w = synth.normal(rng, 1024), synth.normal(rng, 1024), synth.norm_weight(rng, 1024)
+    y1 = oracle.gemm_q8(m1.q, m1.scale, m1.bias, x).astype(np.float32)
+    h_ref, x_ref = oracle.add_rmsnorm(h, y1[:1024], w, 1e-6)
+    y2_ref = oracle.gemm_q8(m2.q, m2.scale, m2.bias, x_ref, act=1)
+    hd = to_dev(h, torch)
+    xw = torch.empty(1024, device="cuda")
+    parts = torch.empty(pg.norm_parts(1024), device="cuda")
+    pg.gemv_q8_residual(q8_dev(m1, torch), to_dev(x, torch), hd, to_dev(w, torch), xw, parts, h_out=hd)
+    y2 = pg.gemv_q8_normed(q8_dev(m2, torch), xw, parts, 1e-6, act=1)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(hd.cpu().numpy(), h_ref) <= TOL_Q8
+    assert oracle.rel_err(y2.cpu().numpy(), y2_ref) <= 2 * TOL_Q8

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_Q8, exact_q8, int_acts, q8_dev, to_dev
+from helpers import TOL_F32, TOL_Q8, exact_q8, int_acts, q8_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +123,49 @@ def test_prefill_heavy_tailed_input(pg, oracle):
     X = (np.maximum(synth.normal(rng, (64, 14336)) * 25, 0) ** 2).astype(np.float32)
     Y = pg.prefill_gemm_q8(q8_dev(m, torch), to_dev(X, torch)).cpu().numpy()
     assert oracle.rel_err(Y, oracle.gemm_q8(m.q, m.scale, m.bias, X)) <= TOL_Q8
+
+
+# ------------------------------------------------------------------ add + RMSNorm fused into the staging
+
+@pytest.mark.parametrize("n,rows,cols,stride", [(1, 300, 544, None), (5, 45, 4096, 6144), (33, 257, 1856, 0),
+                                                (64, 640, 2688, None), (36, 128, 16384, None),
+                                                (64, 14336, 4096, 6144)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_prefill_addnorm(pg, oracle, n, rows, cols, stride, act):
+    """Y = act((rmsnorm(H + delta) w) W^T), the norm done while staging, against the oracle."""
+    _case(f"prefill_addnorm {rows}x{cols} n={n} stride={stride} act={act}")
+    rng = np.random.default_rng(n * 31 + rows + cols + act)
+    m = synth.q8(rng, rows, cols)
+    H = synth.normal(rng, (n, cols))
+    w = synth.norm_weight(rng, cols)
+    if stride == 0:
+        d = dd = None
+    else:
+        wide = synth.normal(rng, (n, stride or cols))
+        d, dd = wide, to_dev(wide, torch)[:, :cols]
+    h_ref, x_ref = oracle.add_rmsnorm(H, d, w, 1e-6, delta_stride=stride or None)
+    idx = np.unique(rng.choice(rows, min(rows, 300), replace=False))
+    y_ref = oracle.gemm_q8_rows(m.q, m.scale, m.bias, idx, x_ref, act=act)
+    Hd = to_dev(H, torch)
+    Xo = torch.full((n, cols), float("nan"), device="cuda")
+    Y = pg.prefill_gemm_q8_addnorm(q8_dev(m, torch), Hd, dd, to_dev(w, torch), 1e-6, act=act, H_out=Hd,
+                                   X_out=Xo)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(Y.cpu().numpy()[:, idx], y_ref) <= TOL_Q8
+    assert oracle.rel_err(Hd.cpu().numpy(), h_ref) <= TOL_F32     # residual updated in place
+    assert oracle.rel_err(Xo.cpu().numpy(), x_ref) <= TOL_F32
+
+
+def test_prefill_addnorm_matches_gemv_addnorm(pg):
+    """Each position of a fused prefill pass equals the fused decode call on that position."""
+    _case("prefill_addnorm vs gemv_q8_addnorm")
+    rng = np.random.default_rng(8)
+    m = synth.q8(rng, 500, 1024)
+    W = q8_dev(m, torch)
+    H = to_dev(synth.normal(rng, (9, 1024)), torch)
+    D = to_dev(synth.normal(rng, (9, 1024)), torch)
+    w = to_dev(synth.norm_weight(rng, 1024), torch)
+    Y = pg.prefill_gemm_q8_addnorm(W, H, D, w, 1e-6)
+    for b in range(9):
+        g = pg.gemv_q8_addnorm(W, H[b].contiguous(), D[b].contiguous(), w, 1e-6)
+        assert float((Y[b] - g).abs().max() / g.pow(2).mean().sqrt()) <= 2 * TOL_Q8
