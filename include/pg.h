@@ -102,18 +102,19 @@ int gemv_q8_addnorm(const int8_t *q, const float *scale, const float *bias, int3
  * boundaries):
  *   gemv_q8_residual: y[r] = act( sum_c wq[r][c] * x[c] ), r < rows, and for
  *     r < hidden:  h_out[r] = h[r] + y[r],   xw[r] = w[r] * h_out[r],
- *     and parts[j] = sum of h_out[r]^2 over r in [8j, 8j + 8) ∩ [0, hidden),
- *     j < ceil(hidden / 8) (f32).
+ *     and parts[0 .. gemv_q8_norm_parts(hidden)) = sums of h_out[r]^2 over a
+ *     fixed partition of [0, hidden) into consecutive row ranges (f32).
  *   gemv_q8_normed: y[r] = act( (sum_c wq[r][c] * xw[c]) / sqrt( sum_j parts[j] / cols + eps ) ),
- *     j < ceil(cols / 8), the parts summed in the same fixed order by every
- *     workgroup.  With xw and parts from gemv_q8_residual (cols = hidden) this
- *     is the product of W with rmsnorm(h + y[:hidden]) * w.
+ *     j < gemv_q8_norm_parts(cols), the parts summed in the same fixed order
+ *     by every workgroup.  With xw and parts from gemv_q8_residual (cols =
+ *     hidden) this is the product of W with rmsnorm(h + y[:hidden]) * w.
  *   x [cols] f32; y [rows] f32; h, w [hidden] f32 (hidden <= rows); h_out
  *   [hidden] f32 (NULL: not written; h_out == h updates the residual in
- *   place); xw [hidden] f32; parts [ceil(hidden / 8)] f32.  Outputs may not
- *   overlap each other or the inputs (other than h_out == h): PG_EINVAL.
+ *   place); xw [hidden] f32; parts [gemv_q8_norm_parts(hidden)] f32.  Outputs
+ *   may not overlap each other or the inputs (other than h_out == h): PG_EINVAL.
  * PG_EINVAL also for eps < 0 or NaN.  PG_EUNSUPPORTED: cols % 32 != 0, cols > 32768.
  */
+int32_t gemv_q8_norm_parts(int32_t hidden);
 int gemv_q8_residual(const int8_t *q, const float *scale, const float *bias, int32_t rows,
                      int32_t cols, const float *x, float *y, int32_t act, const float *h,
                      const float *w, int32_t hidden, float *h_out, float *xw, float *parts,

@@ -64,6 +64,8 @@ def _declare(L):
                                           _i32, _P, _sz, _P]
     L.gemv_q8_residual.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P, _P, _i32, _P, _P, _P, _P]
     L.gemv_q8_normed.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _f, _P, _i32, _P]
+    L.gemv_q8_norm_parts.argtypes = [_i32]
+    L.gemv_q8_norm_parts.restype = _i32
     for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed"):
         getattr(L, name).restype = ctypes.c_int
@@ -189,7 +191,7 @@ def gemv_q8_addnorm(W: Q8Weight, h: torch.Tensor, delta: torch.Tensor | None, w:
 
 def norm_parts(hidden: int) -> int:
     """Length of the sum-of-squares parts gemv_q8_residual writes for ``hidden`` rows."""
-    return -(-hidden // 8)
+    return lib().gemv_q8_norm_parts(hidden)
 
 
 def gemv_q8_residual(W: Q8Weight, x: torch.Tensor, h: torch.Tensor, w: torch.Tensor, xw: torch.Tensor,

@@ -28,7 +28,8 @@ constexpr int kGemvWaves = kGemvThreads / kWave;
 //            and multiplies its finished dot products by the scalar 1/rms
 //  kResid    y = act(W x); then for rows r < n: h_out[r] = h[r] + y[r],
 //            x_out[r] = w[r] * h_out[r], and parts[j] = the sum of h_out^2
-//            over the rows 8j .. 8j + 7 (the rows of workgroup j)
+//            over the rows 8j .. 8j + 7 (the rows of workgroup j; one
+//            part per workgroup keeps what every consumer workgroup reads small)
 //  kScaled   y = act((W x) / sqrt(sum_j parts[j] / cols + eps)), j < n: the
 //            consumer of a kResid product (x = its x_out), which completes
 //            the RMSNorm without another pass over the activations
@@ -58,7 +59,8 @@ __device__ __forceinline__ int xslot(int s, int j) {
 // batches of U steps, one batch ahead of the arithmetic (the first batch
 // before the activation is staged), from clamped in-bounds addresses; a
 // segment past the end of the row meets zeros in the staged activation, so
-// it adds nothing.
+// it adds nothing.  Weights are read with non-temporal loads: each byte is
+// used once, and the staged activation and small vectors keep the caches.
 // What happens around the product is MODE (GemvMode above).
 template <int RW, int U, int MODE>
 __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
                 const int s = min(lane + 64 * (i0 + u), nseg - 1);
 #pragma unroll
                 for (int rr = 0; rr < RW; ++rr) {
-                    w[u][rr] = *reinterpret_cast<const u32x4 *>(qr[rr] + 16 * s);
+                    w[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qr[rr] + 16 * s));
                     sc[u][rr] = sr[rr][s >> 1];
                     bi[u][rr] = br[rr][s >> 1];
                 }
@@ -381,6 +383,10 @@ extern "C" int gemv_q8_addnorm(const int8_t *q, const float *scale, const float 
         return PG_EINVAL;
     const Fuse nm{h, delta, w, eps, h_out, x_out, nullptr, 0};
     return launch_mode<kAddNorm>(q, scale, bias, rows, cols, nullptr, y, act, nm, stream);
+}
+
+extern "C" int32_t gemv_q8_norm_parts(int32_t hidden) {
+    return hidden > 0 ? ceil_div(hidden, kGemvWaves * kQ8Rw) : 0;
 }
 
 extern "C" int gemv_q8_residual(const int8_t *q, const float *scale, const float *bias, int32_t rows,

@@ -190,12 +190,13 @@ def test_gemv_q8_addnorm_exact(pg, oracle):
 
 # ------------------------------------------------------------------ add + RMSNorm split across two GEMVs
 
-def _parts(hp):
-    """Sums of squares over groups of 8 (the contract of gemv_q8_residual), in f64."""
+def _parts(hp, nparts):
+    """Sums of squares over the consecutive, equal row ranges of gemv_q8_residual's partition, in f64."""
     hp = np.asarray(hp, np.float64)
-    pad = np.zeros(-(-hp.size // 8) * 8)
+    g = -(-hp.size // nparts)
+    pad = np.zeros(nparts * g)
     pad[:hp.size] = hp
-    return (pad.reshape(-1, 8) ** 2).sum(1)
+    return (pad.reshape(nparts, g) ** 2).sum(1)
 
 
 @pytest.mark.parametrize("rows,cols,hidden,inplace", [(6144, 4096, 4096, True), (4096, 14336, 4096, False),
@@ -221,7 +222,8 @@ def test_gemv_q8_residual(pg, oracle, rows, cols, hidden, inplace, act):
     assert oracle.rel_err(y.cpu().numpy(), y_ref) <= TOL_Q8
     assert oracle.rel_err(ho.cpu().numpy(), h_ref) <= TOL_Q8
     assert oracle.rel_err(xw.cpu().numpy(), w.astype(np.float64) * h_ref) <= TOL_Q8
-    assert oracle.rel_err(parts.cpu().numpy(), _parts(h_ref)) <= TOL_Q8
+    assert oracle.rel_err(parts.cpu().numpy(), _parts(h_ref, pg.norm_parts(hidden))) <= TOL_Q8
+    assert abs(float(parts.double().sum()) / float((h_ref ** 2).sum()) - 1) <= TOL_Q8
     if not inplace:
         assert np.array_equal(hd.cpu().numpy(), h)
 
@@ -239,7 +241,7 @@ def test_gemv_q8_normed(pg, oracle, rows, cols, act):
     w = synth.norm_weight(rng, cols)
     h_ref, x_ref = oracle.add_rmsnorm(h, d, w, 1e-6)
     xw = (w.astype(np.float64) * h_ref).astype(np.float32)
-    parts = _parts(h_ref).astype(np.float32)
+    parts = _parts(h_ref, pg.norm_parts(cols)).astype(np.float32)
     y = pg.gemv_q8_normed(q8_dev(m, torch), to_dev(xw, torch), to_dev(parts, torch), 1e-6, act=act)
     torch.cuda.synchronize()
     idx = np.unique(rng.choice(rows, min(rows, 500), replace=False))
