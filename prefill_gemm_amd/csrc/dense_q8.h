@@ -1,0 +1,402 @@
+// Matrix-core engine of the batched prefill product over one pass of up to 64
+// positions (prefill_gemm_q8): every weight is read from HBM once per pass.
+//
+// nemotron_prefill.rs (module doc) sets the pass at PB_MAX = 64 positions so
+// that one stream of the weights serves all of them; gemma_batch.rs
+// (`q8_2f_mm_r2`) folds the per-column factor into the staged activations and
+// multiplies the row factor onto the finished sum.  Here the same contraction
+// runs on the bf16 matrix cores of gfx950 (v_mfma_f32_32x32x16_bf16):
+//  - a weight q in [-128, 127] is an exact bf16 integer (B operand, one weight
+//    row per output column of the instruction);
+//  - an activation x enters as x_hi = bf16(x) and x_lo = bf16(x - x_hi)
+//    (A operand, two products), exact to about 2^-17 relative;
+//  - the matrix core sums one 32-column block in f32, and the block's scale
+//    multiplies that block sum on the vector ALU (the scale belongs to one
+//    weight row and one block, so it cannot ride inside the contraction);
+//  - the bias term sum_blk bias[r][blk] * Xsum[m][blk] is a second
+//    contraction over blocks, K = 16 blocks an instruction, with the staged
+//    block sums (hi + lo) and the bias split hi + lo as well.
+//
+// Work of one workgroup: 128 weight rows x a range of blocks x all positions,
+// 2 NK waves.  Wave (rh, kq) owns rows 64 rh .. 64 rh + 63 (two matrix-core
+// row tiles, so every activation fragment read from LDS feeds two weight
+// tiles) and blocks kq * 4/NK .. of every stage of four blocks; the NK
+// partial sums of a row half meet in LDS at the end.  With NK = 4 two waves
+// share every SIMD, so one wave's matrix-core chain overlaps the other's
+// vector work.
+//
+// Memory path.  Every byte moves from global memory straight into LDS
+// (buffer loads to LDS, no registers), shared out over all waves, NX - 1
+// (activations, from L2) or NW - 1 (weights, from HBM) stages ahead:
+//  - weights: one instruction copies 8 rows x 128 contiguous bytes (the
+//    stage's four blocks of each row), so HBM sees whole lines of a row in one
+//    request; the lane -> (row, 16-byte piece) assignment is permuted so that
+//    the matrix-core reads (lane = row, one 16-byte piece) hit distinct LDS
+//    banks;
+//  - scales and biases: 16 rows x 4 blocks (4 bytes a lane) per instruction;
+//  - activation fragments and block sums: as staged, 1 KB per instruction.
+// A wave waits for its own copies of stage c + 1 (memory counter) before the
+// stage barrier; copies are issued in the same order every stage, so the wait
+// is one constant.  Stages past the end re-read the last block and weigh it
+// by zero, which keeps every stage one branch-free stretch.
+#pragma once
+
+#include "pg_device.h"
+
+// Weight stream cache policy: non-temporal (used once; keeps the activations in L2).
+#ifndef PG_DENSE_WNT
+#define PG_DENSE_WNT true
+#endif
+
+namespace pg {
+
+struct DenseArgs {
+    const int8_t *q;
+    const float *scale;
+    const float *bias;
+    int rows, cols;
+    const u32x4 *xp;  // staged A fragments [nb][mts][4][64] (see stage_x_frag_kernel)
+    const u32x4 *xs;  // staged block sums [ng][mts][2][64]
+    int mts;          // position tiles staged (>= MT)
+    int n;            // positions in use
+    float *out;       // out[m * ldo + r]
+    long long ldo;
+    int act;
+};
+
+template <int MT, int NK, int NX, int NW>
+struct DenseCfg {
+    static constexpr int kWaves = 2 * NK;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kRows = 128;
+    static constexpr int kKB = 4;                        // blocks per stage
+    static constexpr int kStagesPerGroup = 4;            // 16 blocks: one bias group
+    // LDS map, in 16-byte slots.
+    static constexpr int kXStage = kKB * MT * 4 * 64;    // activation fragments of a stage
+    static constexpr int kWq = 16 * 64;                  // 128 rows x 128 bytes
+    static constexpr int kWs = 128;                      // 128 rows x 4 scales
+    static constexpr int kWStage = kWq + kWs;
+    static constexpr int kBGroup = 512;                  // 128 rows x 16 biases of a group
+    static constexpr int kXBase = 0;
+    static constexpr int kWBase = NX * kXStage;
+    static constexpr int kBBase = kWBase + NW * kWStage;  // bias ring: 2 groups
+    static constexpr int kSBase = kBBase + 2 * kBGroup;   // block-sum ring: 2 groups
+    static constexpr int kSGroup = 2 * MT * 64;
+    static constexpr int kLdsU4 = kSBase + 2 * kSGroup;
+    static constexpr int kRedU4 = (NK - 1) * 2 * 2 * MT * 16 * 64 / 4;  // K partials of both row halves
+    static constexpr int kBPW = 4 / NK;                  // blocks per wave per stage
+    static constexpr int kXPer = 16 * MT / kWaves;       // activation fragments per wave per stage
+    static constexpr int kQPer = 16 / kWaves;            // weight copies (8 rows each)
+    static constexpr int kSPer = 8 / kWaves;             // scale copies (16 rows each)
+    static constexpr int kBPer = 32 / kWaves / 4;        // bias copies (4 rows x 16) per wave per stage
+    static_assert(NK == 4, "K waves per row half: one block per wave per stage");
+    static_assert(kRedU4 <= kLdsU4, "the partial sums fit the ring");
+    static_assert(kLdsU4 * 16 <= 160 * 1024, "LDS of one compute unit");
+    // Copies one wave issues per stage, and the memory-counter wait that
+    // leaves in flight only the copies issued after stage c + 1's activations.
+    static constexpr int kXCopies = kXPer + 1;
+    static constexpr int kWCopies = kQPer + kSPer + kBPer;
+    static constexpr int kWait = kWCopies + (NX - 2) * (kXCopies + kWCopies);
+    static_assert(NX >= 2 && NW > NX, "weights are requested further ahead than activations");
+    static_assert(kWait <= 63, "outstanding copies fit the memory counter");
+};
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): out-of-range lanes read zero.
+__device__ __forceinline__ i32x4 buf_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32) & 0xffff, (int32_t)bytes, 0x00020000};
+}
+
+// Copy SIZE (16 or 4) bytes a lane from buffer offset voff (per lane, range
+// checked) to LDS at lds_wave_base + SIZE * lane.  Written as inline assembly
+// so that the compiler does not see an LDS store it cannot place: it would
+// otherwise wait for every outstanding copy before each LDS read, which
+// serialises the rings.  Completion is tracked by hand (wait_vm) before the
+// stage barriers.  lds_addr is the LDS byte address of lane 0's destination.
+template <int SIZE, bool NT = false>
+__device__ __forceinline__ void lds_copy(const i32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    if constexpr (SIZE == 16 && NT)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(m0), "v"(voff),
+                     "s"(rsrc)
+                     : "memory", "m0");
+    else if constexpr (SIZE == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
+                     "s"(rsrc)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
+                     "s"(rsrc)
+                     : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS slot (16 bytes) of row (0..127) and 16-byte piece s (0..7) of a weight
+// stage.  Copy instruction i = row / 8 holds rows 8i .. 8i + 7; its lane l
+// carries row 8i + ((l / 8) ^ (i & 1)) and piece (l % 8) ^ (row % 8).  For a
+// fixed piece, 16 consecutive rows land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int wq_slot(int row, int s) {
+    const int i = row >> 3, r8 = row & 7;
+    return i * 64 + 8 * (r8 ^ (i & 1)) + (s ^ r8);
+}
+
+template <int MT, int NK, int NX, int NW>
+__device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base, const int kb0,
+                                            const int kb1, u32x4 *lds) {
+    using C = DenseCfg<MT, NK, NX, NW>;
+    constexpr int KB = C::kKB;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = P.cols >> 5;
+    const int ng = (nb + 15) >> 4;
+    const int nst = (kb1 - kb0 + 15) / 16 * C::kStagesPerGroup;
+
+    // ------------------------------------------------------------ copies
+    // Per-lane buffer offsets at stage 0; a stage adds a wave-uniform step.
+    // Reads past a row's blocks (the tail stage of a range) fetch valid bytes
+    // that are weighted by zero; reads past a buffer's end return zero.
+    const i32x4 rq = buf_rsrc(P.q, (uint32_t)P.rows * (uint32_t)P.cols);
+    const i32x4 rs = buf_rsrc(P.scale, (uint32_t)P.rows * nb * 4u);
+    const i32x4 rb = buf_rsrc(P.bias, (uint32_t)P.rows * nb * 4u);
+    const i32x4 rx = buf_rsrc(P.xp, (uint32_t)nb * P.mts * 4096u);
+    const i32x4 rxs = buf_rsrc(P.xs, (uint32_t)ng * P.mts * 2048u);
+    // LDS byte address of slot i (16 bytes) of the ring.
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4 *)lds;
+    auto laddr = [&](int slot) __attribute__((always_inline)) { return lbase + 16u * (uint32_t)slot; };
+    uint32_t oq[C::kQPer], os[C::kSPer];
+#pragma unroll
+    for (int k = 0; k < C::kQPer; ++k) {
+        const int i = C::kQPer * w + k;
+        const int r8 = (lane >> 3) ^ (i & 1);
+        const int s = (lane & 7) ^ r8;
+        oq[k] = (uint32_t)(r_base + 8 * i + r8) * (uint32_t)P.cols + (uint32_t)(kb0 * 32 + (s >> 1) * 32 + (s & 1) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < C::kSPer; ++k)
+        os[k] = ((uint32_t)(r_base + 16 * (C::kSPer * w + k) + (lane >> 2)) * (uint32_t)nb +
+                 (uint32_t)(kb0 + (lane & 3))) * 4u;
+    // Fragment g = w * kXPer + f of a stage is block g / (4 MT), fragment g % (4 MT).
+    const uint32_t ox = ((uint32_t)(kb0 * P.mts * 4) * 64u + lane) * 16u;
+    const int fs = w % (2 * MT);
+    const uint32_t oxs = ((uint32_t)((((kb0 >> 4) * P.mts + fs % MT) * 2 + fs / MT) * 64) + lane) * 16u;
+
+    // Activation fragments of stage c and one block-sum fragment of its group
+    // (fragment w mod 2 MT), into X slot c % NX.
+    auto copy_x = [&](int c) __attribute__((always_inline)) {
+        const int xslot = C::kXBase + (c % NX) * C::kXStage;
+        const uint32_t step = (uint32_t)(c * KB * P.mts) * 4096u;
+#pragma unroll
+        for (int f = 0; f < C::kXPer; ++f) {
+            const int g = w * C::kXPer + f;
+            const uint32_t src = (uint32_t)((g / (4 * MT)) * P.mts * 4 + g % (4 * MT)) * 1024u;
+            lds_copy<16>(rx, ox + step + src, laddr(xslot + g * 64));
+        }
+        const int it = c / C::kStagesPerGroup;
+        lds_copy<16>(rxs, oxs + (uint32_t)(it * P.mts) * 2048u, laddr(C::kSBase + (it & 1) * C::kSGroup + fs * 64));
+    };
+    // Weights and scales of stage c for this wave's rows, into W slot c % NW
+    // (layout: q pieces by wq_slot, then [row][4] scales), and this wave's
+    // share of the biases of the next group (4 rows x 16 blocks a copy, layout
+    // [row][16]) into bias slot (group + 1) % 2.
+    const uint32_t ob = ((uint32_t)(r_base + (lane >> 4)) * (uint32_t)nb + (uint32_t)(kb0 + 16 + (lane & 15))) * 4u;
+    auto copy_b = [&](int it, int p) __attribute__((always_inline)) {
+        // rows 4p .. 4p + 3 of group it
+        lds_copy<4>(rb, ob + (uint32_t)(4 * p) * (uint32_t)nb * 4u + (uint32_t)(16 * (it - 1)) * 4u,
+                    laddr(C::kBBase + (it & 1) * C::kBGroup + p * 16));
+    };
+    auto copy_w = [&](int c) __attribute__((always_inline)) {
+        const int wslot = C::kWBase + (c % NW) * C::kWStage;
+        const uint32_t sq = (uint32_t)(c * KB) * 32u, ss = (uint32_t)(c * KB) * 4u;
+#pragma unroll
+        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, PG_DENSE_WNT>(rq, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
+#pragma unroll
+        for (int k = 0; k < C::kSPer; ++k)
+            lds_copy<4>(rs, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
+    };
+
+    // Prologue: W(0), X(0), X(1 .. NX - 2), W(1 .. NW - 2).
+    copy_w(0);
+    copy_x(0);
+    for (int c = 1; c < NX - 1; ++c) copy_x(c);
+    for (int c = 1; c < NW - 1; ++c) copy_w(c);
+#pragma unroll
+    for (int k = 0; k < 4 * C::kBPer; ++k) copy_b(0, (4 * w + k / C::kBPer) * C::kBPer + k % C::kBPer);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+
+    // ------------------------------------------------------------ compute
+    const int rh = w & 1, kq = w >> 1;
+    const int h = lane >> 5;
+    const int ml = lane & 31;
+    f32x16 acc[2][MT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x16{};
+    const f32x16 zero{};
+    // Software pipeline over the two row tiles: a stage's matrix-core chain of
+    // tile 0 runs while the vector ALU applies the previous stage's tile-1
+    // scale and converts tile 1's weights; tile 1's chain runs while tile 0's
+    // scale is applied.  Tile 1's products (t1, scale s1) carry over the barrier.
+    f32x16 t1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) t1[mt] = zero;
+    float s1 = 0.0f;
+
+    for (int c = 0; c < nst; ++c) {
+        const int u = c % C::kStagesPerGroup;
+        const int it = c / C::kStagesPerGroup;
+        // Refill the slots stage c - 1 used (every wave is past it), and copy a
+        // share of the next group's biases (its slot was last read a group ago).
+        copy_x(c + NX - 1);
+        copy_w(c + NW - 1);
+#pragma unroll
+        for (int k = 0; k < C::kBPer; ++k) copy_b(it + 1, (4 * w + u) * C::kBPer + k);
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4 *xst = lds + C::kXBase + (c % NX) * C::kXStage + lane;
+        const u32x4 *wst = lds + C::kWBase + (c % NW) * C::kWStage;
+        const float *sst = reinterpret_cast<const float *>(wst + C::kWq);
+
+        const int kbl = kq;  // one block per wave per stage
+        const bool live = kb0 + c * KB + kbl < kb1;
+        u32x4 a[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int fi = 0; fi < 4; ++fi) a[mt][fi] = xst[((kbl * MT + mt) * 4 + fi) * 64];
+        const int row0 = 64 * rh + ml, row1 = row0 + 32;
+        const u32x4 q0 = wst[wq_slot(row0, 2 * kbl + h)];
+        const u32x4 q1 = wst[wq_slot(row1, 2 * kbl + h)];
+        const float sl0 = sst[4 * row0 + kbl], sl1 = sst[4 * row1 + kbl];
+        const float s0 = live ? sl0 : 0.0f;
+        bf16x8 b00, b01, b10, b11;
+        q16_to_bf16(q0, b00, b01);
+        // tile 0 chain; previous tile 1 scale step; tile 1 weights converted
+        f32x16 t0[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            t0[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b00, zero);
+            t0[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b01, t0[mt]);
+            t0[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b00, t0[mt]);
+            t0[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b01, t0[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[1][mt][v] = fmaf(s1, t1[mt][v], acc[1][mt][v]);
+        q16_to_bf16(q1, b10, b11);
+        // tile 1 chain; tile 0 scale step
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            t1[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b10, zero);
+            t1[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b11, t1[mt]);
+            t1[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b10, t1[mt]);
+            t1[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b11, t1[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[0][mt][v] = fmaf(s0, t0[mt][v], acc[0][mt][v]);
+        s1 = live ? sl1 : 0.0f;
+        // Issue order: LDS reads, tile 0's conversion, then each matrix-core
+        // instruction followed by a slice of independent vector work.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * MT + 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (16 * MT + 24) / (4 * MT), 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        if (u == C::kStagesPerGroup - 1 && kq == it % NK) {
+            // Bias term of the group on one K wave (in turn); zero past kb1.
+            const u32x4 *sf = lds + C::kSBase + (it & 1) * C::kSGroup + lane;
+            const float *bg = reinterpret_cast<const float *>(lds + C::kBBase + (it & 1) * C::kBGroup);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int row = 64 * rh + 32 * rt + ml;
+                const float4 b0 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h);
+                const float4 b1 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h + 4);
+                const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                bf16x8 bh, bl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float v = kb0 + 16 * it + 8 * h + i < kb1 ? bv[i] : 0.0f;
+                    const __bf16 vh = to_bf16(v);
+                    bh[i] = vh;
+                    bl[i] = to_bf16(v - (float)vh);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 sh = as_bf16x8(sf[mt * 64]), sl = as_bf16x8(sf[(MT + mt) * 64]);
+                    acc[rt][mt] = mfma_bf16(sh, bh, acc[rt][mt]);
+                    acc[rt][mt] = mfma_bf16(sl, bh, acc[rt][mt]);
+                    acc[rt][mt] = mfma_bf16(sh, bl, acc[rt][mt]);
+                }
+            }
+        }
+
+        // Stage c + 1's copies must have landed before the barrier.
+        wait_vm<C::kWait>();
+        __builtin_amdgcn_s_barrier();
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[1][mt][v] = fmaf(s1, t1[mt][v], acc[1][mt][v]);
+
+    // ------------------------------------------------------------ epilogue
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing refills
+    __builtin_amdgcn_s_barrier();
+    float *red = reinterpret_cast<float *>(lds);
+    auto red_at = [&](int k, int rt, int mt, int v) __attribute__((always_inline)) {
+        return ((((k - 1) * 2 + rh) * 2 + rt) * MT + mt) * 16 * 64 + v * 64 + lane;
+    };
+    if (kq > 0) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[red_at(kq, rt, mt, v)] = acc[rt][mt][v];
+    }
+    __syncthreads();
+    if (kq > 0) return;
+    // Tile by tile: add the other K waves' partials (in order), then store.
+    // Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h + (v % 4), row r.
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int r = r_base + 64 * rh + 32 * rt + ml;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x16 t = acc[rt][mt];
+#pragma unroll
+            for (int k = 1; k < NK; ++k)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) t[v] += red[red_at(k, rt, mt, v)];
+            if (r < P.rows) {
+                float *o = P.out + r;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (m < P.n) o[m * P.ldo] = apply_act(P.act, t[v]);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pg

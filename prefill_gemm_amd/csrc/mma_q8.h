@@ -58,17 +58,6 @@ struct MmaPanel {
     int frag;                 // 1: fragment layout (dense rows, MT tiles staged), 0: row layout
 };
 
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that f can
-// index register arrays with a compile-time constant.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 constexpr int kPanelRows = 128;
 constexpr int kChunk = 4;
 

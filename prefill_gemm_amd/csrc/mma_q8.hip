@@ -7,6 +7,7 @@
 // for) shapes its tile does not cover.
 #include <algorithm>
 
+#include "dense_q8.h"
 #include "mma_q8.h"
 #include "mma_launch.h"
 #include "pg_host.h"
@@ -208,13 +209,25 @@ int launch_stage_x(const float *X, int rows, int cols, void *xp, void *xs, hipSt
 }
 
 // Dense pass: workgroup id -> (panel of 128 rows, K split).  Splits of one
-// panel take consecutive ids, so with 8 or fewer splits the workgroups that
-// read the same activation blocks land on the same XCD (ids are dealt to the
-// 8 XCDs round robin).
+// panel take consecutive ids.  The activation ring is dynamic LDS (more than
+// the 64 KB a static array may take).
+#ifndef PG_DENSE_NX
+#define PG_DENSE_NX 2
+#endif
+#ifndef PG_DENSE_NW
+#define PG_DENSE_NW 4
+#endif
+#ifndef PG_DENSE_NK
+#define PG_DENSE_NK 4
+#endif
+constexpr int kDNK = PG_DENSE_NK, kDNX = PG_DENSE_NX, kDNW = PG_DENSE_NW;
 template <int MT>
-__global__ __launch_bounds__(kMmaThreads) void mma_dense_kernel(MmaPanel P, int splits, int bps,
-                                                        float *partials, long long plane) {
-    __shared__ u32x4 lds[2 * kChunk * MT * 4 * 64];
+using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
+
+template <int MT>
+__global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int splits, int bps,
+                                                                   float *partials, long long plane) {
+    extern __shared__ u32x4 dlds[];
     const int id = blockIdx.x;
     const int split = id % splits, panel = id / splits;
     const int nb = P.cols >> 5;
@@ -224,7 +237,18 @@ __global__ __launch_bounds__(kMmaThreads) void mma_dense_kernel(MmaPanel P, int 
         P.out = partials + (long long)split * plane;
         P.act = 0;
     }
-    mma_panel<MT, kWch>(P, panel * kPanelRows, kb0, kb1, lds);
+    dense_panel<MT, kDNK, kDNX, kDNW>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
+}
+
+template <int MT>
+static int launch_dense(const DenseArgs &P, int grid, int splits, int bps, float *parts, long long plane,
+                        hipStream_t s) {
+    constexpr size_t lds = (size_t)DCfg<MT>::kLdsU4 * sizeof(u32x4);
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return PG_ELAUNCH;
+    hipLaunchKernelGGL(dense_kernel<MT>, dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, splits, bps, parts, plane);
+    return launch_status();
 }
 
 // Y[i] = act( sum_{s < splits} parts[s][i] ), the splits added in order.
@@ -270,16 +294,17 @@ int launch_expert_bank(const MmaPanel &P, int experts, const int32_t *counts,
     return launch_status();
 }
 
-// K splits of a dense pass: enough workgroups to cover the 256 compute units
-// without cutting a split below 8 blocks; large matrices run unsplit.
-int dense_splits(int rows, int cols) {
-    const int panels = ceil_div(rows, kPanelRows);
-    const int nb = cols / 32;
-    if (panels >= 200) return 1;
-    int s = ceil_div(256, panels);
-    s = std::min(s, std::max(1, nb / 8));
-    return std::max(1, s);
+// Blocks per K split of a dense pass: a multiple of 16 (one bias group per
+// loop iteration), with as many splits as keep panels x splits within one
+// workgroup per compute unit (256).
+int dense_blocks_per_split(int rows, int cols) {
+    const int panels = ceil_div(rows, DCfg<2>::kRows);
+    const int groups = ceil_div(cols / 32, 16);
+    const int s = std::min(std::max(1, 256 / panels), groups);
+    return 16 * ceil_div(groups, s);
 }
+
+int dense_splits(int rows, int cols) { return ceil_div(cols / 32, dense_blocks_per_split(rows, cols)); }
 
 }  // namespace pg
 
@@ -340,7 +365,7 @@ static int prefill_run(const int8_t *q, const float *scale, const float *bias, i
     int rc = launch_status();
     if (rc) return rc;
 
-    MmaPanel P{};
+    DenseArgs P{};
     P.q = q;
     P.scale = scale;
     P.bias = bias;
@@ -348,27 +373,19 @@ static int prefill_run(const int8_t *q, const float *scale, const float *bias, i
     P.cols = cols;
     P.xp = reinterpret_cast<const u32x4 *>(xp);
     P.xs = reinterpret_cast<const u32x4 *>(xs);
-    P.zero_row = n;
-    P.frag = 1;
-    P.src_list = nullptr;
-    P.src_div = 1;
-    P.m_valid = n;
+    P.mts = mts;
+    P.n = n;
     P.out = Y;
     P.ldo = rows;
-    P.out_list = nullptr;
     P.act = act;
 
-    const int splits = dense_splits(rows, cols);
     const int nb = cols / 32;
-    const int bps = ceil_div(nb, splits);
+    const int bps = dense_blocks_per_split(rows, cols);
     const int used = ceil_div(nb, bps);  // splits that hold at least one block
-    const int grid = ceil_div(rows, kPanelRows) * used;
+    const int grid = ceil_div(rows, DCfg<2>::kRows) * used;
     const long long plane = (long long)n * rows;
-    if (n > 32)
-        hipLaunchKernelGGL(mma_dense_kernel<2>, dim3(grid), dim3(kMmaThreads), 0, s, P, used, bps, parts, plane);
-    else
-        hipLaunchKernelGGL(mma_dense_kernel<1>, dim3(grid), dim3(kMmaThreads), 0, s, P, used, bps, parts, plane);
-    rc = launch_status();
+    rc = mts == 2 ? launch_dense<2>(P, grid, used, bps, parts, plane, s)
+                  : launch_dense<1>(P, grid, used, bps, parts, plane, s);
     if (rc || used == 1) return rc;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256), 0, s,
                        parts, used, plane, Y, act);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace pg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -83,5 +85,16 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) { return __builtin_bi
 
 // Round-to-nearest-even bf16 of an f32 (the gfx950 packed converter).
 __device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that f can
+// index register arrays with a compile-time constant.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace pg
