@@ -201,6 +201,53 @@ def component_prompt(torch, frames, inp, reps=3):
             "ms": round(ms, 3), "positions_per_s": round(420 / (ms * 1e-3), 1)}
 
 
+def component_decode_single_launch(torch, pg, synth, reps=40):
+    """The same decode frame as ONE persistent launch (decode_frame_q8), each
+    weight copy's call captured into a graph and the graphs replayed alternately."""
+    Ws, out = [], None
+    for c in range(2):
+        f = synth.frame_weights(seed=c)
+        Ws.append(({k: q8_dev(torch, pg, f[k]) for k in ("qkv", "up", "down", "head")},
+                   to_dev(torch, f["w1"]), to_dev(torch, f["w2"]), f["eps"]))
+        del f
+    W0 = Ws[0][0]
+    H, I = W0["qkv"].cols, W0["up"].rows
+    out = {"qkv": torch.empty(W0["qkv"].rows, device="cuda"), "u": torch.empty(I, device="cuda"),
+           "d": torch.empty(H, device="cuda"), "logits": torch.empty(W0["head"].rows, device="cuda")}
+    rng = synth.streams(13, 2)
+    x0 = to_dev(torch, synth.normal(rng[0], H))
+    h = to_dev(torch, synth.normal(rng[1], H))
+    ws = pg.decode_frame_q8_workspace(H, I)
+
+    def call(c):
+        W, w1, w2, eps = Ws[c]
+        pg.decode_frame_q8(W["qkv"], W["up"], W["down"], W["head"], w1, w2, eps, x0, h, out, ws)
+
+    graphs = []
+    s = torch.cuda.Stream()
+    for c in range(2):
+        call(c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call(c)
+        graphs.append(g)
+    for i in range(4):
+        graphs[i % 2].replay()
+    t = Timer(torch)
+    torch.cuda.synchronize()
+    s0 = t.start()
+    for i in range(reps):
+        graphs[i % 2].replay()
+    t.stop(s0)
+    torch.cuda.synchronize()
+    us = t.total_ms() / reps * 1e3
+    nbytes = sum(w.nbytes() for w in W0.values())
+    return {"workload": "q8 decode frame (hidden 4096) as one persistent launch, graph replays over 2 weight copies",
+            "us_per_frame": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "barrier_timeouts": pg.decode_frame_timeouts(ws)}
+
+
 def component_moe(torch, pg, synth, reps=10):
     c = synth.moe(0)
     up, down = q8_dev(torch, pg, c["up"]), q8_dev(torch, pg, c["down"])
@@ -350,6 +397,8 @@ def main():
                 "f16_gemv_4096": component_f16(torch, pg, synth),
                 "prompt_420": component_prompt(torch, frames, inp)}
         del frames
+        torch.cuda.empty_cache()
+        comp["decode_frame_single_launch"] = component_decode_single_launch(torch, pg, synth)
         torch.cuda.empty_cache()
         comp["moe_pass"] = component_moe(torch, pg, synth)
         result["components"] = comp

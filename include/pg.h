@@ -53,6 +53,16 @@ enum {
     PG_EWORKSPACE = -4     /* workspace pointer NULL or smaller than the query returns */
 };
 
+/* A q8-block matrix on the device (the format above): q [rows][cols] int8,
+ * scale and bias [rows][cols/32] f32. */
+typedef struct pg_q8 {
+    const int8_t *q;
+    const float *scale;
+    const float *bias;
+    int32_t rows;
+    int32_t cols;
+} pg_q8;
+
 /* Human-readable text of a PG_* code (static storage). */
 const char *pg_strerror(int code);
 
@@ -175,6 +185,49 @@ int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bi
                             const float *w, float eps, int32_t n, float *H_out, float *X_out,
                             float *Y, int32_t act, void *workspace, size_t workspace_bytes,
                             pg_stream_t stream);
+
+/*
+ * decode_frame_q8 — the whole q8 decode layer frame at one position in ONE
+ * launch (embryo_wide.wgsl, header comment: the token frame fuses its stages
+ * because each dispatch boundary costs microseconds; nemotron_prefill.rs
+ * `pb_add_rms`, add = 1, between the matrix stages; `pb_relu2` on the up
+ * product):
+ *     qkv    = Wqkv x0                       [rows_qkv], rows_qkv >= H
+ *     h1     = h + qkv[:H];   x1 = w1 * h1 / sqrt(mean(h1^2) + eps)
+ *     u      = relu^2(Wup x1)                [I]
+ *     d      = Wdown u                       [H]
+ *     h2     = h1 + d;        x2 = w2 * h2 / sqrt(mean(h2^2) + eps)
+ *     logits = Whead x2                      [V]
+ *     h     <- h2  (in place)
+ * with H = qkv_w->cols = up_w->cols = head_w->cols = down_w->rows and
+ * I = up_w->rows = down_w->cols.  One workgroup per compute unit runs the
+ * four products on its share of each matrix's rows, with a device-wide
+ * barrier between products; each weight byte is read once.  The barrier
+ * needs every workgroup resident at once: the launch takes the whole device
+ * (one workgroup per compute unit), so work on other streams that holds
+ * compute units for the length of the launch delays it.  Barrier waits are
+ * bounded (about a second) instead of hanging, and count themselves
+ * (below).  The call may be captured into a graph.  The mean of squares is
+ * summed in one fixed order, the same for every launch and every row.
+ *   x0 [H], h [H] in/out, w1, w2 [H], qkv [rows_qkv], u [I], d [H],
+ *   logits [V]: f32 device vectors, 16-byte aligned, not overlapping.
+ *   workspace: at least decode_frame_q8_workspace_bytes(H, I) bytes, set up
+ *   once by decode_frame_q8_workspace_init before its first use (it holds
+ *   the barrier counters, a launch counter, w * h and the norm sums).  The
+ *   32-bit word at byte offset 8 counts barrier waits that gave up; non-zero
+ *   means a launch's outputs are not to be trusted.  Launches that share a
+ *   workspace must not overlap (same stream, or ordered streams).
+ * PG_EUNSUPPORTED: a cols % 1024 != 0 or > 16384, a matrix of 2^31 or more
+ *   bytes, or one with more than about 2047 rows per compute unit.
+ *   PG_EINVAL: shapes that do not chain as above, null or misaligned
+ *   pointers, eps < 0 or NaN.  PG_EWORKSPACE: workspace missing or small.
+ */
+size_t decode_frame_q8_workspace_bytes(int32_t hidden, int32_t inter);
+int decode_frame_q8_workspace_init(void *workspace, size_t workspace_bytes, pg_stream_t stream);
+int decode_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                    const float *w1, const float *w2, float eps, const float *x0, float *h, float *qkv,
+                    float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
+                    pg_stream_t stream);
 
 /*
  * add_rmsnorm — fused residual add + RMSNorm, per position b < n

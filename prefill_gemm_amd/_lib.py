@@ -45,6 +45,12 @@ _f = ctypes.c_float
 _sz = ctypes.c_size_t
 
 
+class PgQ8(ctypes.Structure):
+    """struct pg_q8 of pg.h."""
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
 def _declare(L):
     L.pg_strerror.argtypes = [ctypes.c_int]
     L.pg_strerror.restype = ctypes.c_char_p
@@ -66,8 +72,14 @@ def _declare(L):
     L.gemv_q8_normed.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _f, _P, _i32, _P]
     L.gemv_q8_norm_parts.argtypes = [_i32]
     L.gemv_q8_norm_parts.restype = _i32
+    L.decode_frame_q8_workspace_bytes.argtypes = [_i32, _i32]
+    L.decode_frame_q8_workspace_bytes.restype = _sz
+    L.decode_frame_q8_workspace_init.argtypes = [_P, _sz, _P]
+    _q8p = ctypes.POINTER(PgQ8)
+    L.decode_frame_q8.argtypes = [_q8p, _q8p, _q8p, _q8p, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
-                 "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed"):
+                 "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
+                 "decode_frame_q8_workspace_init", "decode_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
 
 
@@ -366,3 +378,47 @@ def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight,
         _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o
+
+
+def decode_frame_q8_workspace_bytes(hidden: int, inter: int) -> int:
+    return lib().decode_frame_q8_workspace_bytes(hidden, inter)
+
+
+def decode_frame_q8_workspace(hidden: int, inter: int, device="cuda", stream=None) -> torch.Tensor:
+    """A cleared workspace for decode_frame_q8 at these sizes (hidden, up rows)."""
+    ws = torch.empty(decode_frame_q8_workspace_bytes(hidden, inter), dtype=torch.uint8, device=device)
+    _check("decode_frame_q8_workspace_init",
+           lib().decode_frame_q8_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def decode_frame_timeouts(workspace: torch.Tensor) -> int:
+    """Waits that gave up in launches on this workspace (the counter at byte 8)."""
+    return int(workspace[8:12].view(torch.int32).item())
+
+
+def _q8struct(W: Q8Weight, name: str) -> PgQ8:
+    W.validate(name)
+    return PgQ8(W.q.data_ptr(), W.scale.data_ptr(), W.bias.data_ptr(), W.rows, W.cols)
+
+
+def decode_frame_q8(qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight, w1: torch.Tensor,
+                    w2: torch.Tensor, eps: float, x0: torch.Tensor, h: torch.Tensor, out: dict,
+                    workspace: torch.Tensor, stream=None) -> dict:
+    """The q8 decode layer frame at one position in one launch: h is updated in place and
+    out = {qkv, u, d, logits} (f32 device vectors) receives the four products."""
+    Ws = [_q8struct(W, nm) for W, nm in ((qkv, "qkv"), (up, "up"), (down, "down"), (head, "head"))]
+    for t, nm in ((w1, "w1"), (w2, "w2"), (x0, "x0"), (h, "h")):
+        _dev(t, torch.float32, nm)
+    H = qkv.cols
+    for k, n in (("qkv", qkv.rows), ("u", up.rows), ("d", H), ("logits", head.rows)):
+        _dev(out[k], torch.float32, k)
+        if out[k].numel() != n:
+            raise ValueError(f"out[{k!r}] must have {n} elements")
+    if any(t.numel() != H for t in (w1, w2, x0, h)):
+        raise ValueError("w1, w2, x0 and h must have qkv.cols elements")
+    _dev(workspace, torch.uint8, "workspace")
+    _check("decode_frame_q8", lib().decode_frame_q8(
+        *[ctypes.byref(W) for W in Ws], _ptr(w1), _ptr(w2), eps, _ptr(x0), _ptr(h), _ptr(out["qkv"]),
+        _ptr(out["u"]), _ptr(out["d"]), _ptr(out["logits"]), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -15,7 +15,7 @@ inline hipStream_t as_stream(pg_stream_t s) { return reinterpret_cast<hipStream_
 // Status of the launch just issued.
 inline int launch_status() { return hipGetLastError() == hipSuccess ? PG_OK : PG_ELAUNCH; }
 
-inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+constexpr size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -28,3 +28,19 @@ def exact_q8(rng, rows, cols, lead=()):
 
 def int_acts(rng, shape, lim=8):
     return rng.integers(-lim, lim + 1, size=shape).astype(np.float32)
+
+
+def oracle_frame(oracle, f, x0, h0):
+    """The frame chain on the oracle, every intermediate rounded to the f32 buffer it lives in."""
+    H = f["qkv"].cols
+    g = lambda m, x, act=0: oracle.gemm_q8(m.q, m.scale, m.bias, x, act=act)
+    s = {}
+    s["qkv"] = g(f["qkv"], x0).astype(np.float32)
+    s["h1"], x1 = oracle.add_rmsnorm(h0, s["qkv"], f["w1"], f["eps"], delta_stride=s["qkv"].shape[1])
+    s["x1"] = x1.astype(np.float32)
+    s["u"] = g(f["up"], s["x1"], act=1).astype(np.float32)
+    s["d"] = g(f["down"], s["u"]).astype(np.float32)
+    s["h2"], x2 = oracle.add_rmsnorm(s["h1"].astype(np.float32), s["d"], f["w2"], f["eps"])
+    s["x2"] = x2.astype(np.float32)
+    s["logits"] = g(f["head"], s["x2"])
+    return s

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_Q8, q8_dev, to_dev
+from helpers import TOL_Q8, oracle_frame, q8_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,22 +23,6 @@ def pg():
 
 def _case(msg):
     print(f"[case] {msg}", flush=True)
-
-
-def oracle_frame(oracle, f, x0, h0):
-    """The frame chain on the oracle, every intermediate rounded to the f32 buffer it lives in."""
-    H = f["qkv"].cols
-    g = lambda m, x, act=0: oracle.gemm_q8(m.q, m.scale, m.bias, x, act=act)
-    s = {}
-    s["qkv"] = g(f["qkv"], x0).astype(np.float32)
-    s["h1"], x1 = oracle.add_rmsnorm(h0, s["qkv"], f["w1"], f["eps"], delta_stride=s["qkv"].shape[1])
-    s["x1"] = x1.astype(np.float32)
-    s["u"] = g(f["up"], s["x1"], act=1).astype(np.float32)
-    s["d"] = g(f["down"], s["u"]).astype(np.float32)
-    s["h2"], x2 = oracle.add_rmsnorm(s["h1"].astype(np.float32), s["d"], f["w2"], f["eps"])
-    s["x2"] = x2.astype(np.float32)
-    s["logits"] = g(f["head"], s["x2"])
-    return s
 
 
 def _frame(pg, f, n):
