@@ -157,6 +157,8 @@ int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const float *x, floa
  * activations as an exact-to-2^-17 bf16 hi+lo pair, products accumulate in
  * f32 per 32-column block, the block scale multiplies each block sum in f32
  * and the bias term sum_blk bias[r][blk] * (sum_{c in blk} X[b][c]) is added.
+ * Where the K range is split over workgroups, the partial sums are added in
+ * split order (the result does not depend on timing).
  * PG_EUNSUPPORTED: cols % 32 != 0, n < 1 or n > 64.
  */
 int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows,
@@ -228,6 +230,43 @@ int decode_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, 
                     const float *w1, const float *w2, float eps, const float *x0, float *h, float *qkv,
                     float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
                     pg_stream_t stream);
+
+/*
+ * prefill_frame_q8 — the q8 layer frame over one prefill pass of n <= 64
+ * positions, every weight read once (nemotron_prefill.rs, module doc: a pass
+ * of up to PB_MAX = 64 positions; `pb_add_rms`, add = 1, between the matrix
+ * stages; `pb_relu2` on the up product), per position b:
+ *     qkv[b]    = Wqkv X0[b]
+ *     h1        = H[b] + qkv[b][:H];   x1 = w1 * h1 / sqrt(mean(h1^2) + eps)
+ *     u[b]      = relu^2(Wup x1)
+ *     d[b]      = Wdown u[b]
+ *     h2        = h1 + d[b];           x2 = w2 * h2 / sqrt(mean(h2^2) + eps)
+ *     logits[b] = Whead x2
+ *     H[b]     <- h2  (in place)
+ * with H = qkv_w->cols = up_w->cols = head_w->cols = down_w->rows and
+ * I = up_w->rows = down_w->cols.  Five launches: the staging of X0, then the
+ * four matrix-core passes; each pass finishes the add + RMSNorm work around
+ * it in its epilogue (the residual add, the staging of w * h' for the next
+ * product, per-position sums of squares) and the next pass multiplies its
+ * finished sums by the position's 1 / rms, so the norm needs no pass of its
+ * own.  Split-K partial sums are added in split order inside the passes.
+ * Arithmetic of each product as prefill_gemm_q8 (the product of a normed
+ * input runs on w * h' and is scaled afterwards); sums of squares and split
+ * partials are added in fixed orders, so results repeat bit for bit.
+ *   X0, H [n][H]; w1, w2 [H]; qkv [n][rows_qkv]; u [n][I]; d [n][H];
+ *   logits [n][V]: f32 device arrays, 16-byte aligned, not overlapping each
+ *   other or the workspace.  workspace: prefill_frame_q8_workspace_bytes(H,
+ *   rows_qkv, I, V, n) bytes (contents on entry do not matter).
+ * PG_EUNSUPPORTED: a cols % 32 != 0 (so H and I are multiples of 32), n > 64.
+ *   PG_EINVAL: shapes that do not chain as above, null or misaligned pointers, n < 1, eps < 0 or
+ *   NaN.  PG_EWORKSPACE: workspace missing or small.
+ */
+size_t prefill_frame_q8_workspace_bytes(int32_t hidden, int32_t qkv_rows, int32_t inter, int32_t vocab,
+                                        int32_t n);
+int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                     const float *w1, const float *w2, float eps, const float *X0, float *H, int32_t n,
+                     float *qkv, float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
+                     pg_stream_t stream);
 
 /*
  * add_rmsnorm — fused residual add + RMSNorm, per position b < n

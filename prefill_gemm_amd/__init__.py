@@ -9,7 +9,8 @@ from ._lib import (PG_EINVAL, PG_ELAUNCH, PG_EUNSUPPORTED, PG_EWORKSPACE, PG_OK,
                    Q8Weight, add_rmsnorm, decode_frame_q8, decode_frame_q8_workspace,
                    decode_frame_q8_workspace_bytes, decode_frame_timeouts, gemv_f16, gemv_q8, gemv_q8_addnorm, gemv_q8_normed,
                    gemv_q8_residual, lib, moe_grouped, norm_parts,
-                   moe_grouped_workspace_bytes, prefill_gemm_q8, prefill_gemm_q8_addnorm,
+                   moe_grouped_workspace_bytes, prefill_frame_q8, prefill_frame_q8_workspace_bytes,
+                   prefill_gemm_q8, prefill_gemm_q8_addnorm,
                    prefill_gemm_q8_workspace_bytes,
                    strerror, version)
 from .frame import PB_MAX, Frame
@@ -19,7 +20,8 @@ lib()
 __all__ = ["PG_OK", "PG_EINVAL", "PG_EUNSUPPORTED", "PG_ELAUNCH", "PG_EWORKSPACE", "PGError",
            "Q8Weight", "decode_frame_q8", "decode_frame_q8_workspace", "decode_frame_q8_workspace_bytes",
            "decode_frame_timeouts", "gemv_q8", "gemv_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
-           "norm_parts", "gemv_f16", "prefill_gemm_q8", "prefill_gemm_q8_addnorm",
+           "norm_parts", "gemv_f16", "prefill_frame_q8", "prefill_frame_q8_workspace_bytes",
+           "prefill_gemm_q8", "prefill_gemm_q8_addnorm",
            "prefill_gemm_q8_workspace_bytes",
            "add_rmsnorm", "moe_grouped", "moe_grouped_workspace_bytes", "strerror", "version",
            "lib", "Frame", "PB_MAX"]

@@ -72,6 +72,9 @@ def _declare(L):
     L.gemv_q8_normed.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _f, _P, _i32, _P]
     L.gemv_q8_norm_parts.argtypes = [_i32]
     L.gemv_q8_norm_parts.restype = _i32
+    L.prefill_frame_q8_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.prefill_frame_q8_workspace_bytes.restype = _sz
+    L.prefill_frame_q8.argtypes = [ctypes.POINTER(PgQ8)] * 4 + [_P, _P, _f, _P, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
     L.decode_frame_q8_workspace_bytes.argtypes = [_i32, _i32]
     L.decode_frame_q8_workspace_bytes.restype = _sz
     L.decode_frame_q8_workspace_init.argtypes = [_P, _sz, _P]
@@ -79,7 +82,7 @@ def _declare(L):
     L.decode_frame_q8.argtypes = [_q8p, _q8p, _q8p, _q8p, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
-                 "decode_frame_q8_workspace_init", "decode_frame_q8"):
+                 "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
 
 
@@ -420,5 +423,31 @@ def decode_frame_q8(qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight,
     _dev(workspace, torch.uint8, "workspace")
     _check("decode_frame_q8", lib().decode_frame_q8(
         *[ctypes.byref(W) for W in Ws], _ptr(w1), _ptr(w2), eps, _ptr(x0), _ptr(h), _ptr(out["qkv"]),
+        _ptr(out["u"]), _ptr(out["d"]), _ptr(out["logits"]), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def prefill_frame_q8_workspace_bytes(hidden: int, qkv_rows: int, inter: int, vocab: int, n: int) -> int:
+    return lib().prefill_frame_q8_workspace_bytes(hidden, qkv_rows, inter, vocab, n)
+
+
+def prefill_frame_q8(qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight, w1: torch.Tensor,
+                     w2: torch.Tensor, eps: float, X0: torch.Tensor, H: torch.Tensor, out: dict,
+                     workspace: torch.Tensor, stream=None) -> dict:
+    """The q8 layer frame over one prefill pass of n <= 64 positions: H [n][hidden] is
+    updated in place and out = {qkv, u, d, logits} ([n][...] f32) receives the products."""
+    Ws = [_q8struct(W, nm) for W, nm in ((qkv, "qkv"), (up, "up"), (down, "down"), (head, "head"))]
+    for t, nm in ((w1, "w1"), (w2, "w2"), (X0, "X0"), (H, "H")):
+        _dev(t, torch.float32, nm)
+    n, hidden = X0.shape
+    if H.shape != X0.shape or hidden != qkv.cols or w1.numel() != hidden or w2.numel() != hidden:
+        raise ValueError("X0 and H must be [n][qkv.cols]; w1, w2 [qkv.cols]")
+    for k, cols in (("qkv", qkv.rows), ("u", up.rows), ("d", hidden), ("logits", head.rows)):
+        _dev(out[k], torch.float32, k)
+        if tuple(out[k].shape) != (n, cols):
+            raise ValueError(f"out[{k!r}] must be [{n}][{cols}]")
+    _dev(workspace, torch.uint8, "workspace")
+    _check("prefill_frame_q8", lib().prefill_frame_q8(
+        *[ctypes.byref(W) for W in Ws], _ptr(w1), _ptr(w2), eps, _ptr(X0), _ptr(H), n, _ptr(out["qkv"]),
         _ptr(out["u"]), _ptr(out["d"]), _ptr(out["logits"]), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

@@ -50,6 +50,20 @@
 
 namespace pg {
 
+// What the finished panel tile y[m][r] (positions m < n, the panel's rows)
+// becomes (DenseArgs::mode):
+//  kDensePlain   out[m][r] = act(y)
+//  kDenseResid   out[m][r] = y; for r < hidden: h' = H[m][r] + y is written
+//                back to H, w[r] * h' is staged as column r of the next
+//                product's activations, and sumsq[panel][m] = the sum of h'^2
+//                over the panel's rows (its part of the next RMSNorm)
+//  kDenseScaled  v = act(y / sqrt(sum_p sumsq_in[p][m] / hidden + eps)) (p in
+//                order); out[m][r] = v, staged as column r of the next
+//                product's activations when nxp is set
+// so that an add + RMSNorm between two products runs in the first one's
+// epilogue and the second one's scaling, with no pass of its own.
+enum DenseMode { kDensePlain = 0, kDenseResid = 1, kDenseScaled = 2 };
+
 struct DenseArgs {
     const int8_t *q;
     const float *scale;
@@ -62,7 +76,60 @@ struct DenseArgs {
     float *out;       // out[m * ldo + r]
     long long ldo;
     int act;
+    // K splits: split s of panel p writes its partial tile [m][128] to
+    // parts + ((s * n + m) * panels + p) * 128; the last split of the panel to
+    // arrive (tickets[p], zeroed before the launch) adds them in split order
+    // and runs the epilogue.
+    int splits;
+    int split;  // this workgroup's split
+    float *parts;
+    unsigned *tickets;
+    // epilogue
+    int mode;
+    float *H;               // kDenseResid: residual [n][hidden], updated in place
+    const float *w;         // kDenseResid: norm weight [hidden]
+    int hidden;             // columns of the residual / of the RMSNorm
+    float *sumsq;           // kDenseResid: [ceil(hidden / 128)][n] written
+    const float *sumsq_in;  // kDenseScaled: [ceil(hidden / 128)][n] read
+    float eps;
+    u32x4 *nxp;             // next product's staged fragments (NULL: none)
+    __bf16 *nxs;            // next product's staged block sums
+    int nnb;                // next product's blocks (its cols / 32)
 };
+
+// Fragment-layout record of one half block (16 columns, half h of block blk)
+// of A row m: the hi/lo bf16 pair of each value, and (h == 0 lane) the
+// block's sum.  Lanes 2i and 2i + 1 hold the two halves of one block.
+__device__ __forceinline__ void put_frag_half(const float v[16], int m, int blk, int h, int nb, int mts,
+                                              u32x4 *__restrict__ xp, __bf16 *__restrict__ xs) {
+    const int mt = m >> 5, lane = (m & 31) + 32 * h;
+    __bf16 hi[16], lo[16];
+    float half_sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        hi[i] = to_bf16(v[i]);
+        lo[i] = to_bf16(v[i] - (float)hi[i]);
+        half_sum += v[i];
+    }
+    if (blk < nb) {
+        u32x4 rec[4];
+        __builtin_memcpy(&rec[0], &hi[0], 16);
+        __builtin_memcpy(&rec[1], &hi[8], 16);
+        __builtin_memcpy(&rec[2], &lo[0], 16);
+        __builtin_memcpy(&rec[3], &lo[8], 16);
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) xp[(((long long)blk * mts + mt) * 4 + fi) * 64 + lane] = rec[fi];
+    }
+    const float block_sum = half_sum + __shfl_xor(half_sum, 1, kWave);
+    if (h == 0) {
+        const __bf16 s_hi = to_bf16(block_sum);
+        const __bf16 s_lo = to_bf16(block_sum - (float)s_hi);
+        const int g = blk >> 4, hh = (blk >> 3) & 1, i = blk & 7;
+        const int sl = (m & 31) + 32 * hh;
+        xs[((((long long)g * mts + mt) * 2 + 0) * 64 + sl) * 8 + i] = s_hi;
+        xs[((((long long)g * mts + mt) * 2 + 1) * 64 + sl) * 8 + i] = s_lo;
+    }
+}
 
 template <int MT, int NK, int NX, int NW>
 struct DenseCfg {
@@ -90,7 +157,9 @@ struct DenseCfg {
     static constexpr int kSPer = 8 / kWaves;             // scale copies (16 rows each)
     static constexpr int kBPer = 32 / kWaves / 4;        // bias copies (4 rows x 16) per wave per stage
     static_assert(NK == 4, "K waves per row half: one block per wave per stage");
-    static_assert(kRedU4 <= kLdsU4, "the partial sums fit the ring");
+    static constexpr int kTileU4 = 64 * 128 / 4;          // the finished panel tile [m][128] f32
+    static constexpr int kTileBase = kRedU4;
+    static_assert(kRedU4 + kTileU4 + 17 <= kLdsU4, "the partial sums, the tile and its scalars fit the ring");
     static_assert(kLdsU4 * 16 <= 160 * 1024, "LDS of one compute unit");
     // Copies one wave issues per stage, and the memory-counter wait that
     // leaves in flight only the copies issued after stage c + 1's activations.
@@ -146,6 +215,172 @@ __device__ __forceinline__ int wq_slot(int row, int s) {
     return i * 64 + 8 * (r8 ^ (i & 1)) + (s ^ r8);
 }
 
+// The panel's finished tile and its epilogue (DenseArgs::mode).  With K
+// splits, every split has written its partial tile; the last to arrive adds
+// them in split order into LDS, the others leave.  Then thread t takes
+// position m = t / 8 and the 16 rows 16 (t % 8) .. of the panel (threads 2i,
+// 2i + 1 hold the two halves of one 32-row block of the next product's
+// columns).
+template <int MT, int NK, int NX, int NW>
+__device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_base, u32x4 *lds) {
+    using C = DenseCfg<MT, NK, NX, NW>;
+    static_assert(C::kThreads == 512, "one thread per (position, 16 rows) of a 64 x 128 tile");
+    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);
+    float *s_inv = reinterpret_cast<float *>(lds + C::kTileBase + C::kTileU4);  // [64]
+    unsigned &s_ticket = *reinterpret_cast<unsigned *>(lds + C::kTileBase + C::kTileU4 + 16);
+    const int t = threadIdx.x;
+    const int panel = r_base / C::kRows;
+    const int prow = min(C::kRows, P.rows - r_base);  // rows of this panel
+    if (P.splits > 1) {
+        // This split's tile goes out as 16-byte chunks (chunk c: position
+        // c / 32, rows 4 (c % 32) ..), written at device scope so that the
+        // panel's last split reads them from another compute unit.
+        __syncthreads();  // the tile is complete
+        const int panels = (P.rows + C::kRows - 1) / C::kRows;
+        const int chunks = P.n * 32;
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            P.parts, (short)0, P.splits * P.n * panels * C::kRows * 4, 0x00020000);
+        auto chunk_off = [&](int sp, int c) __attribute__((always_inline)) {
+            return (((sp * P.n + (c >> 5)) * panels + panel) * C::kRows + 4 * (c & 31)) * 4;
+        };
+        constexpr int kC = 64 * 32 / C::kThreads;  // chunks per thread (n <= 64)
+        constexpr int kDev = 16;                    // buffer cache policy: device scope
+#pragma unroll
+        for (int k = 0; k < kC; ++k) {
+            const int c = t + k * C::kThreads;
+            if (c < chunks)
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4 *>(tile + 4 * c), rp,
+                                                       chunk_off(P.split, c), 0, kDev);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this split's partial has landed
+        __syncthreads();
+        if (t == 0) s_ticket = __hip_atomic_fetch_add(P.tickets + panel, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_ticket != (unsigned)P.splits - 1) return;
+        // Last split: y = sum_s parts[s] in split order, the loads of four
+        // splits in flight at a time.
+        constexpr int kS = 4;
+        float4 y[kC];
+#pragma unroll
+        for (int k = 0; k < kC; ++k) y[k] = make_float4(0, 0, 0, 0);
+        for (int s0 = 0; s0 < P.splits; s0 += kS) {
+            u32x4 v[kS][kC];
+#pragma unroll
+            for (int si = 0; si < kS; ++si)
+#pragma unroll
+                for (int k = 0; k < kC; ++k) {
+                    const int c = t + k * C::kThreads;
+                    v[si][k] = (s0 + si < P.splits && c < chunks)
+                                   ? __builtin_amdgcn_raw_buffer_load_b128(rp, chunk_off(s0 + si, c), 0, kDev)
+                                   : u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+            for (int si = 0; si < kS; ++si)
+#pragma unroll
+                for (int k = 0; k < kC; ++k) {
+                    if (s0 + si >= P.splits) continue;
+                    const float4 a = __builtin_bit_cast(float4, v[si][k]);
+                    if (s0 + si == 0) {
+                        y[k] = a;
+                    } else {
+                        y[k].x += a.x; y[k].y += a.y; y[k].z += a.z; y[k].w += a.w;
+                    }
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < kC; ++k) {
+            const int c = t + k * C::kThreads;
+            if (c < chunks) *reinterpret_cast<float4 *>(tile + 4 * c) = y[k];
+        }
+    }
+    if (P.mode == kDenseScaled && t < 64) {
+        // The panels' sums in panel order, the loads of 16 panels in flight.
+        float ss = 0.0f;
+        const int np = (P.hidden + C::kRows - 1) / C::kRows;
+        const int m = min(t, P.n - 1);
+        for (int p0 = 0; p0 < np; p0 += 16) {
+            float v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = p0 + k < np ? P.sumsq_in[(p0 + k) * P.n + m] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ss += v[k];
+        }
+        s_inv[t] = rsqrtf(ss / (float)P.hidden + P.eps);
+    }
+    __syncthreads();
+
+    const int m = t >> 3, j = (t >> 1) & 3, hh = t & 1;
+    if (m >= P.mts * 32) return;
+    const int rl0 = 32 * j + 16 * hh, r0 = r_base + rl0;
+    // Rows of this item inside the matrix (the last panel may end inside an
+    // item; rows past the end hold zeros).
+    const int cnt = m < P.n ? max(0, min(16, prow - rl0)) : 0;
+    const bool live = cnt > 0;
+    float v[16];
+    if (live) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 a = *reinterpret_cast<const float4 *>(tile + m * 128 + rl0 + 4 * q4);
+            v[4 * q4] = a.x; v[4 * q4 + 1] = a.y; v[4 * q4 + 2] = a.z; v[4 * q4 + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    float *o = P.out + (long long)m * P.ldo + r0;
+    auto store16 = [&](const float (&x)[16]) __attribute__((always_inline)) {
+        if (cnt == 16 && (P.ldo & 3) == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                *reinterpret_cast<float4 *>(o + 4 * q4) = make_float4(x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (i < cnt) o[i] = x[i];
+        }
+    };
+    if (P.mode == kDensePlain) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = apply_act(P.act, v[i]);
+        store16(v);
+        return;
+    }
+    if (P.mode == kDenseScaled) {
+        const float inv = s_inv[m];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = i < cnt ? apply_act(P.act, inv * v[i]) : 0.0f;
+        store16(v);
+        if (P.nxp && r0 < 16 * ((P.nnb + 15) / 16) * 32)
+            put_frag_half(v, m, r0 >> 5, hh, P.nnb, P.mts, P.nxp, P.nxs);
+        return;
+    }
+    // kDenseResid (hidden % 32 == 0: an item below hidden is whole)
+    store16(v);
+    float sq = 0.0f;
+    if (r0 < P.hidden) {
+        float x[16];
+        float *hp = P.H + (long long)m * P.hidden + r0;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            float4 a = make_float4(0, 0, 0, 0), g = make_float4(0, 0, 0, 0);
+            if (live) {
+                a = *reinterpret_cast<const float4 *>(hp + 4 * q4);
+                g = *reinterpret_cast<const float4 *>(P.w + r0 + 4 * q4);
+                a.x += v[4 * q4]; a.y += v[4 * q4 + 1]; a.z += v[4 * q4 + 2]; a.w += v[4 * q4 + 3];
+                *reinterpret_cast<float4 *>(hp + 4 * q4) = a;
+            }
+            sq += (a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w);
+            x[4 * q4] = g.x * a.x; x[4 * q4 + 1] = g.y * a.y; x[4 * q4 + 2] = g.z * a.z; x[4 * q4 + 3] = g.w * a.w;
+        }
+        put_frag_half(x, m, r0 >> 5, hh, P.nnb, P.mts, P.nxp, P.nxs);
+    }
+    // The eight threads of position m, in a fixed butterfly.
+    sq += __shfl_xor(sq, 1, kWave);
+    sq += __shfl_xor(sq, 2, kWave);
+    sq += __shfl_xor(sq, 4, kWave);
+    if ((t & 7) == 0 && r_base < P.hidden && m < P.n) P.sumsq[panel * P.n + m] = sq;
+}
+
 template <int MT, int NK, int NX, int NW>
 __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base, const int kb0,
                                             const int kb1, u32x4 *lds) {
@@ -161,11 +396,19 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // Per-lane buffer offsets at stage 0; a stage adds a wave-uniform step.
     // Reads past a row's blocks (the tail stage of a range) fetch valid bytes
     // that are weighted by zero; reads past a buffer's end return zero.
+    // Copies for stages past the range go through empty resources: they
+    // return zeros at once and move no memory.
     const i32x4 rq = buf_rsrc(P.q, (uint32_t)P.rows * (uint32_t)P.cols);
     const i32x4 rs = buf_rsrc(P.scale, (uint32_t)P.rows * nb * 4u);
     const i32x4 rb = buf_rsrc(P.bias, (uint32_t)P.rows * nb * 4u);
     const i32x4 rx = buf_rsrc(P.xp, (uint32_t)nb * P.mts * 4096u);
     const i32x4 rxs = buf_rsrc(P.xs, (uint32_t)ng * P.mts * 2048u);
+    auto live_rsrc = [](i32x4 r, bool live) __attribute__((always_inline)) {
+#ifndef PG_DENSE_NOSKIP
+        r[2] = live ? r[2] : 0;
+#endif
+        return r;
+    };
     // LDS byte address of slot i (16 bytes) of the ring.
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) u32x4 *)lds;
     auto laddr = [&](int slot) __attribute__((always_inline)) { return lbase + 16u * (uint32_t)slot; };
@@ -191,14 +434,15 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     auto copy_x = [&](int c) __attribute__((always_inline)) {
         const int xslot = C::kXBase + (c % NX) * C::kXStage;
         const uint32_t step = (uint32_t)(c * KB * P.mts) * 4096u;
+        const i32x4 rxc = live_rsrc(rx, c < nst), rxsc = live_rsrc(rxs, c < nst);
 #pragma unroll
         for (int f = 0; f < C::kXPer; ++f) {
             const int g = w * C::kXPer + f;
             const uint32_t src = (uint32_t)((g / (4 * MT)) * P.mts * 4 + g % (4 * MT)) * 1024u;
-            lds_copy<16>(rx, ox + step + src, laddr(xslot + g * 64));
+            lds_copy<16>(rxc, ox + step + src, laddr(xslot + g * 64));
         }
         const int it = c / C::kStagesPerGroup;
-        lds_copy<16>(rxs, oxs + (uint32_t)(it * P.mts) * 2048u, laddr(C::kSBase + (it & 1) * C::kSGroup + fs * 64));
+        lds_copy<16>(rxsc, oxs + (uint32_t)(it * P.mts) * 2048u, laddr(C::kSBase + (it & 1) * C::kSGroup + fs * 64));
     };
     // Weights and scales of stage c for this wave's rows, into W slot c % NW
     // (layout: q pieces by wq_slot, then [row][4] scales), and this wave's
@@ -207,17 +451,18 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     const uint32_t ob = ((uint32_t)(r_base + (lane >> 4)) * (uint32_t)nb + (uint32_t)(kb0 + 16 + (lane & 15))) * 4u;
     auto copy_b = [&](int it, int p) __attribute__((always_inline)) {
         // rows 4p .. 4p + 3 of group it
-        lds_copy<4>(rb, ob + (uint32_t)(4 * p) * (uint32_t)nb * 4u + (uint32_t)(16 * (it - 1)) * 4u,
+        lds_copy<4>(live_rsrc(rb, it * C::kStagesPerGroup < nst), ob + (uint32_t)(4 * p) * (uint32_t)nb * 4u + (uint32_t)(16 * (it - 1)) * 4u,
                     laddr(C::kBBase + (it & 1) * C::kBGroup + p * 16));
     };
     auto copy_w = [&](int c) __attribute__((always_inline)) {
         const int wslot = C::kWBase + (c % NW) * C::kWStage;
         const uint32_t sq = (uint32_t)(c * KB) * 32u, ss = (uint32_t)(c * KB) * 4u;
+        const i32x4 rqc = live_rsrc(rq, c < nst), rsc = live_rsrc(rs, c < nst);
 #pragma unroll
-        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, PG_DENSE_WNT>(rq, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
+        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, PG_DENSE_WNT>(rqc, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
 #pragma unroll
         for (int k = 0; k < C::kSPer; ++k)
-            lds_copy<4>(rs, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
+            lds_copy<4>(rsc, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
     };
 
     // Prologue: W(0), X(0), X(1 .. NX - 2), W(1 .. NW - 2).
@@ -374,29 +619,36 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
                 for (int v = 0; v < 16; ++v) red[red_at(kq, rt, mt, v)] = acc[rt][mt][v];
     }
     __syncthreads();
-    if (kq > 0) return;
-    // Tile by tile: add the other K waves' partials (in order), then store.
-    // Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h + (v % 4), row r.
+    // Tile by tile on the kq == 0 waves: add the other K waves' partials (in
+    // order).  Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h
+    // + (v % 4), row 64 rh + 32 rt + ml of the panel.
+    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);  // [m][128]
+    const bool direct = P.splits == 1 && P.mode == kDensePlain;
+    if (kq == 0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int r = r_base + 64 * rh + 32 * rt + ml;
+        for (int rt = 0; rt < 2; ++rt) {
+            const int rl = 64 * rh + 32 * rt + ml, r = r_base + rl;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            f32x16 t = acc[rt][mt];
+            for (int mt = 0; mt < MT; ++mt) {
+                f32x16 t = acc[rt][mt];
 #pragma unroll
-            for (int k = 1; k < NK; ++k)
+                for (int k = 1; k < NK; ++k)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) t[v] += red[red_at(k, rt, mt, v)];
-            if (r < P.rows) {
-                float *o = P.out + r;
+                    for (int v = 0; v < 16; ++v) t[v] += red[red_at(k, rt, mt, v)];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (m < P.n) o[m * P.ldo] = apply_act(P.act, t[v]);
+                    if (direct) {
+                        if (r < P.rows && m < P.n) P.out[m * P.ldo + r] = apply_act(P.act, t[v]);
+                    } else {
+                        tile[m * 128 + rl] = t[v];
+                    }
                 }
             }
         }
     }
+    if (direct) return;
+    dense_finish<MT, NK, NX, NW>(P, r_base, lds);
 }
 
 }  // namespace pg

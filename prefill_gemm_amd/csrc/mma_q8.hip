@@ -71,45 +71,18 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const float *__restrict__ 
     }
 }
 
-// Fragment-layout record of one half block (16 columns, half h of block blk)
-// of A row m: the hi/lo bf16 pair of each value, and (h == 0 lane) the
-// block's sum.  Lanes 2i and 2i + 1 hold the two halves of one block.
-__device__ __forceinline__ void put_frag_half(const float v[16], int m, int blk, int h, int nb, int mts,
-                                              u32x4 *__restrict__ xp, __bf16 *__restrict__ xs) {
-    const int mt = m >> 5, lane = (m & 31) + 32 * h;
-    __bf16 hi[16], lo[16];
-    float half_sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        hi[i] = to_bf16(v[i]);
-        lo[i] = to_bf16(v[i] - (float)hi[i]);
-        half_sum += v[i];
-    }
-    if (blk < nb) {
-        u32x4 rec[4];
-        __builtin_memcpy(&rec[0], &hi[0], 16);
-        __builtin_memcpy(&rec[1], &hi[8], 16);
-        __builtin_memcpy(&rec[2], &lo[0], 16);
-        __builtin_memcpy(&rec[3], &lo[8], 16);
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) xp[(((long long)blk * mts + mt) * 4 + fi) * 64 + lane] = rec[fi];
-    }
-    const float block_sum = half_sum + __shfl_xor(half_sum, 1, kWave);
-    if (h == 0) {
-        const __bf16 s_hi = to_bf16(block_sum);
-        const __bf16 s_lo = to_bf16(block_sum - (float)s_hi);
-        const int g = blk >> 4, hh = (blk >> 3) & 1, i = blk & 7;
-        const int sl = (m & 31) + 32 * hh;
-        xs[((((long long)g * mts + mt) * 2 + 0) * 64 + sl) * 8 + i] = s_hi;
-        xs[((((long long)g * mts + mt) * 2 + 1) * 64 + sl) * 8 + i] = s_lo;
-    }
-}
-
 // Fragment layout for the dense pass (see mma_q8.h): one thread per (row m,
 // 16-column half block) over mts * 32 rows (rows >= n are zero) and 16 * ng blocks.
+// The staging launch also clears zero[0 .. nzero) (split tickets and block
+// sums of the launches that follow), grid-stride.
+__device__ __forceinline__ void clear_words(unsigned *zero, int nzero) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nzero; i += gridDim.x * blockDim.x) zero[i] = 0u;
+}
+
 __global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
                                                            int cols, int mts, u32x4 *__restrict__ xp,
-                                                           __bf16 *__restrict__ xs) {
+                                                           __bf16 *__restrict__ xs, unsigned *zero, int nzero) {
+    clear_words(zero, nzero);
     const int nb = cols >> 5;
     const int ng = (nb + 15) >> 4;
     const int per_row = ng * 32;
@@ -144,8 +117,9 @@ constexpr int kStageNormIter = 4;  // cols <= 4 * 256 * 16 = 16384
 __global__ __launch_bounds__(256) void stage_norm_frag_kernel(
     const float *__restrict__ H, const float *__restrict__ delta, int dstride, const float *__restrict__ w,
     float eps, int n, int cols, int mts, float *__restrict__ H_out, float *__restrict__ X_out,
-    u32x4 *__restrict__ xp, __bf16 *__restrict__ xs) {
+    u32x4 *__restrict__ xp, __bf16 *__restrict__ xs, unsigned *zero, int nzero) {
     __shared__ float red[4];
+    clear_words(zero, nzero);
     const int nb = cols >> 5;
     const int ng = (nb + 15) >> 4;
     const int per_row = ng * 32;
@@ -225,41 +199,25 @@ template <int MT>
 using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
 
 template <int MT>
-__global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int splits, int bps,
-                                                                   float *partials, long long plane) {
+__global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int bps) {
     extern __shared__ u32x4 dlds[];
     const int id = blockIdx.x;
-    const int split = id % splits, panel = id / splits;
+    const int split = id % P.splits, panel = id / P.splits;
     const int nb = P.cols >> 5;
     const int kb0 = split * bps;
     const int kb1 = min(nb, kb0 + bps);
-    if (splits > 1) {
-        P.out = partials + (long long)split * plane;
-        P.act = 0;
-    }
+    P.split = split;
     dense_panel<MT, kDNK, kDNX, kDNW>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
 }
 
 template <int MT>
-static int launch_dense(const DenseArgs &P, int grid, int splits, int bps, float *parts, long long plane,
-                        hipStream_t s) {
+static int launch_dense(const DenseArgs &P, int grid, int bps, hipStream_t s) {
     constexpr size_t lds = (size_t)DCfg<MT>::kLdsU4 * sizeof(u32x4);
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL(dense_kernel<MT>, dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, splits, bps, parts, plane);
+    hipLaunchKernelGGL(dense_kernel<MT>, dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
     return launch_status();
-}
-
-// Y[i] = act( sum_{s < splits} parts[s][i] ), the splits added in order.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ parts,
-                                                            int splits, long long plane,
-                                                            float *__restrict__ Y, int act) {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= plane) return;
-    float acc = parts[i];
-    for (int s = 1; s < splits; ++s) acc += parts[(long long)s * plane + i];
-    Y[i] = apply_act(act, acc);
 }
 
 // Grouped expert bank: workgroup (panel of 128 rows, expert e).  An expert no
@@ -315,13 +273,29 @@ static size_t frag_x_bytes(int n, int cols) { return (size_t)ceil_div(n, 32) * c
 static size_t frag_s_bytes(int n, int cols) {
     return (size_t)ceil_div(n, 32) * ceil_div(cols / 32, 16) * 2048;
 }
+static int dense_panels(int rows) { return ceil_div(rows, DCfg<2>::kRows); }
+static size_t parts_bytes(int rows, int cols, int n) {
+    const int s = dense_splits(rows, cols);
+    return s > 1 ? (size_t)s * n * ceil_div(rows, DCfg<2>::kRows) * DCfg<2>::kRows * sizeof(float) : 0;
+}
+
+// Workspace of one product: staged fragments, block sums, split tickets,
+// split partials.
+struct OneLayout {
+    size_t xs, tickets, parts, total;
+};
+static OneLayout one_layout(int rows, int cols, int n) {
+    OneLayout L;
+    L.xs = round_up(frag_x_bytes(n, cols), 256);
+    L.tickets = L.xs + round_up(frag_s_bytes(n, cols), 256);
+    L.parts = L.tickets + round_up((size_t)dense_panels(rows) * 4, 256);
+    L.total = L.parts + parts_bytes(rows, cols, n);
+    return L;
+}
 
 extern "C" size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n) {
     if (rows <= 0 || cols <= 0 || n <= 0 || cols % 32) return 0;
-    size_t bytes = round_up(frag_x_bytes(n, cols), 256) + round_up(frag_s_bytes(n, cols), 256);
-    const int s = dense_splits(rows, cols);
-    if (s > 1) bytes += (size_t)s * n * rows * sizeof(float);
-    return bytes;
+    return one_layout(rows, cols, n).total;
 }
 
 // Residual add + RMSNorm ahead of a prefill product (stage_norm_frag_kernel).
@@ -341,57 +315,65 @@ static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
     return pa < pb + bn && pb < pa + an;
 }
 
+static int launch_stage_frag(const float *X, int n, int cols, void *xp, void *xs, unsigned *zero, int nzero,
+                             hipStream_t s) {
+    const int mts = ceil_div(n, 32);
+    const int nb = cols / 32, ng = (nb + 15) / 16;
+    const long long threads = (long long)mts * 32 * ng * 32;
+    hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, X, n, cols,
+                       mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), zero, nzero);
+    return launch_status();
+}
+
+// The dense pass over one product whose activations are staged at (xp, xs);
+// the epilogue fields of P are the caller's.  Split partials and tickets at
+// (parts, tickets); the tickets must be zero.
+static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, unsigned *tickets, hipStream_t s) {
+    P.xp = reinterpret_cast<const u32x4 *>(xp);
+    P.xs = reinterpret_cast<const u32x4 *>(xs);
+    P.mts = ceil_div(P.n, 32);
+    const int nb = P.cols / 32;
+    const int bps = dense_blocks_per_split(P.rows, P.cols);
+    P.splits = ceil_div(nb, bps);  // splits that hold at least one block
+    P.parts = parts;
+    P.tickets = tickets;
+    const int grid = dense_panels(P.rows) * P.splits;
+    return P.mts == 2 ? launch_dense<2>(P, grid, bps, s) : launch_dense<1>(P, grid, bps, s);
+}
+
 // Staging (plain or normed) into the workspace, then the dense matrix-core pass
-// [+ the ordered split-K reduction].  Arguments are checked by the callers.
+// (split partials added in order inside it).  Arguments are checked by the callers.
 static int prefill_run(const int8_t *q, const float *scale, const float *bias, int rows, int cols,
                        const float *X, const StageNorm *nm, int n, float *Y, int act, void *workspace,
                        hipStream_t s) {
     char *ws = static_cast<char *>(workspace);
-    void *xp = ws;
-    void *xs = ws + round_up(frag_x_bytes(n, cols), 256);
-    float *parts = reinterpret_cast<float *>(ws + round_up(frag_x_bytes(n, cols), 256) +
-                                             round_up(frag_s_bytes(n, cols), 256));
+    const OneLayout L = one_layout(rows, cols, n);
+    void *xp = ws, *xs = ws + L.xs;
+    unsigned *tickets = reinterpret_cast<unsigned *>(ws + L.tickets);
     const int mts = ceil_div(n, 32);
+    int rc;
     if (nm) {
         hipLaunchKernelGGL(stage_norm_frag_kernel, dim3(mts * 32), dim3(256), 0, s, nm->H, nm->delta,
                            nm->dstride, nm->w, nm->eps, n, cols, mts, nm->H_out, nm->X_out,
-                           reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs));
+                           reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), tickets, dense_panels(rows));
+        rc = launch_status();
     } else {
-        const int nb = cols / 32, ng = (nb + 15) / 16;
-        const long long threads = (long long)mts * 32 * ng * 32;
-        hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                           X, n, cols, mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs));
+        rc = launch_stage_frag(X, n, cols, xp, xs, tickets, dense_panels(rows), s);
     }
-    int rc = launch_status();
     if (rc) return rc;
-
     DenseArgs P{};
     P.q = q;
     P.scale = scale;
     P.bias = bias;
     P.rows = rows;
     P.cols = cols;
-    P.xp = reinterpret_cast<const u32x4 *>(xp);
-    P.xs = reinterpret_cast<const u32x4 *>(xs);
-    P.mts = mts;
     P.n = n;
     P.out = Y;
     P.ldo = rows;
     P.act = act;
-
-    const int nb = cols / 32;
-    const int bps = dense_blocks_per_split(rows, cols);
-    const int used = ceil_div(nb, bps);  // splits that hold at least one block
-    const int grid = ceil_div(rows, DCfg<2>::kRows) * used;
-    const long long plane = (long long)n * rows;
-    rc = mts == 2 ? launch_dense<2>(P, grid, used, bps, parts, plane, s)
-                  : launch_dense<1>(P, grid, used, bps, parts, plane, s);
-    if (rc || used == 1) return rc;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((plane + 255) / 256)), dim3(256), 0, s,
-                       parts, used, plane, Y, act);
-    return launch_status();
+    P.mode = kDensePlain;
+    return run_dense(P, xp, xs, reinterpret_cast<float *>(ws + L.parts), tickets, s);
 }
-
 extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias,
                                int32_t rows, int32_t cols, const float *X, int32_t n, float *Y,
                                int32_t act, void *workspace, size_t workspace_bytes,
@@ -439,4 +421,130 @@ extern "C" int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, cons
         return PG_EINVAL;
     const StageNorm nm{H, delta, delta_stride, w, eps, H_out, X_out};
     return prefill_run(q, scale, bias, rows, cols, nullptr, &nm, n, Y, act, workspace, as_stream(stream));
+}
+
+// ---------------------------------------------------------------- prefill frame
+// The four products of the layer frame over one pass of n positions, five
+// launches: the x0 staging, then QKV, up, down and head, each dense pass
+// finishing the add + RMSNorm work around it in its epilogue (DenseMode) and
+// staging the next product's activations there.
+namespace {
+
+struct FrameLayout {
+    size_t xp[4], xs[4];    // staged activations of the four products
+    size_t tickets[4];      // split tickets; tickets[0] .. the end of xs[3] are cleared by the first launch
+    size_t sumsq1, sumsq2;  // [ceil(H / 128)][n]
+    size_t parts, total;
+};
+
+FrameLayout frame_layout(int H, int qkv_rows, int I, int V, int n) {
+    FrameLayout L;
+    const int cols[4] = {H, H, I, H}, rows[4] = {qkv_rows, I, H, V};
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += round_up(bytes, 256);
+        return at;
+    };
+    for (int i = 0; i < 4; ++i) L.xp[i] = take(frag_x_bytes(n, cols[i]));
+    L.xs[0] = take(frag_s_bytes(n, cols[0]));
+    for (int i = 0; i < 4; ++i) L.tickets[i] = take((size_t)dense_panels(rows[i]) * 4);
+    for (int i = 1; i < 4; ++i) L.xs[i] = take(frag_s_bytes(n, cols[i]));
+    const int hp = ceil_div(H, 128);
+    L.sumsq1 = take((size_t)hp * n * 4);
+    L.sumsq2 = take((size_t)hp * n * 4);
+    size_t pb = 0;
+    for (int i = 0; i < 4; ++i) pb = std::max(pb, parts_bytes(rows[i], cols[i], n));
+    L.parts = take(pb);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+extern "C" size_t prefill_frame_q8_workspace_bytes(int32_t hidden, int32_t qkv_rows, int32_t inter, int32_t vocab,
+                                                   int32_t n) {
+    if (hidden <= 0 || qkv_rows <= 0 || inter <= 0 || vocab <= 0 || n <= 0 || n > 64) return 0;
+    if (hidden % 32 || inter % 32) return 0;
+    return frame_layout(hidden, qkv_rows, inter, vocab, n).total;
+}
+
+extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                                const float *w1, const float *w2, float eps, const float *X0, float *H, int32_t n,
+                                float *qkv, float *u, float *d, float *logits, void *workspace,
+                                size_t workspace_bytes, pg_stream_t stream) {
+    if (!qkv_w || !up_w || !down_w || !head_w || !w1 || !w2 || !X0 || !H || !qkv || !u || !d || !logits)
+        return PG_EINVAL;
+    if (!(eps >= 0.0f) || n <= 0) return PG_EINVAL;
+    const pg_q8 *Ws[4] = {qkv_w, up_w, down_w, head_w};
+    for (const pg_q8 *W : Ws) {
+        if (!W->q || !W->scale || !W->bias || W->rows <= 0 || W->cols <= 0) return PG_EINVAL;
+        if (!aligned16(W->q) || !aligned16(W->scale) || !aligned16(W->bias)) return PG_EINVAL;
+        if (W->cols % 32) return PG_EUNSUPPORTED;
+    }
+    const int Hd = qkv_w->cols, I = up_w->rows;
+    if (qkv_w->rows < Hd || up_w->cols != Hd || down_w->cols != I || down_w->rows != Hd || head_w->cols != Hd)
+        return PG_EINVAL;
+    if (n > 64) return PG_EUNSUPPORTED;
+    const float *ptrs[] = {w1, w2, X0, H, qkv, u, d, logits};
+    for (const float *p : ptrs)
+        if (!aligned16(p)) return PG_EINVAL;
+    const FrameLayout L = frame_layout(Hd, qkv_w->rows, I, head_w->rows, n);
+    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return PG_EWORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    hipStream_t s = as_stream(stream);
+    auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
+    auto tick = [&](int i) { return reinterpret_cast<unsigned *>(ws + L.tickets[i]); };
+    const int nzero = (int)((L.xs[3] + round_up(frag_s_bytes(n, Hd), 256) - L.tickets[0]) / 4);
+    int rc = launch_stage_frag(X0, n, Hd, at(L.xp[0]), at(L.xs[0]), tick(0), nzero, s);
+    if (rc) return rc;
+    float *parts = reinterpret_cast<float *>(ws + L.parts);
+    float *ss1 = reinterpret_cast<float *>(ws + L.sumsq1), *ss2 = reinterpret_cast<float *>(ws + L.sumsq2);
+    auto base = [&](const pg_q8 *W, float *out) {
+        DenseArgs P{};
+        P.q = W->q;
+        P.scale = W->scale;
+        P.bias = W->bias;
+        P.rows = W->rows;
+        P.cols = W->cols;
+        P.n = n;
+        P.out = out;
+        P.ldo = W->rows;
+        P.hidden = Hd;
+        P.eps = eps;
+        return P;
+    };
+    auto next = [&](DenseArgs &P, int i, int cols) {
+        P.nxp = reinterpret_cast<u32x4 *>(at(L.xp[i]));
+        P.nxs = reinterpret_cast<__bf16 *>(at(L.xs[i]));
+        P.nnb = cols / 32;
+    };
+    // QKV: h1 = h + qkv[:, :H] into H, w1 * h1 staged for up, sums of h1^2.
+    DenseArgs P = base(qkv_w, qkv);
+    P.mode = kDenseResid;
+    P.H = H;
+    P.w = w1;
+    P.sumsq = ss1;
+    next(P, 1, Hd);
+    if ((rc = run_dense(P, at(L.xp[0]), at(L.xs[0]), parts, tick(0), s))) return rc;
+    // up: u = relu^2(W (w1 * h1) / rms(h1)), staged for down.
+    P = base(up_w, u);
+    P.mode = kDenseScaled;
+    P.act = 1;
+    P.sumsq_in = ss1;
+    next(P, 2, I);
+    if ((rc = run_dense(P, at(L.xp[1]), at(L.xs[1]), parts, tick(1), s))) return rc;
+    // down: h2 = h1 + d into H, w2 * h2 staged for the head, sums of h2^2.
+    P = base(down_w, d);
+    P.mode = kDenseResid;
+    P.H = H;
+    P.w = w2;
+    P.sumsq = ss2;
+    next(P, 3, Hd);
+    if ((rc = run_dense(P, at(L.xp[2]), at(L.xs[2]), parts, tick(2), s))) return rc;
+    // head: logits = W (w2 * h2) / rms(h2).
+    P = base(head_w, logits);
+    P.mode = kDenseScaled;
+    P.sumsq_in = ss2;
+    return run_dense(P, at(L.xp[3]), at(L.xs[3]), parts, tick(3), s);
 }

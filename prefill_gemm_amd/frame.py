@@ -14,8 +14,10 @@ The two residual + norm sites run inside the products around them, so a
 frame is four product calls.  Decode: the QKV and down GEMVs add their output
 into the residual and leave w * h and partial sums of squares
 (gemv_q8_residual); the up and head GEMVs apply 1/rms to their dot products
-(gemv_q8_normed) -- four GEMV launches back to back.  Prefill: the up and head
-products stage rmsnorm(h + delta) * w themselves (prefill_gemm_q8_addnorm).  ``capture()`` records
+(gemv_q8_normed) -- four GEMV launches back to back.  Prefill: one
+prefill_frame_q8 call (five launches: the staging of x0 and the four
+matrix-core passes, each finishing the add + norm work around it in its
+epilogue).  ``capture()`` records
 the whole frame once into a HIP graph (through torch.cuda.CUDAGraph) so
 replays pay one launch for the frame (nemotron_prefill.rs builds its bind
 groups once and keeps the pass size in a device buffer for the same reason).
@@ -24,8 +26,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (Q8Weight, gemv_q8, gemv_q8_normed, gemv_q8_residual, norm_parts, prefill_gemm_q8,
-                   prefill_gemm_q8_addnorm, prefill_gemm_q8_workspace_bytes)
+from ._lib import (Q8Weight, gemv_q8, gemv_q8_normed, gemv_q8_residual, norm_parts, prefill_frame_q8,
+                   prefill_frame_q8_workspace_bytes, prefill_gemm_q8, prefill_gemm_q8_workspace_bytes)
 
 PB_MAX = 64
 
@@ -50,7 +52,8 @@ class Frame:
             for k in ("p1", "p2"):
                 self.buf[k] = torch.empty(norm_parts(self.hidden), **f32)
         if n > 1:
-            need = max(prefill_gemm_q8_workspace_bytes(w.rows, w.cols, n) for w in self.W.values())
+            need = max(max(prefill_gemm_q8_workspace_bytes(w.rows, w.cols, n) for w in self.W.values()),
+                       prefill_frame_q8_workspace_bytes(self.hidden, qkv.rows, up.rows, head.rows, n))
             self.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         self.graph = None
 
@@ -64,7 +67,8 @@ class Frame:
             prefill_gemm_q8(self.W[name], x, y, act, workspace=self.workspace)
 
     def stages(self, x0: torch.Tensor, h: torch.Tensor):
-        """The frame as its four product calls (zero-argument callables, in order)."""
+        """The frame as its library calls (zero-argument callables, in order): four
+        GEMV calls at one position, one prefill_frame_q8 call for a pass."""
         b = self.buf
         H = self.hidden
         W = self.W
@@ -77,12 +81,9 @@ class Frame:
                                              y=b["d"].view(-1), h_out=hv),
                     lambda: gemv_q8_normed(W["head"], b["xw2"], b["p2"], self.eps, y=b["logits"].view(-1))]
         ws = self.workspace
-        return [lambda: prefill_gemm_q8(W["qkv"], x0, b["qkv"], workspace=ws),
-                lambda: prefill_gemm_q8_addnorm(W["up"], h, b["qkv"][:, :H], self.w1, self.eps, Y=b["u"], act=1,
-                                                H_out=h, workspace=ws),
-                lambda: prefill_gemm_q8(W["down"], b["u"], b["d"], workspace=ws),
-                lambda: prefill_gemm_q8_addnorm(W["head"], h, b["d"], self.w2, self.eps, Y=b["logits"], H_out=h,
-                                                workspace=ws)]
+        return [lambda: prefill_frame_q8(W["qkv"], W["up"], W["down"], W["head"], self.w1, self.w2, self.eps, x0, h,
+                                         {"qkv": b["qkv"], "u": b["u"], "d": b["d"], "logits": b["logits"]},
+                                         ws)]
 
     def run(self, x0: torch.Tensor, h: torch.Tensor) -> torch.Tensor:
         """Run the frame on x0 [n][hidden]; h [n][hidden] is the residual, updated in place
