@@ -37,8 +37,15 @@
 //  - activation fragments and block sums: as staged, 1 KB per instruction.
 // A wave waits for its own copies of stage c + 1 (memory counter) before the
 // stage barrier; copies are issued in the same order every stage, so the wait
-// is one constant.  Stages past the end re-read the last block and weigh it
-// by zero, which keeps every stage one branch-free stretch.
+// is one constant.  Blocks past the range inside a stage are weighted by
+// zero, and copies for stages past the end go through empty buffer
+// resources (zeros, no memory traffic), which keeps every stage one
+// branch-free stretch.
+//
+// K splits.  When a product has too few 128-row panels to fill the device,
+// workgroups split its blocks; every split writes its partial tile and the
+// panel's last split to arrive adds all of them in split order (so the result
+// does not depend on timing) and runs the epilogue (DenseMode).
 #pragma once
 
 #include "pg_device.h"
