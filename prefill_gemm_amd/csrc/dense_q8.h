@@ -104,6 +104,15 @@ struct DenseArgs {
     int nnb;                // next product's blocks (its cols / 32)
 };
 
+// Fragment layout of the staged activations: the 64 lanes of one matrix-core
+// fragment are contiguous (one 1 KB load a fragment).
+//  xp: [blk][mt][fi = part * 2 + ks][lane = m % 32 + 32 h], 16 bytes each:
+//      part 0 = hi, 1 = lo; element i of k-step ks of half h is column
+//      32 blk + 16 h + 8 ks + i;
+//  xs: [g][mt][part][lane = m % 32 + 32 h], 16 bytes each: element i of half h
+//      is the sum of row m over block 16 g + 8 h + i (zero past the last block).
+// Rows m >= n are zero.
+//
 // Fragment-layout record of one half block (16 columns, half h of block blk)
 // of A row m: the hi/lo bf16 pair of each value, and (h == 0 lane) the
 // block's sum.  Lanes 2i and 2i + 1 hold the two halves of one block.

@@ -1,0 +1,34 @@
+// Grouped expert bank launcher (defined in expert_q8.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pg {
+
+// One bank of q8 experts [E][rows][cols] applied to the entries each expert
+// was chosen for: out[j][r] for j in lists[e][0 .. counts[e]), reading the
+// activation row x[j / src_div] (ldx floats apart).  Rows of `out` are ldo
+// floats apart; act = 1 applies relu^2.
+struct ExpertBank {
+    const int8_t *q;
+    const float *scale;
+    const float *bias;
+    int rows, cols;
+    long long q_stride;  // int8 elements from one expert to the next
+    long long s_stride;  // scale / bias elements from one expert to the next
+    const float *x;
+    long long ldx;
+    int src_div;
+    const int32_t *counts;
+    const int32_t *lists;  // [E][cap]
+    int cap;               // at most 64
+    float *out;
+    long long ldo;
+    int act;
+};
+
+// Grid (row blocks, experts); an expert with no entries returns at once.
+int launch_expert_bank(const ExpertBank &P, int experts, hipStream_t s);
+
+}  // namespace pg

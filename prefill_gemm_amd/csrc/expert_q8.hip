@@ -1,0 +1,427 @@
+// Grouped expert banks of the routed-MoE pass (moe_grouped).
+//
+// nemotron_prefill.rs, `pb_q8_bank`: one workgroup per (row block, expert); an
+// expert that no entry chose returns at once; the expert's weights are read
+// once for all of its entries.  For expert e with cnt entries m = 0 .. cnt-1
+// (lists[e][m] = entry j, ascending):
+//     out[j][r] = act( sum_c (scale[e][r][c/32] * q[e][r][c] + bias[e][r][c/32]) * x[j / src_div][c] )
+// regrouped per 32-column block as scale * (sum_c q x) + bias * (sum_c x).
+//
+// A pass of 64 positions with top-6 over 128 experts gives about three entries
+// per expert, so this is a matrix product with a very short side.  It runs on
+// the 16 x 16 x 32 bf16 matrix cores (v_mfma_f32_16x16x32_bf16), which pad the
+// entries only to 16:
+//  - B operand = weights, exact bf16 integers; a lane streams 16 bytes of one
+//    weight row per step (a step = 16 rows x 2 blocks, 1 KB a wave);
+//  - lanes l and l + 32 trade the upper 8 bytes of their load
+//    (v_permlane32_swap), so that each matrix-core product sees 32 columns of
+//    one block and the block scale can multiply its result;
+//  - A operand = the entries' activations as bf16 hi + lo (two products, exact
+//    to about 2^-17), staged once per workgroup in LDS from the f32 rows,
+//    together with the f32 block sums that the bias multiplies.
+// Each wave owns kExpTiles tiles of 16 weight rows over all columns, with
+// kExpDepth steps of weights in flight; the block scales and biases arrive a
+// window of steps at a time, spread over the four lanes of a row.  When the
+// entries' staged rows exceed the LDS budget, the columns are taken in
+// chunks, each staged between two barriers.
+#include "expert_q8.h"
+#include "pg_device.h"
+#include "pg_host.h"
+
+#ifndef PG_EXP_T
+#define PG_EXP_T 1
+#endif
+#ifndef PG_EXP_D
+#define PG_EXP_D 8
+#endif
+#ifndef PG_EXP_LDS
+#define PG_EXP_LDS (76 * 1024)
+#endif
+
+namespace pg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kExpThreads = 256;
+constexpr int kExpWaves = kExpThreads / kWave;
+constexpr int kExpTiles = PG_EXP_T;
+constexpr int kExpDepth = PG_EXP_D;
+constexpr int kExpDepth4 = 4;
+constexpr int kExpRows = kExpWaves * 16 * kExpTiles;
+constexpr int kExpLds = PG_EXP_LDS;
+constexpr int kExpMaxCnt = 64;
+
+// LDS bytes of a chunk of `kp` block pairs for cnt entries in MT tiles of 16:
+// hi and lo arrays of cnt + 1 rows (the last all zero) of 64 bytes a block
+// plus 16 bytes of padding a row, and the block sums [block][16 MT] f32.
+__host__ __device__ constexpr int exp_chunk_bytes(int kp, int cnt, int mt) {
+    return 2 * (cnt + 1) * (128 * kp + 16) + 2 * kp * 16 * mt * 4;
+}
+
+// Block pairs per chunk: the most that fit, a multiple of the ring depth D.
+__device__ __forceinline__ int exp_chunk_pairs(int cnt, int mt, int d, int np) {
+    const int per = 2 * (cnt + 1) * 128 + 2 * 16 * mt * 4;
+    int kp = (kExpLds - 32 * (cnt + 1)) / per;
+    kp -= kp % d;
+    const int need = (np + d - 1) / d * d;
+    return kp < need ? kp : need;
+}
+// Ring depths: up to 32 entries (two tiles of 16) the ring holds kExpDepth
+// steps; with four tiles, kExpDepth4.  Either way one ring of steps must fit
+// the LDS budget at the largest entry count of its case.
+static_assert(exp_chunk_bytes(kExpDepth, 32, 2) <= kExpLds, "LDS budget: two entry tiles");
+static_assert(exp_chunk_bytes(kExpDepth4, kExpMaxCnt, 4) <= kExpLds, "LDS budget: four entry tiles");
+
+#ifndef PG_EXP_NT
+#define PG_EXP_NT 0
+#endif
+constexpr int kExpNT = PG_EXP_NT;  // weight load cache policy (2: non-temporal)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t exp_rsrc(const void *p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 a, const bf16x8 b, const f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight int8 (two dwords, column order) as a bf16x8 operand; integers in
+// [-128, 127] are exact in bf16.
+__device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t w0, uint32_t w1) {
+    const uint32_t in[2] = {w0, w1};
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int v = (int)in[j];
+        p[2 * j] = pack_bf16_exact((float)(int8_t)v, (float)(int8_t)(v >> 8));
+        p[2 * j + 1] = pack_bf16_exact((float)(int8_t)(v >> 16), (float)(v >> 24));
+    }
+    bf16x8 r;
+    __builtin_memcpy(&r, p, 16);
+    return r;
+}
+
+// Stage blocks [cb0, cb0 + 2 kp) of the entries' rows (row cnt and blocks
+// past the last are zeros).  Item = (row, quarter block of 8 columns); the 4
+// quarters of a block sit on adjacent lanes, which add their sums with two
+// exchanges into the block sum.  A thread requests kStageBatch items before
+// it waits for any of them (the requests queue behind the weight stream).
+constexpr int kStageBatch = 6;
+
+template <int MT>
+__device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *list, int cnt, int cb0,
+                                          int kp, char *lds) {
+    const int nb = P.cols >> 5;
+    const int kc = 2 * kp;
+    const int pitch = 64 * kc + 16;
+    char *lo_base = lds + (cnt + 1) * pitch;
+    float *xsum = reinterpret_cast<float *>(lds + 2 * (cnt + 1) * pitch);
+    const int total = (cnt + 1) * 4 * kc;
+    for (int base = 0; base < total; base += kStageBatch * kExpThreads) {
+        float4 xa[kStageBatch][2];
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            const int it = base + k * kExpThreads + threadIdx.x;
+            const int r = it / (4 * kc);
+            const int qb = it - r * 4 * kc;
+            const int blk = cb0 + (qb >> 2);
+            xa[k][0] = xa[k][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (it < total && r < cnt && blk < nb) {
+                const long long src = list[r] / P.src_div;
+                const float4 *xp = reinterpret_cast<const float4 *>(P.x + src * P.ldx + 32 * blk + 8 * (qb & 3));
+                xa[k][0] = xp[0];
+                xa[k][1] = xp[1];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kStageBatch; ++k) {
+            // Every requested item is consumed (stores only for items in range),
+            // so no load of the batch is left pending past the staging.
+            const int it = base + k * kExpThreads + threadIdx.x;
+            const bool in = it < total;
+            const int r = it / (4 * kc);
+            const int qb = it - r * 4 * kc;
+            const int bl = qb >> 2, i = qb & 3;
+            const float v[8] = {xa[k][0].x, xa[k][0].y, xa[k][0].z, xa[k][0].w,
+                                xa[k][1].x, xa[k][1].y, xa[k][1].z, xa[k][1].w};
+            __bf16 hi[8], lo[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                hi[j] = to_bf16(v[j]);
+                lo[j] = to_bf16(v[j] - (float)hi[j]);
+            }
+            u32x4 h4, l4;
+            __builtin_memcpy(&h4, hi, 16);
+            __builtin_memcpy(&l4, lo, 16);
+            const int off = r * pitch + 64 * bl + 16 * i;
+            if (in) {
+                *reinterpret_cast<u32x4 *>(lds + off) = h4;
+                *reinterpret_cast<u32x4 *>(lo_base + off) = l4;
+            }
+            float sum = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+            sum += __shfl_xor(sum, 1, kWave);
+            sum += __shfl_xor(sum, 2, kWave);
+            if (in && i == 0 && r < 16 * MT) xsum[bl * 16 * MT + r] = sum;
+        }
+    }
+    // Block sums of the padding rows past the zero row.
+    for (int it = threadIdx.x; it < kc * 16 * MT; it += kExpThreads)
+        if (it % (16 * MT) > cnt) xsum[it] = 0.0f;
+}
+
+// Tiles [tg T, tg T + T) of this wave's kExpTiles, all columns.  AL is the
+// widest scale / bias load (in floats: 4, 2 or 1) that the block count and
+// the vectors' alignment allow.
+template <int MT, int T, int D, int AL>
+__device__ __forceinline__ void exp_pass(const ExpertBank &P, int e, int cnt, int tg, char *lds) {
+    constexpr int V = D / 2;                   // blocks of a window per lane group
+    constexpr int LW = AL < V ? AL : V;        // floats per scale / bias load
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15, g = lane >> 4;
+    const int nb = P.cols >> 5;
+    const int np = (nb + 1) >> 1;
+    const int nwin = (np + D - 1) / D;
+    const int32_t *list = P.lists + (long long)e * P.cap;
+    const int kp = exp_chunk_pairs(cnt, MT, D, np);
+    const int pitch = 128 * kp + 16;
+    const int lo_off = (cnt + 1) * pitch;
+    const int xs_off = 2 * (cnt + 1) * pitch;
+
+    // Weights, scales and biases go through buffer resources: a step past the
+    // last takes an empty resource (zeros, no memory traffic), so that every
+    // step issues the same loads and the memory counter waits stay constant;
+    // the reads of the missing second block of an odd block count (and of the
+    // blocks past the last in a window) land in the next row or return zeros
+    // past the end, and meet zero activations.
+    const int8_t *qe = P.q + (long long)e * P.q_stride;
+    const float *se = P.scale + (long long)e * P.s_stride;
+    const float *be = P.bias + (long long)e * P.s_stride;
+    const int q_bytes = P.rows * P.cols;
+    const int s_bytes = P.rows * nb * 4;
+    const int row0 = blockIdx.x * kExpRows + wave * 16 * kExpTiles + 16 * T * tg;
+    int vq[T], vs[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int r = min(row0 + 16 * t + i16, P.rows - 1);
+        vq[t] = r * P.cols + 16 * g;
+        vs[t] = (r * nb + V * g) * 4;
+    }
+
+    // Weight ring: step p (blocks 2p, 2p + 1) in slot p % D.
+    u32x4 wq[D][T];
+    auto load = [&](int p, u32x4 (&w)[T]) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rq = exp_rsrc(qe, p < np ? q_bytes : 0);
+#pragma unroll
+        for (int t = 0; t < T; ++t) w[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq[t], 64 * p, kExpNT);
+    };
+    // Scales and biases come a window of D steps (2D blocks) at a time: lane
+    // group g holds blocks V g .. V g + V - 1 of the window for its row, and
+    // a step takes its two blocks from the group that holds them (a lane
+    // permute), so that the four lanes of a row do not each load them.
+    float sw[T][V], bw[T][V], swn[T][V], bwn[T][V];
+    auto load_win = [&](int w) __attribute__((always_inline)) {
+        const bool live = w < nwin;
+        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(se, live ? s_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rb = exp_rsrc(be, live ? s_bytes : 0);
+        const int off = 8 * D * w;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int j = 0; j < V; j += LW) {
+                if (LW == 4) {
+                    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vs[t], off + 4 * j, 0));
+                    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vs[t], off + 4 * j, 0));
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        swn[t][j + k] = a[k];
+                        bwn[t][j + k] = b[k];
+                    }
+                } else if (LW == 2) {
+                    const f32x2 a = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vs[t], off + 4 * j, 0));
+                    const f32x2 b = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, vs[t], off + 4 * j, 0));
+                    swn[t][j] = a[0];
+                    swn[t][j + 1] = a[1];
+                    bwn[t][j] = b[0];
+                    bwn[t][j + 1] = b[1];
+                } else {
+                    swn[t][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vs[t], off + 4 * j, 0));
+                    bwn[t][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, vs[t], off + 4 * j, 0));
+                }
+            }
+    };
+
+    f32x4 acc[T][MT];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // A operand of lane (i16, g): entry 16 mt + i16 (the zero row past cnt),
+    // columns 16 (g & 1) + 8 (g >> 1) .. + 7 of the block, matching the
+    // weight columns this lane group holds after the exchange.
+    const int a_col = 2 * (16 * (g & 1) + 8 * (g >> 1));
+    int a_row[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + i16;
+        a_row[mt] = (m < cnt ? m : cnt) * pitch + a_col;
+    }
+
+    // Step u of a window: blocks 2u, 2u + 1 sit in lane group 2u / V at
+    // entries 2u % V and 2u % V + 1.
+    auto compute = [&](auto uc, int p, int cb0, const u32x4 (&w)[T]) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int gs = 2 * u / V, ev = 2 * u % V;
+        const int src = (i16 + 16 * gs) * 4;
+        f32x2 s[T], b[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            s[t].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[t][ev])));
+            s[t].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[t][ev + 1])));
+            b[t].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[t][ev])));
+            b[t].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[t][ev + 1])));
+        }
+        const int bl = 2 * p - cb0;
+        // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
+        // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
+        bf16x8 b0[T], b1[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const auto e0 = __builtin_amdgcn_permlane32_swap(w[t].x, w[t].z, false, false);
+            const auto e1 = __builtin_amdgcn_permlane32_swap(w[t].y, w[t].w, false, false);
+            b0[t] = q8_to_bf16(e0[0], e1[0]);
+            b1[t] = q8_to_bf16(e0[1], e1[1]);
+        }
+        const f32x4 z{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const char *a = lds + a_row[mt] + 64 * bl;
+            const bf16x8 ah0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(a));
+            const bf16x8 ah1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(a + 64));
+            const bf16x8 al0 = as_bf16x8(*reinterpret_cast<const u32x4 *>(a + lo_off));
+            const bf16x8 al1 = as_bf16x8(*reinterpret_cast<const u32x4 *>(a + lo_off + 64));
+            const float *xs = reinterpret_cast<const float *>(lds + xs_off) + bl * 16 * MT + 16 * mt + 4 * g;
+            const f32x4 xs0 = *reinterpret_cast<const f32x4 *>(xs);
+            const f32x4 xs1 = *reinterpret_cast<const f32x4 *>(xs + 16 * MT);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                f32x4 d0 = mfma16(ah0, b0[t], z);
+                d0 = mfma16(al0, b0[t], d0);
+                f32x4 d1 = mfma16(ah1, b1[t], z);
+                d1 = mfma16(al1, b1[t], d1);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float a = acc[t][mt][v];
+                    a = fmaf(s[t].x, d0[v], a);
+                    a = fmaf(s[t].y, d1[v], a);
+                    a = fmaf(b[t].x, xs0[v], a);
+                    a = fmaf(b[t].y, xs1[v], a);
+                    acc[t][mt][v] = a;
+                }
+            }
+        }
+    };
+
+    // Loads are issued in step order (the scheduler may not interleave them),
+    // so that the wait for step p's data is always the same count: window w + 1
+    // goes out at the start of window w, ahead of the weights of its steps.
+    load_win(0);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        load(u, wq[u]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    for (int c0 = 0; c0 < np; c0 += kp) {
+        if (c0 > 0 || tg > 0) __syncthreads();
+        exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds);
+        __syncthreads();
+        const int c1 = min(np, c0 + kp);
+        for (int p0 = c0; p0 < c1; p0 += D) {
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    sw[t][j] = swn[t][j];
+                    bw[t][j] = bwn[t][j];
+                }
+            load_win(p0 / D + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<D>([&](auto uc) __attribute__((always_inline)) {
+                constexpr int u = decltype(uc)::value;
+                const int p = p0 + u;
+                if (p < c1) compute(uc, p, 2 * c0, wq[u]);
+                load(p + D, wq[u]);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+    }
+
+    // Output element v of tile (t, mt): entry 16 mt + 4 g + v, weight row
+    // row0 + 16 t + i16.
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int r = row0 + 16 * t + i16;
+        if (r >= P.rows) continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = 16 * mt + 4 * g + v;
+                if (m < cnt) P.out[(long long)list[m] * P.ldo + r] = apply_act(P.act, acc[t][mt][v]);
+            }
+    }
+}
+
+// Entries in tiles of 16: up to two tiles take all of a wave's weight tiles
+// in one pass; four take them one at a time (each pass stages its own
+// activations), which keeps the registers within two waves per SIMD.
+template <int MT, int AL>
+__device__ __forceinline__ void exp_body(const ExpertBank &P, int e, int cnt, char *lds) {
+    if (MT <= 2) {
+        exp_pass<MT, kExpTiles, kExpDepth, AL>(P, e, cnt, 0, lds);
+    } else {
+        for (int tg = 0; tg < kExpTiles; ++tg) exp_pass<MT, 1, kExpDepth4, AL>(P, e, cnt, tg, lds);
+    }
+}
+
+template <int AL>
+__global__ __launch_bounds__(kExpThreads, 2) void expert_bank_kernel(ExpertBank P) {
+    extern __shared__ u32x4 exp_lds[];
+    const int e = blockIdx.y;
+    const int cnt = min(P.counts[e], min(P.cap, kExpMaxCnt));
+    if (cnt <= 0) return;
+    char *lds = reinterpret_cast<char *>(exp_lds);
+    if (cnt <= 16)
+        exp_body<1, AL>(P, e, cnt, lds);
+    else if (cnt <= 32)
+        exp_body<2, AL>(P, e, cnt, lds);
+    else
+        exp_body<4, AL>(P, e, cnt, lds);
+}
+
+template <int AL>
+static int launch_bank(const ExpertBank &P, int experts, hipStream_t s) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kExpLds);
+    if (attr != hipSuccess) return PG_ELAUNCH;
+    hipLaunchKernelGGL(expert_bank_kernel<AL>, dim3(ceil_div(P.rows, kExpRows), experts), dim3(kExpThreads),
+                       kExpLds, s, P);
+    return launch_status();
+}
+
+int launch_expert_bank(const ExpertBank &P, int experts, hipStream_t s) {
+    if (P.rows < 1 || P.cols < 32 || P.cols % 32 || P.cap > kExpMaxCnt) return PG_EUNSUPPORTED;
+    if ((long long)P.rows * P.cols >= (1ll << 31)) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
+    // Widest scale / bias loads: a row's blocks must start on that boundary.
+    const int nb = P.cols / 32;
+    const uintptr_t a = (uintptr_t)P.scale | (uintptr_t)P.bias;
+    if (nb % 4 == 0 && (a & 15) == 0) return launch_bank<4>(P, experts, s);
+    if (nb % 2 == 0 && (a & 7) == 0) return launch_bank<2>(P, experts, s);
+    if ((a & 3) == 0) return launch_bank<1>(P, experts, s);
+    return PG_EINVAL;
+}
+
+}  // namespace pg

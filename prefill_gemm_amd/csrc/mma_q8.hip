@@ -8,70 +8,11 @@
 #include <algorithm>
 
 #include "dense_q8.h"
-#include "mma_q8.h"
-#include "mma_launch.h"
 #include "pg_host.h"
 
 namespace pg {
 
-constexpr int kWch = 2;  // weight chunks in flight per wave
-
-// One thread per (row, 16-column half block), over rows + 1 rows (the last is
-// the zero row) and 16 * ng blocks per row (blocks past the last give zeros in xs).
-__global__ __launch_bounds__(256) void stage_x_kernel(const float *__restrict__ X, int rows,
-                                                      int cols, uint4 *__restrict__ xp,
-                                                      __bf16 *__restrict__ xs) {
-    const int nb = cols >> 5;
-    const int ng = (nb + 15) >> 4;
-    const int per_row = ng * 32;
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const int row = (int)(t / per_row);
-    const int hb = (int)(t % per_row);
-    const int blk = hb >> 1, h = hb & 1;
-    if (row > rows) return;
-    const bool live = row < rows && blk < nb;
-    float v[16];
-    if (live) {
-        const float4 *src = reinterpret_cast<const float4 *>(X + (long long)row * cols + 32 * blk + 16 * h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 a = src[j];
-            v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-    }
-    __bf16 hi[16], lo[16];
-    float half_sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        hi[i] = to_bf16(v[i]);
-        lo[i] = to_bf16(v[i] - (float)hi[i]);
-        half_sum += v[i];
-    }
-    if (blk < nb) {
-        uint4 rec[4];
-        __builtin_memcpy(&rec[0], &hi[0], 16);
-        __builtin_memcpy(&rec[1], &hi[8], 16);
-        __builtin_memcpy(&rec[2], &lo[0], 16);
-        __builtin_memcpy(&rec[3], &lo[8], 16);
-        uint4 *dst = xp + (((long long)row * nb + blk) * 2 + h) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = rec[j];
-    }
-    const float block_sum = half_sum + __shfl_xor(half_sum, 1, kWave);
-    if (h == 0) {
-        const __bf16 s_hi = to_bf16(block_sum);
-        const __bf16 s_lo = to_bf16(block_sum - (float)s_hi);
-        const int g = blk >> 4, hh = (blk >> 3) & 1, i = blk & 7;
-        __bf16 *rec = xs + (((long long)row * ng + g) * 2 + hh) * 16;
-        rec[i] = s_hi;
-        rec[8 + i] = s_lo;
-    }
-}
-
-// Fragment layout for the dense pass (see mma_q8.h): one thread per (row m,
+// Fragment layout for the dense pass (see dense_q8.h): one thread per (row m,
 // 16-column half block) over mts * 32 rows (rows >= n are zero) and 16 * ng blocks.
 // The staging launch also clears zero[0 .. nzero) (split tickets and block
 // sums of the launches that follow), grid-stride.
@@ -173,15 +114,6 @@ __global__ __launch_bounds__(256) void stage_norm_frag_kernel(
     }
 }
 
-int launch_stage_x(const float *X, int rows, int cols, void *xp, void *xs, hipStream_t s) {
-    const int nb = cols / 32, ng = (nb + 15) / 16;
-    const long long threads = (long long)(rows + 1) * ng * 32;
-    const int grid = (int)((threads + 255) / 256);
-    hipLaunchKernelGGL(stage_x_kernel, dim3(grid), dim3(256), 0, s, X, rows, cols,
-                       reinterpret_cast<uint4 *>(xp), reinterpret_cast<__bf16 *>(xs));
-    return launch_status();
-}
-
 // Dense pass: workgroup id -> (panel of 128 rows, K split).  Splits of one
 // panel take consecutive ids.  The activation ring is dynamic LDS (more than
 // the 64 KB a static array may take).
@@ -217,38 +149,6 @@ static int launch_dense(const DenseArgs &P, int grid, int bps, hipStream_t s) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return PG_ELAUNCH;
     hipLaunchKernelGGL(dense_kernel<MT>, dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
-    return launch_status();
-}
-
-// Grouped expert bank: workgroup (panel of 128 rows, expert e).  An expert no
-// position chose returns at once (nemotron_prefill.rs, `pb_q8_bank`: cnt == 0).
-__global__ __launch_bounds__(kMmaThreads) void mma_expert_kernel(MmaPanel P, const int32_t *counts,
-                                                         const int32_t *lists, int cap,
-                                                         long long q_stride, long long s_stride) {
-    __shared__ u32x4 lds[2 * kChunk * 2 * 4 * 64];
-    const int e = blockIdx.y;
-    const int cnt = min(counts[e], min(cap, 64));
-    if (cnt <= 0) return;
-    P.q += e * q_stride;
-    P.scale += e * s_stride;
-    P.bias += e * s_stride;
-    P.src_list = lists + (long long)e * cap;
-    P.out_list = lists + (long long)e * cap;
-    P.m_valid = cnt;
-    const int nb = P.cols >> 5;
-    if (cnt > 32)
-        mma_panel<2, kWch>(P, blockIdx.x * kPanelRows, 0, nb, lds);
-    else
-        mma_panel<1, kWch>(P, blockIdx.x * kPanelRows, 0, nb, lds);
-}
-
-int launch_expert_bank(const MmaPanel &P, int experts, const int32_t *counts,
-                       const int32_t *lists, int cap, hipStream_t s) {
-    const long long q_stride = (long long)P.rows * P.cols;
-    const long long s_stride = (long long)P.rows * (P.cols / 32);
-    dim3 grid(ceil_div(P.rows, kPanelRows), experts);
-    hipLaunchKernelGGL(mma_expert_kernel, grid, dim3(kMmaThreads), 0, s, P, counts, lists, cap, q_stride,
-                       s_stride);
     return launch_status();
 }
 

@@ -11,7 +11,7 @@
 // instead of once per entry.
 #include <math.h>
 
-#include "mma_launch.h"
+#include "expert_q8.h"
 #include "pg_device.h"
 #include "pg_host.h"
 
@@ -136,25 +136,16 @@ __global__ __launch_bounds__(256) void group_kernel(const int32_t *__restrict__ 
 }
 
 struct MoeLayout {
-    size_t xp_x, xs_x, u, xp_u, xs_u, d, total;
+    size_t u, d, total;
 };
 
+// Workspace: the entries' up rows U [n k][I] and down rows D [n k][H].
 static MoeLayout moe_layout(int n, int H, int I, int k) {
     MoeLayout L{};
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t at = off;
-        off += round_up(bytes, 256);
-        return at;
-    };
-    const int nk = n * k;
-    L.xp_x = take(stage_x_bytes(n, H));
-    L.xs_x = take(stage_s_bytes(n, H));
-    L.u = take((size_t)nk * I * sizeof(float));
-    L.xp_u = take(stage_x_bytes(nk, I));
-    L.xs_u = take(stage_s_bytes(nk, I));
-    L.d = take((size_t)nk * H * sizeof(float));
-    L.total = off;
+    const size_t nk = (size_t)n * k;
+    L.u = 0;
+    L.d = round_up(nk * I * sizeof(float), 256);
+    L.total = L.d + round_up(nk * H * sizeof(float), 256);
     return L;
 }
 
@@ -195,11 +186,10 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     float *U = reinterpret_cast<float *>(ws + L.u);
     float *D = reinterpret_cast<float *>(ws + L.d);
 
-    int rc = launch_stage_x(X, n, H, ws + L.xp_x, ws + L.xs_x, s);
-    if (rc) return rc;
     hipLaunchKernelGGL(router_logits_kernel, dim3(ceil_div(E, 4), ceil_div(n, kRouterPos)),
                        dim3(256), 0, s, X, Wr, n, H, E, logits);
-    if ((rc = launch_status())) return rc;
+    int rc = launch_status();
+    if (rc) return rc;
     hipLaunchKernelGGL(route_kernel, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel,
                        route_w);
     if ((rc = launch_status())) return rc;
@@ -207,39 +197,40 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
                        lists);
     if ((rc = launch_status())) return rc;
 
-    MmaPanel up{};
+    ExpertBank up{};
     up.q = up_q;
     up.scale = up_scale;
     up.bias = up_bias;
     up.rows = I;
     up.cols = H;
-    up.xp = reinterpret_cast<const u32x4 *>(ws + L.xp_x);
-    up.xs = reinterpret_cast<const u32x4 *>(ws + L.xs_x);
-    up.zero_row = n;
+    up.q_stride = (long long)I * H;
+    up.s_stride = (long long)I * (H / 32);
+    up.x = X;
+    up.ldx = H;
     up.src_div = top_k;
+    up.counts = counts;
+    up.lists = lists;
+    up.cap = n;
     up.out = U;
     up.ldo = I;
     up.act = 1;
-    up.frag = 0;
-    if ((rc = launch_expert_bank(up, E, counts, lists, n, s))) return rc;
+    if ((rc = launch_expert_bank(up, E, s))) return rc;
 
-    if ((rc = launch_stage_x(U, nk, I, ws + L.xp_u, ws + L.xs_u, s))) return rc;
-
-    MmaPanel dn{};
+    ExpertBank dn = up;
     dn.q = down_q;
     dn.scale = down_scale;
     dn.bias = down_bias;
     dn.rows = H;
     dn.cols = I;
-    dn.xp = reinterpret_cast<const u32x4 *>(ws + L.xp_u);
-    dn.xs = reinterpret_cast<const u32x4 *>(ws + L.xs_u);
-    dn.zero_row = nk;
+    dn.q_stride = (long long)H * I;
+    dn.s_stride = (long long)H * (I / 32);
+    dn.x = U;
+    dn.ldx = I;
     dn.src_div = 1;
     dn.out = D;
     dn.ldo = H;
     dn.act = 0;
-    dn.frag = 0;
-    if ((rc = launch_expert_bank(dn, E, counts, lists, n, s))) return rc;
+    if ((rc = launch_expert_bank(dn, E, s))) return rc;
 
     return launch_moe_combine(h, D, route_w, n, top_k, w_norm, eps, H, out, s);
 }
