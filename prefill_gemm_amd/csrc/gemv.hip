@@ -35,6 +35,10 @@ constexpr int kGemvWaves = kGemvThreads / kWave;
 //            the RMSNorm without another pass over the activations
 enum GemvMode { kPlain = 0, kAddNorm = 1, kResid = 2, kScaled = 3 };
 
+// Norm parts per thread that a kScaled product requests up front (2 x 256
+// threads cover the 512 parts of a 4096-row residual; more are read after).
+constexpr int kPartsAhead = 2;
+
 struct Fuse {
     const float *h;      // residual [cols] (kAddNorm) or [n] (kResid)
     const float *delta;  // kAddNorm: added to h first (NULL: nothing)
@@ -105,7 +109,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
     };
     load(0, wa, sa, ba);
 
+    // kScaled: the first kPartsAhead norm parts a thread adds are requested
+    // before the activation, so that both arrive in one round trip.
     float ss = 0.0f;
+    float pa[kPartsAhead];
+    if (MODE == kScaled) {
+#pragma unroll
+        for (int k = 0; k < kPartsAhead; ++k) {
+            const int j = threadIdx.x + kGemvThreads * k;
+            pa[k] = j < nm.n ? nm.parts[j] : 0.0f;
+        }
+    }
     for (int s = threadIdx.x; s < steps * 64; s += kGemvThreads) {
         float4 a[4];
         float sum = 0.0f;
@@ -141,7 +155,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
         seg_sum[s] = sum;
     }
     if (MODE == kScaled) {
-        for (int j = threadIdx.x; j < nm.n; j += kGemvThreads) ss += nm.parts[j];
+#pragma unroll
+        for (int k = 0; k < kPartsAhead; ++k) ss += pa[k];
+        for (int j = threadIdx.x + kGemvThreads * kPartsAhead; j < nm.n; j += kGemvThreads) ss += nm.parts[j];
     }
     if (NORM || MODE == kScaled) {
         ss = wave_sum(ss);
@@ -308,7 +324,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_f16_kernel(
     }
 }
 
-constexpr int kQ8Rw = 2, kQ8U = 2;
+#ifndef PG_GEMV_RW
+#define PG_GEMV_RW 2
+#endif
+#ifndef PG_GEMV_U
+#define PG_GEMV_U 2
+#endif
+constexpr int kQ8Rw = PG_GEMV_RW, kQ8U = PG_GEMV_U;
 constexpr int kF16Rw = 2, kF16U = 4;
 
 static int gemv_grid(int rows, int rw) { return ceil_div(rows, kGemvWaves * rw); }
