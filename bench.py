@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-components", action="store_true", help="only the timed steps")
+    ap.add_argument("--moe-only", action="store_true",
+                    help="run only the routed-MoE pass component (for profiling its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -325,6 +327,9 @@ def main():
         return
     import prefill_gemm_amd as pg
     import synth
+    if args.moe_only:
+        print(json.dumps({"moe_pass": component_moe(torch, pg, synth)}), flush=True)
+        return
 
     log("building inputs ...")
     frames, frame_bytes = make_frames(torch, pg, synth, (1, 64, 36))

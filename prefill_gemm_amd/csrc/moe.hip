@@ -28,6 +28,12 @@ constexpr int kMaxTopK = 16;
 // the 4-column groups l, l+64, ...; the 64 lane sums fold pairwise for
 // s = 32, 16, ..., 1 (lane l += lane l+s); the logit is lane 0's value.
 // Grid (ceil(E / 4), ceil(n / 8)); wave -> expert, 8 positions per workgroup.
+// The groups go in batches of kRouterBatch per lane: a batch's router and
+// activation loads for all 8 positions are issued before any of them is used
+// (one round trip per batch instead of one per group and position); each
+// position's chain still runs over its groups in ascending order.
+constexpr int kRouterBatch = 4;
+
 __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ X,
                                                             const float *__restrict__ Wr, int n,
                                                             int H, int E,
@@ -36,25 +42,48 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
     const int e = blockIdx.x * 4 + wave;
     if (e >= E) return;
     const int G4 = H >> 2;
+    const int b0 = blockIdx.y * kRouterPos;
     const float4 *wr = reinterpret_cast<const float4 *>(Wr + (long long)e * H);
-    for (int bb = 0; bb < kRouterPos; ++bb) {
-        const int b = blockIdx.y * kRouterPos + bb;
-        if (b >= n) break;
-        const float4 *xr = reinterpret_cast<const float4 *>(X + (long long)b * H);
-        float acc = 0.0f;
-        for (int g = lane; g < G4; g += 64) {
-            const float4 w = wr[g], x = xr[g];
-            acc = fmaf(w.x, x.x, acc);
-            acc = fmaf(w.y, x.y, acc);
-            acc = fmaf(w.z, x.z, acc);
-            acc = fmaf(w.w, x.w, acc);
+    float acc[kRouterPos];
+#pragma unroll
+    for (int bb = 0; bb < kRouterPos; ++bb) acc[bb] = 0.0f;
+    for (int g0 = lane; g0 < G4; g0 += 64 * kRouterBatch) {
+        float4 w[kRouterBatch], x[kRouterPos][kRouterBatch];
+#pragma unroll
+        for (int k = 0; k < kRouterBatch; ++k) {
+            const int g = g0 + 64 * k;
+            w[k] = g < G4 ? wr[g] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+            for (int bb = 0; bb < kRouterPos; ++bb) {
+                const int b = min(b0 + bb, n - 1);
+                x[bb][k] = g < G4 ? reinterpret_cast<const float4 *>(X + (long long)b * H)[g]
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
 #pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-            const float o = __shfl_down(acc, s, kWave);
-            acc = acc + o;
+        for (int k = 0; k < kRouterBatch; ++k) {
+            if (g0 + 64 * k >= G4) break;  // past the row: the chain ends (no extra terms)
+#pragma unroll
+            for (int bb = 0; bb < kRouterPos; ++bb) {
+                float a = acc[bb];
+                a = fmaf(w[k].x, x[bb][k].x, a);
+                a = fmaf(w[k].y, x[bb][k].y, a);
+                a = fmaf(w[k].z, x[bb][k].z, a);
+                a = fmaf(w[k].w, x[bb][k].w, a);
+                acc[bb] = a;
+            }
         }
-        if (lane == 0) logits[(long long)b * E + e] = acc;
+    }
+#pragma unroll
+    for (int bb = 0; bb < kRouterPos; ++bb) {
+        float v = acc[bb];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const float o = __shfl_down(v, s, kWave);
+            v = v + o;
+        }
+        const int b = b0 + bb;
+        if (lane == 0 && b < n) logits[(long long)b * E + e] = v;
     }
 }
 
