@@ -23,12 +23,13 @@ struct ExpertBank {
     const int32_t *counts;
     const int32_t *lists;  // [E][cap]
     int cap;               // at most 64
+    int experts;
     float *out;
     long long ldo;
     int act;
 };
 
-// Grid (row blocks, experts); an expert with no entries returns at once.
-int launch_expert_bank(const ExpertBank &P, int experts, hipStream_t s);
+// Experts [0, experts); those with no entries are skipped.
+int launch_expert_bank(const ExpertBank &P, hipStream_t s);
 
 }  // namespace pg

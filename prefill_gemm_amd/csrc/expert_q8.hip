@@ -28,14 +28,11 @@
 #include "pg_device.h"
 #include "pg_host.h"
 
-#ifndef PG_EXP_T
-#define PG_EXP_T 1
-#endif
 #ifndef PG_EXP_D
 #define PG_EXP_D 8
 #endif
 #ifndef PG_EXP_LDS
-#define PG_EXP_LDS (76 * 1024)
+#define PG_EXP_LDS (148 * 1024)
 #endif
 
 namespace pg {
@@ -43,14 +40,30 @@ namespace pg {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kExpThreads = 256;
+#ifndef PG_EXP_SCHED
+#define PG_EXP_SCHED 0
+#endif
+#ifndef PG_EXP_THREADS
+#define PG_EXP_THREADS 512
+#endif
+// What the scheduler may move across a step boundary (never memory loads,
+// which keep their issue order).
+constexpr int kExpSched = PG_EXP_SCHED;
+constexpr int kExpThreads = PG_EXP_THREADS;
 constexpr int kExpWaves = kExpThreads / kWave;
-constexpr int kExpTiles = PG_EXP_T;
+#ifndef PG_EXP_T
+#define PG_EXP_T 1
+#endif
 constexpr int kExpDepth = PG_EXP_D;
-constexpr int kExpDepth4 = 4;
-constexpr int kExpRows = kExpWaves * 16 * kExpTiles;
+constexpr int kExpTiles = PG_EXP_T;                    // 16-row weight tiles per wave
+constexpr int kExpRows = kExpWaves * 16 * kExpTiles;   // weight rows of one work item
+#ifndef PG_EXP_GROUP
+#define PG_EXP_GROUP 16
+#endif
+constexpr int kExpGroup = PG_EXP_GROUP;                // entries per pass over an item
 constexpr int kExpLds = PG_EXP_LDS;
 constexpr int kExpMaxCnt = 64;
+constexpr int kExpMaxExperts = 1024;
 
 // LDS bytes of a chunk of `kp` block pairs for cnt entries in MT tiles of 16:
 // hi and lo arrays of cnt + 1 rows (the last all zero) of 64 bytes a block
@@ -67,11 +80,9 @@ __device__ __forceinline__ int exp_chunk_pairs(int cnt, int mt, int d, int np) {
     const int need = (np + d - 1) / d * d;
     return kp < need ? kp : need;
 }
-// Ring depths: up to 32 entries (two tiles of 16) the ring holds kExpDepth
-// steps; with four tiles, kExpDepth4.  Either way one ring of steps must fit
-// the LDS budget at the largest entry count of its case.
-static_assert(exp_chunk_bytes(kExpDepth, 32, 2) <= kExpLds, "LDS budget: two entry tiles");
-static_assert(exp_chunk_bytes(kExpDepth4, kExpMaxCnt, 4) <= kExpLds, "LDS budget: four entry tiles");
+// One ring of steps must fit the LDS budget at the largest entry count.
+static_assert(exp_chunk_bytes(kExpDepth, kExpGroup, kExpGroup / 16) <= kExpLds, "LDS budget");
+static_assert(kExpLds + kExpMaxExperts * 4 + 16 <= 160 * 1024, "LDS of a compute unit");
 
 #ifndef PG_EXP_NT
 #define PG_EXP_NT 0
@@ -170,93 +181,100 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
         if (it % (16 * MT) > cnt) xsum[it] = 0.0f;
 }
 
-// Tiles [tg T, tg T + T) of this wave's kExpTiles, all columns.  AL is the
-// widest scale / bias load (in floats: 4, 2 or 1) that the block count and
-// the vectors' alignment allow.
-template <int MT, int T, int D, int AL>
-__device__ __forceinline__ void exp_pass(const ExpertBank &P, int e, int cnt, int tg, char *lds) {
-    constexpr int V = D / 2;                   // blocks of a window per lane group
-    constexpr int LW = AL < V ? AL : V;        // floats per scale / bias load
+// Load-side target: a work item's expert (its weight, scale and bias bases)
+// and this lane's offsets in its row.  Past the last item: no memory moves.
+struct ExpTgt {
+    const int8_t *q;
+    const float *s, *b;
+    int vq[kExpTiles], vs[kExpTiles];
+    bool live;
+};
+
+// One pass over a work item (expert e, weight rows rb * kExpRows ..) for its
+// entries m0 .. m0 + cnt - 1 (at most kExpGroup): its column chunks (staged
+// when the expert or the entry group changes, or every time when the entries
+// take more than one chunk), its steps, and its outputs.  The weight ring and
+// the scale windows come in holding this pass's first steps and leave holding
+// those of the pass after it (target tn).
+template <int MT, int D, int AL>
+__device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int cnt, int rb, bool fresh,
+                                         const ExpTgt &tc, const ExpTgt &tn, u32x4 (&wq)[D][kExpTiles],
+                                         float (&sw)[kExpTiles][D / 2], float (&bw)[kExpTiles][D / 2],
+                                         float (&swn)[kExpTiles][D / 2], float (&bwn)[kExpTiles][D / 2],
+                                         char *lds) {
+    constexpr int T = kExpTiles;
+    constexpr int V = D / 2;             // blocks of a window per lane group
+    constexpr int LW = AL < V ? AL : V;  // floats per scale / bias load
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15, g = lane >> 4;
     const int nb = P.cols >> 5;
     const int np = (nb + 1) >> 1;
-    const int nwin = (np + D - 1) / D;
-    const int32_t *list = P.lists + (long long)e * P.cap;
+    const int npp = (np + D - 1) / D * D;
+    const int q_bytes = P.rows * P.cols;
+    const int s_bytes = P.rows * nb * 4;
+    const int32_t *list = P.lists + (long long)e * P.cap + m0;
     const int kp = exp_chunk_pairs(cnt, MT, D, np);
+    const bool chunked = kp < npp;
     const int pitch = 128 * kp + 16;
     const int lo_off = (cnt + 1) * pitch;
     const int xs_off = 2 * (cnt + 1) * pitch;
 
-    // Weights, scales and biases go through buffer resources: a step past the
-    // last takes an empty resource (zeros, no memory traffic), so that every
-    // step issues the same loads and the memory counter waits stay constant;
-    // the reads of the missing second block of an odd block count (and of the
-    // blocks past the last in a window) land in the next row or return zeros
-    // past the end, and meet zero activations.
-    const int8_t *qe = P.q + (long long)e * P.q_stride;
-    const float *se = P.scale + (long long)e * P.s_stride;
-    const float *be = P.bias + (long long)e * P.s_stride;
-    const int q_bytes = P.rows * P.cols;
-    const int s_bytes = P.rows * nb * 4;
-    const int row0 = blockIdx.x * kExpRows + wave * 16 * kExpTiles + 16 * T * tg;
-    int vq[T], vs[T];
+    // Output rows of this lane's results (entry 16 mt + 4 g + v), requested
+    // now so that their wait at the end does not queue behind the next pass.
+    int orow[MT][4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int r = min(row0 + 16 * t + i16, P.rows - 1);
-        vq[t] = r * P.cols + 16 * g;
-        vs[t] = (r * nb + V * g) * 4;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 16 * mt + 4 * g + v;
+            orow[mt][v] = m < cnt ? list[m] : -1;
+        }
 
-    // Weight ring: step p (blocks 2p, 2p + 1) in slot p % D.
-    u32x4 wq[D][T];
-    auto load = [&](int p, u32x4 (&w)[T]) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rq = exp_rsrc(qe, p < np ? q_bytes : 0);
+    auto load = [&](const ExpTgt &t, int p, u32x4 (&w)[T]) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rq = exp_rsrc(t.q, t.live && p < np ? q_bytes : 0);
 #pragma unroll
-        for (int t = 0; t < T; ++t) w[t] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq[t], 64 * p, kExpNT);
+        for (int k = 0; k < T; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 64 * p, kExpNT);
     };
     // Scales and biases come a window of D steps (2D blocks) at a time: lane
     // group g holds blocks V g .. V g + V - 1 of the window for its row, and
     // a step takes its two blocks from the group that holds them (a lane
     // permute), so that the four lanes of a row do not each load them.
-    float sw[T][V], bw[T][V], swn[T][V], bwn[T][V];
-    auto load_win = [&](int w) __attribute__((always_inline)) {
-        const bool live = w < nwin;
-        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(se, live ? s_bytes : 0);
-        const __amdgpu_buffer_rsrc_t rb = exp_rsrc(be, live ? s_bytes : 0);
+    auto load_win = [&](const ExpTgt &t, int w) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t.s, t.live ? s_bytes : 0);
+        const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t.b, t.live ? s_bytes : 0);
         const int off = 8 * D * w;
 #pragma unroll
-        for (int t = 0; t < T; ++t)
+        for (int k = 0; k < T; ++k)
 #pragma unroll
             for (int j = 0; j < V; j += LW) {
                 if (LW == 4) {
-                    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vs[t], off + 4 * j, 0));
-                    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, vs[t], off + 4 * j, 0));
+                    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, t.vs[k], off + 4 * j, 0));
+                    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbs, t.vs[k], off + 4 * j, 0));
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        swn[t][j + k] = a[k];
-                        bwn[t][j + k] = b[k];
+                    for (int i = 0; i < 4; ++i) {
+                        swn[k][j + i] = a[i];
+                        bwn[k][j + i] = b[i];
                     }
                 } else if (LW == 2) {
-                    const f32x2 a = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vs[t], off + 4 * j, 0));
-                    const f32x2 b = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, vs[t], off + 4 * j, 0));
-                    swn[t][j] = a[0];
-                    swn[t][j + 1] = a[1];
-                    bwn[t][j] = b[0];
-                    bwn[t][j + 1] = b[1];
+                    const f32x2 a = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, t.vs[k], off + 4 * j, 0));
+                    const f32x2 b = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rbs, t.vs[k], off + 4 * j, 0));
+                    swn[k][j] = a[0];
+                    swn[k][j + 1] = a[1];
+                    bwn[k][j] = b[0];
+                    bwn[k][j + 1] = b[1];
                 } else {
-                    swn[t][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vs[t], off + 4 * j, 0));
-                    bwn[t][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, vs[t], off + 4 * j, 0));
+                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t.vs[k], off + 4 * j, 0));
+                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t.vs[k], off + 4 * j, 0));
                 }
             }
     };
 
     f32x4 acc[T][MT];
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int k = 0; k < T; ++k)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mt = 0; mt < MT; ++mt) acc[k][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // A operand of lane (i16, g): entry 16 mt + i16 (the zero row past cnt),
     // columns 16 (g & 1) + 8 (g >> 1) .. + 7 of the block, matching the
@@ -275,24 +293,21 @@ __device__ __forceinline__ void exp_pass(const ExpertBank &P, int e, int cnt, in
         constexpr int u = decltype(uc)::value;
         constexpr int gs = 2 * u / V, ev = 2 * u % V;
         const int src = (i16 + 16 * gs) * 4;
-        f32x2 s[T], b[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            s[t].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[t][ev])));
-            s[t].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[t][ev + 1])));
-            b[t].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[t][ev])));
-            b[t].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[t][ev + 1])));
-        }
         const int bl = 2 * p - cb0;
-        // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
-        // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
+        f32x2 s[T], b[T];
         bf16x8 b0[T], b1[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const auto e0 = __builtin_amdgcn_permlane32_swap(w[t].x, w[t].z, false, false);
-            const auto e1 = __builtin_amdgcn_permlane32_swap(w[t].y, w[t].w, false, false);
-            b0[t] = q8_to_bf16(e0[0], e1[0]);
-            b1[t] = q8_to_bf16(e0[1], e1[1]);
+        for (int k = 0; k < T; ++k) {
+            s[k].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[k][ev])));
+            s[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[k][ev + 1])));
+            b[k].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev])));
+            b[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev + 1])));
+            // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
+            // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
+            const auto e0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
+            const auto e1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
+            b0[k] = q8_to_bf16(e0[0], e1[0]);
+            b1[k] = q8_to_bf16(e0[1], e1[1]);
         }
         const f32x4 z{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -306,121 +321,210 @@ __device__ __forceinline__ void exp_pass(const ExpertBank &P, int e, int cnt, in
             const f32x4 xs0 = *reinterpret_cast<const f32x4 *>(xs);
             const f32x4 xs1 = *reinterpret_cast<const f32x4 *>(xs + 16 * MT);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                f32x4 d0 = mfma16(ah0, b0[t], z);
-                d0 = mfma16(al0, b0[t], d0);
-                f32x4 d1 = mfma16(ah1, b1[t], z);
-                d1 = mfma16(al1, b1[t], d1);
+            for (int k = 0; k < T; ++k) {
+                f32x4 d0 = mfma16(ah0, b0[k], z);
+                d0 = mfma16(al0, b0[k], d0);
+                f32x4 d1 = mfma16(ah1, b1[k], z);
+                d1 = mfma16(al1, b1[k], d1);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    float a = acc[t][mt][v];
-                    a = fmaf(s[t].x, d0[v], a);
-                    a = fmaf(s[t].y, d1[v], a);
-                    a = fmaf(b[t].x, xs0[v], a);
-                    a = fmaf(b[t].y, xs1[v], a);
-                    acc[t][mt][v] = a;
+                    float x = acc[k][mt][v];
+                    x = fmaf(s[k].x, d0[v], x);
+                    x = fmaf(s[k].y, d1[v], x);
+                    x = fmaf(b[k].x, xs0[v], x);
+                    x = fmaf(b[k].y, xs1[v], x);
+                    acc[k][mt][v] = x;
                 }
             }
         }
     };
 
-    // Loads are issued in step order (the scheduler may not interleave them),
-    // so that the wait for step p's data is always the same count: window w + 1
-    // goes out at the start of window w, ahead of the weights of its steps.
-    load_win(0);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<D>([&](auto uc) __attribute__((always_inline)) {
-        constexpr int u = decltype(uc)::value;
-        load(u, wq[u]);
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    for (int c0 = 0; c0 < np; c0 += kp) {
-        if (c0 > 0 || tg > 0) __syncthreads();
-        exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds);
-        __syncthreads();
-        const int c1 = min(np, c0 + kp);
+    // Every window issues the same loads in the same order (window w + 1 at
+    // the start of window w, then one weight step per step), so the wait for
+    // a step's data is always the same count.  The last window of the pass
+    // requests the next pass's first window and steps.
+    for (int c0 = 0; c0 < npp; c0 += kp) {
+        if (c0 > 0 || chunked || fresh) {
+            __syncthreads();
+            exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds);
+            __syncthreads();
+        }
+        const int c1 = min(npp, c0 + kp);
         for (int p0 = c0; p0 < c1; p0 += D) {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
+            for (int k = 0; k < T; ++k)
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    sw[t][j] = swn[t][j];
-                    bw[t][j] = bwn[t][j];
+                    sw[k][j] = swn[k][j];
+                    bw[k][j] = bwn[k][j];
                 }
-            load_win(p0 / D + 1);
-            __builtin_amdgcn_sched_barrier(0);
+            const bool last = p0 + D >= npp;
+            const ExpTgt &tl = last ? tn : tc;
+            const int pl = last ? p0 + D - npp : p0 + D;
+            load_win(tl, pl / D);
+            __builtin_amdgcn_sched_barrier(kExpSched);
             static_for<D>([&](auto uc) __attribute__((always_inline)) {
                 constexpr int u = decltype(uc)::value;
                 const int p = p0 + u;
-                if (p < c1) compute(uc, p, 2 * c0, wq[u]);
-                load(p + D, wq[u]);
-                __builtin_amdgcn_sched_barrier(0);
+#ifdef PG_EXP_NOCOMP
+                if (p < np) acc[0][0][0] += __builtin_bit_cast(float, wq[u][0].x ^ wq[u][T - 1].w) + sw[0][0] + bw[T - 1][0];
+#else
+                if (p < np) compute(uc, p, 2 * c0, wq[u]);
+#endif
+                load(tl, pl + u, wq[u]);
+                __builtin_amdgcn_sched_barrier(kExpSched);
             });
         }
     }
 
-    // Output element v of tile (t, mt): entry 16 mt + 4 g + v, weight row
-    // row0 + 16 t + i16.
+    // Output element v of tile (k, mt): entry 16 mt + 4 g + v, weight row
+    // rb * kExpRows + (wave T + k) * 16 + i16.
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int r = row0 + 16 * t + i16;
+    for (int k = 0; k < T; ++k) {
+        const int r = rb * kExpRows + (wave * T + k) * 16 + i16;
         if (r >= P.rows) continue;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = 16 * mt + 4 * g + v;
-                if (m < cnt) P.out[(long long)list[m] * P.ldo + r] = apply_act(P.act, acc[t][mt][v]);
-            }
+            for (int v = 0; v < 4; ++v)
+                if (orow[mt][v] >= 0) P.out[(long long)orow[mt][v] * P.ldo + r] = apply_act(P.act, acc[k][mt][v]);
     }
 }
 
-// Entries in tiles of 16: up to two tiles take all of a wave's weight tiles
-// in one pass; four take them one at a time (each pass stages its own
-// activations), which keeps the registers within two waves per SIMD.
-template <int MT, int AL>
-__device__ __forceinline__ void exp_body(const ExpertBank &P, int e, int cnt, char *lds) {
-    if (MT <= 2) {
-        exp_pass<MT, kExpTiles, kExpDepth, AL>(P, e, cnt, 0, lds);
-    } else {
-        for (int tg = 0; tg < kExpTiles; ++tg) exp_pass<MT, 1, kExpDepth4, AL>(P, e, cnt, tg, lds);
-    }
-}
-
+// Persistent workgroups, one per compute unit.  The work items are (active
+// expert, block of kExpRows weight rows), experts in ascending order; each
+// workgroup takes one contiguous share, so that it stages an expert's entries
+// once for all of that expert's items in its share, and its weight stream
+// runs from one item into the next without draining.  An expert with more
+// than kExpGroup entries takes one pass per group of kExpGroup over each item.
 template <int AL>
-__global__ __launch_bounds__(kExpThreads, 2) void expert_bank_kernel(ExpertBank P) {
+__global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
     extern __shared__ u32x4 exp_lds[];
-    const int e = blockIdx.y;
-    const int cnt = min(P.counts[e], min(P.cap, kExpMaxCnt));
-    if (cnt <= 0) return;
+    __shared__ int act[kExpMaxExperts];
+    __shared__ int nact_s;
+    constexpr int D = kExpDepth, T = kExpTiles, V = D / 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int i16 = lane & 15, g = lane >> 4;
     char *lds = reinterpret_cast<char *>(exp_lds);
-    if (cnt <= 16)
-        exp_body<1, AL>(P, e, cnt, lds);
-    else if (cnt <= 32)
-        exp_body<2, AL>(P, e, cnt, lds);
-    else
-        exp_body<4, AL>(P, e, cnt, lds);
+
+    // Active experts (at least one entry), ascending.
+    if (wave == 0) {
+        int base = 0;
+        for (int e0 = 0; e0 < P.experts; e0 += 64) {
+            const int e = e0 + lane;
+            const bool on = e < P.experts && P.counts[e] > 0;
+            const unsigned long long m = __ballot(on);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (on) act[base + below] = e;
+            base += __popcll(m);
+        }
+        if (lane == 0) nact_s = base;
+    }
+    __syncthreads();
+    const int RB = (P.rows + kExpRows - 1) / kExpRows;
+    const long long N = (long long)nact_s * RB;
+    const int i0 = (int)(N * blockIdx.x / gridDim.x);
+    const int i1 = (int)(N * (blockIdx.x + 1) / gridDim.x);
+    if (i0 >= i1) return;
+
+    const int nb = P.cols >> 5;
+    auto target = [&](int item) __attribute__((always_inline)) {
+        ExpTgt t;
+        t.live = item < i1;
+        const int it = t.live ? item : i1 - 1;
+        const int e = __builtin_amdgcn_readfirstlane(act[it / RB]);
+        const int rb = it % RB;
+        t.q = P.q + (long long)e * P.q_stride;
+        t.s = P.scale + (long long)e * P.s_stride;
+        t.b = P.bias + (long long)e * P.s_stride;
+#pragma unroll
+        for (int k = 0; k < T; ++k) {
+            const int r = min(rb * kExpRows + (wave * T + k) * 16 + i16, P.rows - 1);
+            t.vq[k] = r * P.cols + 16 * g;
+            t.vs[k] = (r * nb + V * g) * 4;
+        }
+        return t;
+    };
+    auto count = [&](int e) __attribute__((always_inline)) { return min(P.counts[e], min(P.cap, kExpMaxCnt)); };
+
+    // The ring and the windows start out holding the first item's window 0
+    // and steps 0 .. D - 1 (loaded in step order).
+    u32x4 wq[D][T];
+    float sw[T][V], bw[T][V], swn[T][V], bwn[T][V];
+    {
+        const ExpTgt t0 = target(i0);
+        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t0.s, P.rows * nb * 4);
+        const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t0.b, P.rows * nb * 4);
+#pragma unroll
+        for (int k = 0; k < T; ++k)
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t0.vs[k], 4 * j, 0));
+                bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t0.vs[k], 4 * j, 0));
+            }
+        __builtin_amdgcn_sched_barrier(kExpSched);
+        const int np = (nb + 1) >> 1;
+        static_for<D>([&](auto uc) __attribute__((always_inline)) {
+            constexpr int u = decltype(uc)::value;
+            const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
+#pragma unroll
+            for (int k = 0; k < T; ++k) wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 64 * u, kExpNT);
+            __builtin_amdgcn_sched_barrier(kExpSched);
+        });
+    }
+
+    int prev = -1;
+    for (int item = i0; item < i1; ++item) {
+        const int e = __builtin_amdgcn_readfirstlane(act[item / RB]);
+        const int rb = item % RB;
+        const int cnt = count(e);
+        const ExpTgt tc = target(item), tn = target(item + 1);
+        const int groups = (cnt + kExpGroup - 1) / kExpGroup;
+        for (int gi = 0; gi < groups; ++gi) {
+            const int m0 = gi * kExpGroup;
+            const int cg = min(kExpGroup, cnt - m0);
+            const bool fresh = e != prev || groups > 1;
+            const ExpTgt &nx = gi + 1 < groups ? tc : tn;
+            if (kExpGroup <= 16 || cg <= 16)
+                exp_item<1, D, AL>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+            else
+                exp_item<2, D, AL>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+        }
+        prev = e;
+    }
+}
+
+static int exp_grid() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
 }
 
 template <int AL>
-static int launch_bank(const ExpertBank &P, int experts, hipStream_t s) {
+static int launch_bank(const ExpertBank &P, hipStream_t s) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kExpLds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL(expert_bank_kernel<AL>, dim3(ceil_div(P.rows, kExpRows), experts), dim3(kExpThreads),
-                       kExpLds, s, P);
+    hipLaunchKernelGGL(expert_bank_kernel<AL>, dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
     return launch_status();
 }
 
-int launch_expert_bank(const ExpertBank &P, int experts, hipStream_t s) {
+int launch_expert_bank(const ExpertBank &P, hipStream_t s) {
     if (P.rows < 1 || P.cols < 32 || P.cols % 32 || P.cap > kExpMaxCnt) return PG_EUNSUPPORTED;
+    if (P.experts < 1 || P.experts > kExpMaxExperts) return PG_EUNSUPPORTED;
     if ((long long)P.rows * P.cols >= (1ll << 31)) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
     // Widest scale / bias loads: a row's blocks must start on that boundary.
     const int nb = P.cols / 32;
     const uintptr_t a = (uintptr_t)P.scale | (uintptr_t)P.bias;
-    if (nb % 4 == 0 && (a & 15) == 0) return launch_bank<4>(P, experts, s);
-    if (nb % 2 == 0 && (a & 7) == 0) return launch_bank<2>(P, experts, s);
-    if ((a & 3) == 0) return launch_bank<1>(P, experts, s);
+    if (nb % 4 == 0 && (a & 15) == 0) return launch_bank<4>(P, s);
+    if (nb % 2 == 0 && (a & 7) == 0) return launch_bank<2>(P, s);
+    if ((a & 3) == 0) return launch_bank<1>(P, s);
     return PG_EINVAL;
 }
 

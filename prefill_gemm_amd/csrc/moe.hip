@@ -240,10 +240,11 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     up.counts = counts;
     up.lists = lists;
     up.cap = n;
+    up.experts = E;
     up.out = U;
     up.ldo = I;
     up.act = 1;
-    if ((rc = launch_expert_bank(up, E, s))) return rc;
+    if ((rc = launch_expert_bank(up, s))) return rc;
 
     ExpertBank dn = up;
     dn.q = down_q;
@@ -259,7 +260,7 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     dn.out = D;
     dn.ldo = H;
     dn.act = 0;
-    if ((rc = launch_expert_bank(dn, E, s))) return rc;
+    if ((rc = launch_expert_bank(dn, s))) return rc;
 
     return launch_moe_combine(h, D, route_w, n, top_k, w_norm, eps, H, out, s);
 }

@@ -89,7 +89,10 @@ def _check_routing(oracle, c, o, renorm=0):
 @pytest.mark.parametrize("shape", [synth.MoEShape(n=8, hidden=64, inter=96, experts=6, top_k=2),
                                    synth.MoEShape(n=40, hidden=256, inter=160, experts=16, top_k=4),
                                    synth.MoEShape(n=1, hidden=32, inter=32, experts=1, top_k=1),
-                                   synth.MoEShape(n=64, hidden=128, inter=64, experts=3, top_k=3)])
+                                   synth.MoEShape(n=64, hidden=128, inter=64, experts=3, top_k=3),
+                                   # about 24 entries per expert over 4096 columns: two entry
+                                   # groups per item, each staged in column chunks
+                                   synth.MoEShape(n=48, hidden=4096, inter=160, experts=4, top_k=2)])
 @pytest.mark.parametrize("renorm", [0, 1])
 def test_moe_small(pg, oracle, shape, renorm):
     _case(f"moe {shape} renorm={renorm}")
