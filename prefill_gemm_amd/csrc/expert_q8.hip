@@ -366,11 +366,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             static_for<D>([&](auto uc) __attribute__((always_inline)) {
                 constexpr int u = decltype(uc)::value;
                 const int p = p0 + u;
-#ifdef PG_EXP_NOCOMP
-                if (p < np) acc[0][0][0] += __builtin_bit_cast(float, wq[u][0].x ^ wq[u][T - 1].w) + sw[0][0] + bw[T - 1][0];
-#else
                 if (p < np) compute(uc, p, 2 * c0, wq[u]);
-#endif
                 load(tl, pl + u, wq[u]);
                 __builtin_amdgcn_sched_barrier(kExpSched);
             });
