@@ -137,27 +137,36 @@ def run_step(torch, dec, pre, inp, timers):
 # ----------------------------------------------------------------- components
 
 def component_f16(torch, pg, synth, reps=100, copies=16):
+    """The f16 GEMV repeated back to back (steady state), over rotated copies so
+    that the weights come from HBM; also one call at a time between events."""
     rng = synth.streams(7, copies + 1)
     Ws = [to_dev(torch, synth.f16(rng[i], 4096, 4096)) for i in range(copies)]
     x = to_dev(torch, synth.normal(rng[copies], 4096))
     y = torch.empty(4096, device="cuda")
     for i in range(copies):
         pg.gemv_f16(Ws[i], x, y)
-    t = Timer(torch)
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        for r in range(reps):
+            pg.gemv_f16(Ws[r % copies], x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    t = Timer(torch)
     for r in range(reps):
         s = t.start()
         pg.gemv_f16(Ws[r % copies], x, y)
         t.stop(s)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    per = t.total_ms() / reps
+    single = t.total_ms() / reps
     nbytes = 4096 * 4096 * 2
-    return {"workload": "f16 GEMV 4096x4096, 100 reps over 16 rotated copies",
-            "us_per_gemv": round(per * 1e3, 3), "GB_s": round(nbytes / (per * 1e-3) / 1e9, 1),
-            "GB_s_wall": round(reps * nbytes / wall / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / (per * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return {"workload": "f16 GEMV 4096x4096, 100 back-to-back launches over 16 rotated copies",
+            "us_per_gemv": round(best * 1e3, 3), "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "us_per_isolated_call": round(single * 1e3, 3)}
 
 
 def component_gemv_norm(torch, pg, synth, reps=200):

@@ -331,7 +331,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_f16_kernel(
 #define PG_GEMV_U 2
 #endif
 constexpr int kQ8Rw = PG_GEMV_RW, kQ8U = PG_GEMV_U;
-constexpr int kF16Rw = 2, kF16U = 4;
+// f16: one row per wave (4096-column rows: the whole row in one batch of 4 x 2 steps).
+constexpr int kF16Rw = 1, kF16U = 4;
 
 static int gemv_grid(int rows, int rw) { return ceil_div(rows, kGemvWaves * rw); }
 
