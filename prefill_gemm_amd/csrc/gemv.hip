@@ -155,6 +155,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q8_kernel(
         seg_sum[s] = sum;
     }
     if (MODE == kScaled) {
+        // Opaque to the compiler, so that no add of a part (and its wait for
+        // the memory counter, which covers the weights requested earlier) is
+        // moved ahead of the activation staging.
+#pragma unroll
+        for (int k = 0; k < kPartsAhead; ++k) asm volatile("" : "+v"(pa[k]));
 #pragma unroll
         for (int k = 0; k < kPartsAhead; ++k) ss += pa[k];
         for (int j = threadIdx.x + kGemvThreads * kPartsAhead; j < nm.n; j += kGemvThreads) ss += nm.parts[j];
