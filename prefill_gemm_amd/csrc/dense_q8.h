@@ -488,7 +488,9 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     for (int c = 1; c < NW - 1; ++c) copy_w(c);
 #pragma unroll
     for (int k = 0; k < 4 * C::kBPer; ++k) copy_b(0, (4 * w + k / C::kBPer) * C::kBPer + k % C::kBPer);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Stage 0 only: the copies issued after X(0) (the other prologue stages and
+    // group 0's biases) may still be in flight; the stage-end waits cover them.
+    wait_vm<(NX - 2) * C::kXCopies + (NW - 2) * (C::kQPer + C::kSPer) + 4 * C::kBPer>();
     __builtin_amdgcn_s_barrier();
 
     // ------------------------------------------------------------ compute
