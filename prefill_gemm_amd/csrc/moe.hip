@@ -89,10 +89,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 
 // One wave per position: softmax over all E logits, then k rounds that take
 // the largest remaining logit (lower index on an exact tie) and mask it.
+// V = logits per lane (E <= 64 V); a lane's experts are lane, lane + 64, ...
+template <int V>
 __global__ __launch_bounds__(64) void route_kernel(const float *__restrict__ logits, int E, int k,
                                                    int renorm, int32_t *__restrict__ sel,
                                                    float *__restrict__ rw) {
-    constexpr int V = kMaxExperts / kWave;
     const int b = blockIdx.x, lane = threadIdx.x;
     float v[V];
     float mx = -INFINITY;
@@ -219,8 +220,15 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
                        dim3(256), 0, s, X, Wr, n, H, E, logits);
     int rc = launch_status();
     if (rc) return rc;
-    hipLaunchKernelGGL(route_kernel, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel,
-                       route_w);
+    if (E <= 64)
+        hipLaunchKernelGGL(route_kernel<1>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
+    else if (E <= 128)
+        hipLaunchKernelGGL(route_kernel<2>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
+    else if (E <= 256)
+        hipLaunchKernelGGL(route_kernel<4>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
+    else
+        hipLaunchKernelGGL(route_kernel<kMaxExperts / kWave>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm,
+                           sel, route_w);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(group_kernel, dim3(ceil_div(E, 4)), dim3(256), 0, s, sel, nk, E, n, counts,
                        lists);
