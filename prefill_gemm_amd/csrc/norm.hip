@@ -11,6 +11,7 @@ constexpr int kNormThreads = 256;
 constexpr int kNormMaxV = 16;  // float4 per thread: hidden <= 16384
 
 // Sum over the workgroup; every thread receives the total.
+template <int THREADS = kNormThreads>
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -18,7 +19,7 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
     __syncthreads();
     float t = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kNormThreads / kWave; ++i) t += red[i];
+    for (int i = 0; i < THREADS / kWave; ++i) t += red[i];
     return t;
 }
 
@@ -63,39 +64,69 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
 
 // MoE combine: h' = h + sum_t rw[b][t] * D[b*k + t] (slot order t ascending);
 // out = w * (h' * rsqrt(mean(h'^2) + eps)).
-__global__ __launch_bounds__(kNormThreads) void moe_combine_kernel(
+// One workgroup of 1024 threads per position (a position's rows are few and
+// short, so every load of the position should be in flight at once): the
+// slots' rows come kCombT at a time, and each element adds them in slot order.
+constexpr int kCombThreads = 1024;
+constexpr int kCombV = 4;  // float4 per thread: hidden <= 16384
+constexpr int kCombT = 4;  // slots requested together
+
+__global__ __launch_bounds__(kCombThreads) void moe_combine_kernel(
     float *__restrict__ h, const float *__restrict__ D, const float *__restrict__ rw, int k,
     const float *__restrict__ w, float eps, int hidden, float *__restrict__ out) {
-    __shared__ float red[kNormThreads / kWave];
+    __shared__ float red[kCombThreads / kWave];
     const int b = blockIdx.x;
     const int h4 = hidden >> 2;
     float4 *hr = reinterpret_cast<float4 *>(h + (long long)b * hidden);
-    float4 v[kNormMaxV];
+    float4 v[kCombV], m[kCombV];
+#pragma unroll
+    for (int kk = 0; kk < kCombV; ++kk) {
+        const int i = threadIdx.x + kk * kCombThreads;
+        v[kk] = i < h4 ? hr[i] : make_float4(0, 0, 0, 0);
+        m[kk] = make_float4(0, 0, 0, 0);
+    }
+    for (int t0 = 0; t0 < k; t0 += kCombT) {
+        float c[kCombT];
+        float4 d[kCombT][kCombV];
+#pragma unroll
+        for (int tt = 0; tt < kCombT; ++tt) {
+            const int t = t0 + tt;
+            c[tt] = t < k ? rw[b * k + t] : 0.0f;
+            const float4 *dr = reinterpret_cast<const float4 *>(D + (long long)(b * k + min(t, k - 1)) * hidden);
+#pragma unroll
+            for (int kk = 0; kk < kCombV; ++kk) {
+                const int i = threadIdx.x + kk * kCombThreads;
+                d[tt][kk] = t < k && i < h4 ? dr[i] : make_float4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kCombT; ++tt) {
+            if (t0 + tt >= k) break;
+#pragma unroll
+            for (int kk = 0; kk < kCombV; ++kk) {
+                m[kk].x = fmaf(c[tt], d[tt][kk].x, m[kk].x); m[kk].y = fmaf(c[tt], d[tt][kk].y, m[kk].y);
+                m[kk].z = fmaf(c[tt], d[tt][kk].z, m[kk].z); m[kk].w = fmaf(c[tt], d[tt][kk].w, m[kk].w);
+            }
+        }
+    }
     float ss = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < kNormMaxV; ++kk) {
-        const int i = threadIdx.x + kk * kNormThreads;
+    for (int kk = 0; kk < kCombV; ++kk) {
+        const int i = threadIdx.x + kk * kCombThreads;
         if (i < h4) {
-            float4 m = make_float4(0, 0, 0, 0);
-            for (int t = 0; t < k; ++t) {
-                const float c = rw[b * k + t];
-                const float4 d = reinterpret_cast<const float4 *>(D + (long long)(b * k + t) * hidden)[i];
-                m.x = fmaf(c, d.x, m.x); m.y = fmaf(c, d.y, m.y);
-                m.z = fmaf(c, d.z, m.z); m.w = fmaf(c, d.w, m.w);
-            }
-            float4 a = hr[i];
-            a.x += m.x; a.y += m.y; a.z += m.z; a.w += m.w;
+            float4 a = v[kk];
+            a.x += m[kk].x; a.y += m[kk].y; a.z += m[kk].z; a.w += m[kk].w;
             hr[i] = a;
             v[kk] = a;
             ss += (a.x * a.x + a.y * a.y) + (a.z * a.z + a.w * a.w);
         }
     }
-    const float inv = rsqrtf(block_sum(ss, red) / (float)hidden + eps);
+    const float inv = rsqrtf(block_sum<kCombThreads>(ss, red) / (float)hidden + eps);
     const float4 *wr = reinterpret_cast<const float4 *>(w);
     float4 *orow = reinterpret_cast<float4 *>(out + (long long)b * hidden);
 #pragma unroll
-    for (int kk = 0; kk < kNormMaxV; ++kk) {
-        const int i = threadIdx.x + kk * kNormThreads;
+    for (int kk = 0; kk < kCombV; ++kk) {
+        const int i = threadIdx.x + kk * kCombThreads;
         if (i < h4) {
             const float4 g = wr[i];
             orow[i] = make_float4(g.x * (v[kk].x * inv), g.y * (v[kk].y * inv),
@@ -106,7 +137,7 @@ __global__ __launch_bounds__(kNormThreads) void moe_combine_kernel(
 
 int launch_moe_combine(float *h, const float *D, const float *rw, int n, int k, const float *w,
                        float eps, int hidden, float *out, hipStream_t s) {
-    hipLaunchKernelGGL(moe_combine_kernel, dim3(n), dim3(kNormThreads), 0, s, h, D, rw, k, w, eps,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(n), dim3(kCombThreads), 0, s, h, D, rw, k, w, eps,
                        hidden, out);
     return launch_status();
 }
