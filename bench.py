@@ -170,6 +170,8 @@ def component_f16(torch, pg, synth, reps=100, copies=16):
 
 
 def component_gemv_norm(torch, pg, synth, reps=200):
+    """The small q8 GEMV followed by add + RMSNorm, pairs back to back (steady
+    state; the 1.3 MB of weights stay in cache), and one pair at a time."""
     c = synth.gemv_add_norm(0)
     W = q8_dev(torch, pg, c["W"])
     x, w = to_dev(torch, c["x"]), to_dev(torch, c["w"])
@@ -179,8 +181,16 @@ def component_gemv_norm(torch, pg, synth, reps=200):
     for _ in range(5):
         pg.gemv_q8(W, x, y)
         pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
-    t = Timer(torch)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pg.gemv_q8(W, x, y)
+        pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    back_to_back = e0.elapsed_time(e1) / reps
+    t = Timer(torch)
     for _ in range(reps):
         s = t.start()
         pg.gemv_q8(W, x, y)
@@ -188,7 +198,8 @@ def component_gemv_norm(torch, pg, synth, reps=200):
         t.stop(s)
     torch.cuda.synchronize()
     return {"workload": "q8 GEMV 1024x1024 + add + RMSNorm (cache resident)",
-            "us_per_pair": round(t.total_ms() / reps * 1e3, 3)}
+            "us_per_pair": round(back_to_back * 1e3, 3),
+            "us_per_isolated_pair": round(t.total_ms() / reps * 1e3, 3)}
 
 
 def component_prompt(torch, frames, inp, reps=3):
