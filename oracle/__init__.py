@@ -54,6 +54,8 @@ def _declare(L):
     L.oracle_gemm_q8.argtypes = [_P, _P, _P, _I, _I, _P, _I, _i, _P]
     L.oracle_gemm_q8_rows.argtypes = [_P, _P, _P, _I, _I, _P, _I, _P, _I, _i, _P]
     L.oracle_gemm_f16.argtypes = [_P, _I, _I, _P, _I, _i, _P]
+    L.oracle_dequant_q82.argtypes = [_P, _P, _P, _I, _I, _P]
+    L.oracle_gemm_q82.argtypes = [_P, _P, _P, _I, _I, _P, _I, _i, _P]
     L.oracle_add_rmsnorm.argtypes = [_P, _P, _I, _P, _D, _I, _I, _P, _P]
     L.oracle_router_logits_f64.argtypes = [_P, _P, _I, _I, _I, _P]
     L.oracle_router_logits_f32.argtypes = [_P, _P, _I, _I, _I, _P]
@@ -124,6 +126,35 @@ def gemm_f16(W, X, act: int = 0) -> np.ndarray:
     rows, cols = Wb.shape
     Y = np.empty((X.shape[0], rows), np.float64)
     lib().oracle_gemm_f16(_p(Wb), rows, cols, _p(X), X.shape[0], act, _p(Y))
+    return Y[0] if vec else Y
+
+
+def _f16bits(a) -> np.ndarray:
+    return _c(np.asarray(a, dtype=np.float16).view(np.uint16), np.uint16)
+
+
+def dequant_q82(q, rs, cf) -> np.ndarray:
+    """q8_2f: w[r][c] = f16(rs[r]) * f16(cf[c]) * q[r][c] (float64); rs, cf given as float16."""
+    q = _c(q, np.int8)
+    rows, cols = q.shape
+    rb, cb = _f16bits(rs), _f16bits(cf)
+    assert rb.size == rows and cb.size == cols
+    w = np.empty((rows, cols), np.float64)
+    lib().oracle_dequant_q82(_p(q), _p(rb), _p(cb), rows, cols, _p(w))
+    return w
+
+
+def gemm_q82(q, rs, cf, X, act: int = 0) -> np.ndarray:
+    """Y[b][r] = act(sum_c rs[r] cf[c] q[r][c] X[b][c]); rs, cf float16; X [n][cols] or [cols]."""
+    q = _c(q, np.int8)
+    rows, cols = q.shape
+    rb, cb = _f16bits(rs), _f16bits(cf)
+    assert rb.size == rows and cb.size == cols
+    vec = np.ndim(X) == 1
+    X = _c(np.atleast_2d(X), np.float32)
+    assert X.shape[1] == cols
+    Y = np.empty((X.shape[0], rows), np.float64)
+    lib().oracle_gemm_q82(_p(q), _p(rb), _p(cb), rows, cols, _p(X), X.shape[0], act, _p(Y))
     return Y[0] if vec else Y
 
 

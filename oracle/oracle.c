@@ -25,10 +25,9 @@
  *  - routed expert FFN and the slot-ordered weighted sum into the residual:
  *    nemotron_prefill.rs, `pb_q8_bank` and `pb_add_rms` (add == 2).
  *
- * The int8 block format (32 consecutive columns of a row share one f32 scale
- * and one f32 bias, w = scale*q + bias) is this library's weight format; the
- * pages' own q8_2f format (int8 body, f16 row scales, f16 column field) is a
- * different encoding of the same idea.
+ * Two int8 formats: the block format (32 consecutive columns of a row share
+ * one f32 scale and one f32 bias, w = scale*q + bias), and the pages' own
+ * q8_2f format (int8 body, f16 row scales, f16 column field, w = rs*cf*q).
  *
  * Parity status: every function here is pinned by the CPU test suite (closed
  * forms, invariants, brute force, textbook routines); none is "parity unpinned".
@@ -122,6 +121,40 @@ void oracle_gemm_f16(const uint16_t *W, int64_t rows, int64_t cols, const float 
         double acc = 0.0;
         for (int64_t c = 0; c < cols; ++c)
             acc += oracle_f16_to_f64(W[r * cols + c]) * (double)X[b * cols + c];
+        Y[b * rows + r] = act_apply(act, acc);
+    }
+}
+
+/* ------------------------------------------------------------ q8_2f */
+
+/* The pages' own int8 format (gemma_batch.rs, `q8_2f_mm_r2` doc comment and
+ * epilogue; nemotron_prefill.rs, the q8_2f expert-bank payload): an int8 body
+ * q[rows][cols], one binary16 scale per row rs[rows] and one binary16 factor per
+ * column cf[cols] (the "column field").  The column field multiplies the
+ * activation before the product and the row scale the finished sum, so the
+ * weight the product applies is
+ *     w[r][c] = rs[r] * cf[c] * q[r][c]. */
+static inline double q82_weight(const int8_t *q, const uint16_t *rs, const uint16_t *cf,
+                                int64_t cols, int64_t r, int64_t c) {
+    return oracle_f16_to_f64(rs[r]) * oracle_f16_to_f64(cf[c]) * (double)q[r * cols + c];
+}
+
+void oracle_dequant_q82(const int8_t *q, const uint16_t *rs, const uint16_t *cf, int64_t rows,
+                        int64_t cols, double *w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            w[r * cols + c] = q82_weight(q, rs, cf, cols, r, c);
+}
+
+/* Y[b][r] = act( sum_c w[r][c] * X[b][c] ) with the q8_2f weight above. */
+void oracle_gemm_q82(const int8_t *q, const uint16_t *rs, const uint16_t *cf, int64_t rows,
+                     int64_t cols, const float *X, int64_t n, int act, double *Y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * rows; ++i) {
+        int64_t b = i / rows, r = i % rows;
+        double acc = 0.0;
+        for (int64_t c = 0; c < cols; ++c)
+            acc += q82_weight(q, rs, cf, cols, r, c) * (double)X[b * cols + c];
         Y[b * rows + r] = act_apply(act, acc);
     }
 }

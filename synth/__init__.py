@@ -58,6 +58,23 @@ def q8(rng: np.random.Generator, rows: int, cols: int, lead: tuple = ()) -> Q8:
     return Q8(q, scale, bias)
 
 
+class Q82:
+    """A q8_2f matrix: int8 body [rows][cols], binary16 row scales [rows] and column field [cols]."""
+
+    def __init__(self, q: np.ndarray, rs: np.ndarray, cf: np.ndarray):
+        self.q, self.rs, self.cf = q, rs, cf
+
+
+def q82(rng: np.random.Generator, rows: int, cols: int) -> Q82:
+    """Draw a q8_2f matrix: q U[-127, 127], row scales U(1e-3, 1e-2) and column field
+    U(0.5, 1.5), both rounded to binary16 (the pages fix no distribution; these keep the
+    weights in the block format's range)."""
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    rs = rng.uniform(1e-3, 1e-2, size=rows).astype(np.float16)
+    cf = rng.uniform(0.5, 1.5, size=cols).astype(np.float16)
+    return Q82(q, rs, cf)
+
+
 def f16(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
     """N(0, 0.02) weights rounded to binary16 (round to nearest even)."""
     return rng.normal(0.0, 0.02, size=(rows, cols)).astype(np.float16)

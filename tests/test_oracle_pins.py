@@ -172,6 +172,86 @@ def test_gemm_q8_act_and_rows(oracle):
         assert np.array_equal(oracle.gemm_q8(q, s, b, X[p]), Y0[p])
 
 
+# ------------------------------------------------------------------ q8_2f products
+
+def _rand_q82(rng, rows, cols):
+    """q8_2f inputs (synthetic recipe): q U[-127,127], row scales U(1e-3,1e-2) and column
+    field U(0.5,1.5), both rounded to binary16."""
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    rs = rng.uniform(1e-3, 1e-2, rows).astype(np.float16)
+    cf = rng.uniform(0.5, 1.5, cols).astype(np.float16)
+    return q, rs, cf
+
+
+def test_gemm_q82_brute_force_fractions(oracle):
+    """Exact rational evaluation of w = rs[r] cf[c] q[r][c] on a tiny 3x40 matrix (binary16
+    values are exact in binary64, so Fraction(float(.)) is their exact value)."""
+    rng = np.random.default_rng(31)
+    q, rs, cf = _rand_q82(rng, 3, 40)
+    X = rng.standard_normal((2, 40)).astype(np.float32)
+    Y = oracle.gemm_q82(q, rs, cf, X)
+    for p in range(2):
+        for r in range(3):
+            acc = sum(Fraction(float(rs[r])) * Fraction(float(cf[c])) * int(q[r, c]) * Fraction(float(X[p, c]))
+                      for c in range(40))
+            assert abs(Y[p, r] - float(acc)) <= 1e-13 * max(1.0, abs(float(acc)))
+
+
+def test_gemm_q82_exact_integer_case(oracle):
+    """Power-of-two row scales and column field with integer x: the f64 result equals the
+    integer product exactly (the case a device must match bit for bit)."""
+    rng = np.random.default_rng(32)
+    rows, cols, n = 29, 160, 4
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
+    cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
+    X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
+    Y = oracle.gemm_q82(q, rs, cf, X)
+    num = (X.astype(np.int64) * (cf.astype(np.float64) * 2).astype(np.int64)) @ q.astype(np.int64).T
+    exact = num * rs.astype(np.float64)[None, :] / 2
+    assert np.array_equal(Y, exact)
+
+
+def test_gemm_q82_equals_block_format_without_column_field(oracle):
+    """cf = 1 and rs[r] = s_r make q8_2f the block format with scale s_r on every block and
+    zero bias: the two oracles agree (a swapped row / column role would not)."""
+    rng = np.random.default_rng(33)
+    rows, cols, n = 24, 96, 3
+    q, rs, _ = _rand_q82(rng, rows, cols)
+    cf = np.ones(cols, np.float16)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    s = np.repeat(rs.astype(np.float32)[:, None], cols // BLOCK, 1)
+    b = np.zeros_like(s)
+    np.testing.assert_allclose(oracle.gemm_q82(q, rs, cf, X), oracle.gemm_q8(q, s, b, X),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_gemm_q82_column_field_folds_into_x(oracle):
+    """The column field can be moved onto the activation (the pages fold it into the staged
+    x): with power-of-two cf the folded x is exact in f32 and the results are equal."""
+    rng = np.random.default_rng(34)
+    rows, cols, n = 17, 128, 2
+    q, rs, _ = _rand_q82(rng, rows, cols)
+    cf = (2.0 ** rng.integers(-2, 3, cols)).astype(np.float16)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    folded = (X * cf.astype(np.float32)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.gemm_q82(q, rs, cf, X),
+                                  oracle.gemm_q82(q, rs, np.ones(cols, np.float16), folded))
+
+
+def test_gemm_q82_textbook_numpy_and_act(oracle):
+    rng = np.random.default_rng(35)
+    rows, cols, n = 45, 224, 3
+    q, rs, cf = _rand_q82(rng, rows, cols)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    W = rs.astype(np.float64)[:, None] * cf.astype(np.float64)[None, :] * q
+    ref = X.astype(np.float64) @ W.T
+    np.testing.assert_allclose(oracle.dequant_q82(q, rs, cf), W, rtol=0, atol=0)
+    np.testing.assert_allclose(oracle.gemm_q82(q, rs, cf, X), ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.gemm_q82(q, rs, cf, X, act=1), np.maximum(ref, 0) ** 2,
+                               rtol=1e-12, atol=1e-13)
+
+
 def test_relu2_closed_form(oracle):
     """relu^2 on outputs with known values: 3 -> 9, -2 -> 0, 0 -> 0."""
     q = np.zeros((3, 32), np.int8)
