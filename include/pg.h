@@ -144,6 +144,23 @@ int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const float *x, floa
              int32_t act, pg_stream_t stream);
 
 /*
+ * gemv_q82 — the decode product on the pages' own int8 format, q8_2f
+ * (gemma_batch.rs, `q8_2f_mm_r2` doc comment and epilogue; nemotron_prefill.rs,
+ * the q8_2f expert-bank payload): an int8 body, one binary16 scale per row and
+ * one binary16 factor per column (the column field),
+ *     y[r] = act( f16(row_scale[r]) * sum_c q[r][c] * (f16(col_field[c]) * x[c]) ).
+ * The column field multiplies the activation once (f32) before the product, the
+ * row scale the finished f32 sum.
+ *   q [rows][cols] int8 row-major (16-byte aligned), row_scale [rows] and
+ *   col_field [cols] binary16 bits (col_field 8-byte aligned), x [cols] f32
+ *   (16-byte aligned), y [rows] f32 (must not overlap x).  The pages keep the
+ *   three parts in one buffer in this order; here they are separate pointers.
+ * PG_EUNSUPPORTED: cols % 16 != 0, cols > 32768.
+ */
+int gemv_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field, int32_t rows,
+             int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
+
+/*
  * prefill_gemm_q8 — batched prefill product over one pass of n positions,
  * every weight read from HBM once per pass (nemotron_prefill.rs, module doc:
  * up to PB_MAX = 64 positions a pass; gemma_batch.rs, `encode_q82_mm`:

@@ -80,7 +80,8 @@ def _declare(L):
     L.decode_frame_q8_workspace_init.argtypes = [_P, _sz, _P]
     _q8p = ctypes.POINTER(PgQ8)
     L.decode_frame_q8.argtypes = [_q8p, _q8p, _q8p, _q8p, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    L.gemv_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -148,6 +149,48 @@ class Q8Weight:
         _dev(self.bias, torch.float32, name + ".bias")
         if self.scale.shape != self.q.shape[:-1] + (self.q.shape[-1] // 32,) or self.bias.shape != self.scale.shape:
             raise ValueError(f"{name}: scale/bias must be [.., rows, cols/32]")
+
+
+@dataclass
+class Q82Weight:
+    """A q8_2f matrix on the device: q int8 [rows, cols], row scales rs float16 [rows],
+    column field cf float16 [cols]."""
+
+    q: torch.Tensor
+    rs: torch.Tensor
+    cf: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.q.shape[1]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.q, self.rs, self.cf))
+
+    def validate(self, name="W"):
+        _dev(self.q, torch.int8, name + ".q")
+        _dev(self.rs, torch.float16, name + ".rs")
+        _dev(self.cf, torch.float16, name + ".cf")
+        if self.q.dim() != 2 or self.rs.shape != (self.rows,) or self.cf.shape != (self.cols,):
+            raise ValueError(f"{name}: q [rows, cols], rs [rows], cf [cols]")
+
+
+def gemv_q82(W: Q82Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):
+    """y = act(rs * (q (cf * x))) for one position on a q8_2f matrix."""
+    W.validate()
+    _dev(x, torch.float32, "x")
+    if x.numel() != W.cols:
+        raise ValueError("x length must equal W.cols")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    _check("gemv_q82", lib().gemv_q82(_ptr(W.q), _ptr(W.rs), _ptr(W.cf), W.rows, W.cols, _ptr(x), _ptr(y),
+                                      act, _stream(stream)))
+    return y
 
 
 def gemv_q8(W: Q8Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):

@@ -336,6 +336,99 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_f16_kernel(
 #define PG_GEMV_U 2
 #endif
 constexpr int kQ8Rw = PG_GEMV_RW, kQ8U = PG_GEMV_U;
+// q8_2f weights (gemma_batch.rs, `q8_2f_mm_r2` doc comment and epilogue): the
+// column field folds into the staged activation, x'[c] = f16(cf[c]) * x[c],
+// the row scale multiplies the finished sum.  Same streaming and batching as
+// gemv_q8_kernel, without per-block factors: a 16-column segment is 16 plain
+// fused multiply-adds of the decoded int8 with x'.
+template <int RW, int U>
+__global__ __launch_bounds__(kGemvThreads) void gemv_q82_kernel(
+    const int8_t *__restrict__ q, const uint16_t *__restrict__ rs, const uint16_t *__restrict__ cf,
+    int rows, int cols, const float *__restrict__ x, float *__restrict__ y, int act) {
+    extern __shared__ float4 sx[];
+    const int nseg = cols >> 4;
+    const int steps = (nseg + 63) >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r0 = (blockIdx.x * kGemvWaves + wave) * RW;
+    const int8_t *qr[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) qr[rr] = q + (long long)min(r0 + rr, rows - 1) * cols;
+    u32x4 wa[U][RW], wb[U][RW];
+    auto load = [&](int i0, u32x4 (&w)[U][RW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u < steps) {
+                const int s = min(lane + 64 * (i0 + u), nseg - 1);
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr)
+                    w[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(qr[rr] + 16 * s));
+            }
+        }
+    };
+    load(0, wa);
+    for (int s = threadIdx.x; s < steps * 64; s += kGemvThreads) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 a = make_float4(0, 0, 0, 0);
+            if (s < nseg) {
+                const float4 v = reinterpret_cast<const float4 *>(x)[4 * s + j];
+                const uint2 h = reinterpret_cast<const uint2 *>(cf)[4 * s + j];  // 4 binary16
+                _Float16 c[4];
+                __builtin_memcpy(c, &h, 8);
+                a = make_float4((float)c[0] * v.x, (float)c[1] * v.y, (float)c[2] * v.z, (float)c[3] * v.w);
+            }
+            sx[xslot<4>(s, j)] = a;
+        }
+    }
+    __syncthreads();
+
+    float acc[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) acc[rr] = 0.0f;
+    auto compute = [&](int i0, const u32x4 (&w)[U][RW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u;
+            if (i < steps) {
+                float xv[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 a = sx[(i * 4 + j) * 64 + lane];
+                    xv[4 * j] = a.x; xv[4 * j + 1] = a.y; xv[4 * j + 2] = a.z; xv[4 * j + 3] = a.w;
+                }
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    float f[16];
+                    q16_to_f32(w[u][rr], f);
+                    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 16; k += 2) {
+                        d0 = fmaf(f[k], xv[k], d0);
+                        d1 = fmaf(f[k + 1], xv[k + 1], d1);
+                    }
+                    acc[rr] += d0 + d1;
+                }
+            }
+        }
+    };
+    for (int i0 = 0; i0 < steps; i0 += 2 * U) {
+        load(i0 + U, wb);
+        compute(i0, wa);
+        load(i0 + 2 * U, wa);
+        compute(i0 + U, wb);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        const int r = r0 + rr;
+        const float v = wave_sum(acc[rr]);
+        if (lane == rr && r < rows) {
+            const _Float16 sr = __builtin_bit_cast(_Float16, rs[r]);
+            y[r] = apply_act(act, (float)sr * v);
+        }
+    }
+}
+
 // f16: one row per wave (4096-column rows: the whole row in one batch of 4 x 2 steps).
 constexpr int kF16Rw = 1, kF16U = 4;
 
@@ -457,6 +550,24 @@ extern "C" int gemv_q8_normed(const int8_t *q, const float *scale, const float *
         return PG_EINVAL;
     const Fuse nm{nullptr, nullptr, nullptr, eps, nullptr, nullptr, const_cast<float *>(parts), nparts};
     return launch_mode<kScaled>(q, scale, bias, rows, cols, xw, y, act, nm, stream);
+}
+
+extern "C" int gemv_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field, int32_t rows,
+                        int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream) {
+    if (!q || !row_scale || !col_field || !x || !y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(x) || ((uintptr_t)col_field & 7) || ((uintptr_t)row_scale & 1))
+        return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 16 || cols > 32768) return PG_EUNSUPPORTED;
+    if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
+    const size_t lds = (size_t)ceil_div(cols / 16, 64) * 4 * 64 * sizeof(float4);
+    static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q82_kernel<kQ8Rw, kQ8U>),
+                                    (size_t)ceil_div(32768 / 16, 64) * 4 * 64 * sizeof(float4));
+    if (ok != PG_OK) return PG_ELAUNCH;
+    hipLaunchKernelGGL((gemv_q82_kernel<kQ8Rw, kQ8U>), dim3(gemv_grid(rows, kQ8Rw)), dim3(kGemvThreads), lds,
+                       as_stream(stream), q, row_scale, col_field, rows, cols, x, y, act);
+    return launch_status();
 }
 
 extern "C" int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const float *x, float *y,
