@@ -6,13 +6,14 @@ A step is one pass of the hot path over one batch of synthetic input:
     residual add + RMSNorm, up 4096->14336 with relu^2, down 14336->4096,
     residual add + RMSNorm, head 4096->32000), and
   * the same frame as one prefill pass over 64 positions.
-Two weight copies (2 x 342 MB, more than the 256 MB Infinity Cache) alternate
-between steps so the weights stream from HBM.  `value` is the decode frame's
+Eight weight copies (8 x 342 MB, more than ten times the 256 MB Infinity
+Cache) rotate between steps so the weights stream from HBM.  `value` is the decode frame's
 weight-stream rate (weight bytes per frame / frame time, GB/s); the prefill
 rate (positions/s) is reported beside it.  After the timed steps (not part of
 ms_per_step) the other workloads are measured: the 1024x1024 GEMV + add +
-RMSNorm, the 4096x4096 f16 GEMV over 16 rotated copies, the 420-position
-prompt as 6 x 64 + 36, and the routed-MoE pass.
+RMSNorm, the 4096x4096 f16 GEMV over 64 rotated copies, the 420-position
+prompt as 6 x 64 + 36, the decode frame as one persistent launch, the
+routed-MoE pass, and the q8_2f GEMVs on the frame's shapes.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -102,46 +103,82 @@ def q8_dev(torch, pg, m):
     return pg.Q8Weight(to_dev(torch, m.q), to_dev(torch, m.scale), to_dev(torch, m.bias))
 
 
-def make_frames(torch, pg, synth, n_list, copies=2):
+# Weight copies a streaming measurement rotates through: two drawn on the host,
+# the rest device clones at other addresses.  8 x 342 MB (2.7 GB) is more than ten
+# times the 256 MB Infinity Cache, so a copy's lines are gone before it comes round
+# again (with two copies, 5% of a frame's time was the cache's).
+COPIES = 8
+
+
+def q8_clone(torch, pg, W):
+    return pg.Q8Weight(W.q.clone(), W.scale.clone(), W.bias.clone())
+
+
+def make_frames(torch, pg, synth, n_list, copies=COPIES, host_copies=2):
     frames = {n: [] for n in n_list}
     nbytes = None
-    for c in range(copies):
+    host = []
+    for c in range(host_copies):
         f = synth.frame_weights(seed=c)
-        W = {k: q8_dev(torch, pg, f[k]) for k in ("qkv", "up", "down", "head")}
-        w1, w2 = to_dev(torch, f["w1"]), to_dev(torch, f["w2"])
-        for n in n_list:
-            frames[n].append(pg.Frame(W["qkv"], W["up"], W["down"], W["head"], w1, w2, f["eps"], n=n))
-        nbytes = sum(w.nbytes() for w in W.values())
+        host.append(({k: q8_dev(torch, pg, f[k]) for k in ("qkv", "up", "down", "head")},
+                     to_dev(torch, f["w1"]), to_dev(torch, f["w2"]), f["eps"]))
         del f
+    for c in range(copies):
+        W0, w1, w2, eps = host[c % host_copies]
+        W = W0 if c < host_copies else {k: q8_clone(torch, pg, v) for k, v in W0.items()}
+        for n in n_list:
+            frames[n].append(pg.Frame(W["qkv"], W["up"], W["down"], W["head"], w1, w2, eps, n=n))
+        nbytes = sum(w.nbytes() for w in W.values())
     return frames, nbytes
 
 
 # ----------------------------------------------------------------- timed step
 
-def run_step(torch, dec, pre, inp, timers):
-    """One decode frame (four GEMV launches back to back: QKV, up with the first
-    add + RMSNorm fused in, down, head with the second) + one 64-position
-    prefill pass; HIP events around each part on torch's current stream."""
-    inp["h1"].copy_(inp["h1_0"])
-    inp["h64"].copy_(inp["h64_0"])
-    stages = dec.stages(inp["x1"], inp["h1"])
-    s = timers["decode"].start()
-    for st in stages:
-        st()
-    timers["decode"].stop(s)
-    s = timers["prefill"].start()
-    pre.run(inp["x64"], inp["h64"])
-    timers["prefill"].stop(s)
+def capture_steps(torch, frames, inp):
+    """Per weight copy, the decode frame (four GEMV launches) and the prefill pass
+    (one prefill_frame_q8 call, five launches) each captured into a HIP graph, so
+    that the timed replays measure the GPU's work and not the host's launch rate."""
+    s = torch.cuda.Stream()
+    graphs = []
+    for dec, pre in zip(frames[1], frames[64]):
+        inp["h1"].copy_(inp["h1_0"])
+        inp["h64"].copy_(inp["h64_0"])
+        for st in dec.stages(inp["x1"], inp["h1"]):   # eager once: kernel attributes, buffers
+            st()
+        pre.run(inp["x64"], inp["h64"])
+        torch.cuda.synchronize()
+        gd, gp = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd, stream=s):
+            for st in dec.stages(inp["x1"], inp["h1"]):
+                st()
+        with torch.cuda.graph(gp, stream=s):
+            pre.run(inp["x64"], inp["h64"])
+        graphs.append((gd, gp))
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_replays(torch, graphs, which, K):
+    """K graph replays back to back (the weight copies in rotation) between one pair
+    of HIP events on torch's current stream: the steady-state time per replay."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        graphs[i % len(graphs)][which].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
 
 
 # ----------------------------------------------------------------- components
 
-def component_f16(torch, pg, synth, reps=100, copies=16):
+def component_f16(torch, pg, synth, reps=100, copies=64, host_copies=16):
     """The f16 GEMV repeated back to back (steady state), over rotated copies so
     that the weights come from HBM; also one call at a time between events."""
-    rng = synth.streams(7, copies + 1)
-    Ws = [to_dev(torch, synth.f16(rng[i], 4096, 4096)) for i in range(copies)]
-    x = to_dev(torch, synth.normal(rng[copies], 4096))
+    rng = synth.streams(7, host_copies + 1)
+    Ws = [to_dev(torch, synth.f16(rng[i], 4096, 4096)) for i in range(host_copies)]
+    Ws += [Ws[i % host_copies].clone() for i in range(host_copies, copies)]
+    x = to_dev(torch, synth.normal(rng[host_copies], 4096))
     y = torch.empty(4096, device="cuda")
     for i in range(copies):
         pg.gemv_f16(Ws[i], x, y)
@@ -163,10 +200,49 @@ def component_f16(torch, pg, synth, reps=100, copies=16):
     torch.cuda.synchronize()
     single = t.total_ms() / reps
     nbytes = 4096 * 4096 * 2
-    return {"workload": "f16 GEMV 4096x4096, 100 back-to-back launches over 16 rotated copies",
+    return {"workload": "f16 GEMV 4096x4096, 100 back-to-back launches over 64 rotated copies (2.1 GB)",
             "us_per_gemv": round(best * 1e3, 3), "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "us_per_isolated_call": round(single * 1e3, 3)}
+
+
+def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
+    """The pages' own int8 format (q8_2f) on the decode frame's four shapes: the four
+    GEMVs back to back, the weights rotating through 8 copies (2.2 GB)."""
+    shapes = [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)]
+    rng = synth.streams(11, host_copies * len(shapes) + len(shapes))
+    Ws = []
+    for c in range(host_copies):
+        row = []
+        for i, (r, k) in enumerate(shapes):
+            m = synth.q82(rng[c * len(shapes) + i], r, k)
+            row.append(pg.Q82Weight(to_dev(torch, m.q), torch.as_tensor(m.rs).cuda(), torch.as_tensor(m.cf).cuda()))
+        Ws.append(row)
+    for c in range(host_copies, copies):
+        Ws.append([pg.Q82Weight(W.q.clone(), W.rs.clone(), W.cf.clone()) for W in Ws[c % host_copies]])
+    xs = [to_dev(torch, synth.normal(rng[host_copies * len(shapes) + i], k)) for i, (r, k) in enumerate(shapes)]
+    ys = [torch.empty(r, device="cuda") for r, k in shapes]
+
+    def chain(c):
+        for W, x, y in zip(Ws[c], xs, ys):
+            pg.gemv_q82(W, x, y)
+    for c in range(copies):
+        chain(c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        for r in range(reps):
+            chain(r % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    nbytes = sum(W.nbytes() for W in Ws[0])
+    return {"workload": "q8_2f GEMVs on the decode frame's shapes (QKV, up, down, head), back to back",
+            "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
+            "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def component_gemv_norm(torch, pg, synth, reps=200):
@@ -214,8 +290,8 @@ def component_prompt(torch, frames, inp, reps=3):
     for r in range(reps):
         s = t.start()
         for p in range(6):
-            frames[64][p % 2].run(inp["x64"], inp["h64"])
-        frames[36][r % 2].run(x36, h36)
+            frames[64][(7 * r + p) % len(frames[64])].run(inp["x64"], inp["h64"])
+        frames[36][(7 * r + 6) % len(frames[36])].run(x36, h36)
         t.stop(s)
     torch.cuda.synchronize()
     ms = t.total_ms() / reps
@@ -232,6 +308,9 @@ def component_decode_single_launch(torch, pg, synth, reps=40):
         Ws.append(({k: q8_dev(torch, pg, f[k]) for k in ("qkv", "up", "down", "head")},
                    to_dev(torch, f["w1"]), to_dev(torch, f["w2"]), f["eps"]))
         del f
+    for c in range(2, COPIES):
+        W, w1, w2, eps = Ws[c % 2]
+        Ws.append(({k: q8_clone(torch, pg, v) for k, v in W.items()}, w1, w2, eps))
     W0 = Ws[0][0]
     H, I = W0["qkv"].cols, W0["up"].rows
     out = {"qkv": torch.empty(W0["qkv"].rows, device="cuda"), "u": torch.empty(I, device="cuda"),
@@ -247,25 +326,25 @@ def component_decode_single_launch(torch, pg, synth, reps=40):
 
     graphs = []
     s = torch.cuda.Stream()
-    for c in range(2):
+    for c in range(len(Ws)):
         call(c)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             call(c)
         graphs.append(g)
-    for i in range(4):
-        graphs[i % 2].replay()
+    for i in range(len(graphs)):
+        graphs[i].replay()
     t = Timer(torch)
     torch.cuda.synchronize()
     s0 = t.start()
     for i in range(reps):
-        graphs[i % 2].replay()
+        graphs[i % len(graphs)].replay()
     t.stop(s0)
     torch.cuda.synchronize()
     us = t.total_ms() / reps * 1e3
     nbytes = sum(w.nbytes() for w in W0.values())
-    return {"workload": "q8 decode frame (hidden 4096) as one persistent launch, graph replays over 2 weight copies",
+    return {"workload": "q8 decode frame (hidden 4096) as one persistent launch, graph replays over 8 weight copies",
             "us_per_frame": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "barrier_timeouts": pg.decode_frame_timeouts(ws)}
 
@@ -361,24 +440,20 @@ def main():
     inp["h1"] = inp["h1_0"].clone()
     inp["h64"] = inp["h64_0"].clone()
 
+    log("capturing graphs ...")
+    graphs = capture_steps(torch, frames, inp)
     log(f"warmup {args.warmup} steps ...")
-    for i in range(args.warmup):
-        run_step(torch, frames[1][i % 2], frames[64][i % 2], inp,
-                 {"decode": Timer(torch), "prefill": Timer(torch)})
-    torch.cuda.synchronize()
-
+    for which in (0, 1):
+        time_replays(torch, graphs, which, args.warmup)
     log(f"timing {args.steps} steps ...")
-    timers = {"decode": Timer(torch), "prefill": Timer(torch)}
+    inp["h1"].copy_(inp["h1_0"])
+    inp["h64"].copy_(inp["h64_0"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(torch, frames[1][i % 2], frames[64][i % 2], inp, timers)
-    torch.cuda.synchronize()
+    dec_ms = time_replays(torch, graphs, 0, args.steps)
+    pre_ms = time_replays(torch, graphs, 1, args.steps)
     wall = time.perf_counter() - t0
-
     K = args.steps
-    dec_ms = timers["decode"].total_ms() / K
-    pre_ms = timers["prefill"].total_ms() / K
     gemv_avg_ms = dec_ms / 4           # the decode frame is four GEMV launches back to back
     gemv_bytes_per_launch = frame_bytes / 4
     achieved = gemv_bytes_per_launch / (gemv_avg_ms * 1e-3) / 1e9
@@ -401,7 +476,7 @@ def main():
         "data": "synthetic (seeded numpy: q8 U[-127,127], scale U(1e-3,1e-2), bias N(0,1e-3); x,h N(0,1))",
         "config": {"workload": "q8 layer frame, hidden 4096 (QKV 6144, up 14336 relu^2, down, head 32000, "
                                "2x add+RMSNorm): decode at 1 position + prefill pass at 64 positions",
-                   "decode_batch": 1, "prefill_batch": 64, "weight_copies_rotated": 2,
+                   "decode_batch": 1, "prefill_batch": 64, "weight_copies_rotated": COPIES,
                    "frame_weight_bytes": frame_bytes},
         "decode_frame_us": round(dec_ms * 1e3, 2),
         "decode_tokens_per_s": round(1.0 / (dec_ms * 1e-3), 1),
@@ -421,11 +496,13 @@ def main():
         comp = {"gemv_add_norm_1024": component_gemv_norm(torch, pg, synth),
                 "f16_gemv_4096": component_f16(torch, pg, synth),
                 "prompt_420": component_prompt(torch, frames, inp)}
-        del frames
+        del frames, graphs
         torch.cuda.empty_cache()
         comp["decode_frame_single_launch"] = component_decode_single_launch(torch, pg, synth)
         torch.cuda.empty_cache()
         comp["moe_pass"] = component_moe(torch, pg, synth)
+        torch.cuda.empty_cache()
+        comp["q82_gemv_frame_shapes"] = component_q82(torch, pg, synth)
         result["components"] = comp
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
