@@ -239,10 +239,36 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
         torch.cuda.synchronize()
         best = min(best, e0.elapsed_time(e1) / reps)
     nbytes = sum(W.nbytes() for W in Ws[0])
+
+    # The same four products over a pass of 64 positions (prefill_gemm_q82).
+    n = 64
+    Xs = [to_dev(torch, synth.normal(rng[host_copies * len(shapes) + i], (n, k))) for i, (r, k) in enumerate(shapes)]
+    Ys = [torch.empty(n, r, device="cuda") for r, k in shapes]
+    wss = [torch.empty(pg.prefill_gemm_q8_workspace_bytes(r, k, n), dtype=torch.uint8, device="cuda")
+           for r, k in shapes]
+
+    def pchain(c):
+        for W, X, Y, ws in zip(Ws[c], Xs, Ys, wss):
+            pg.prefill_gemm_q82(W, X, Y, workspace=ws)
+    for c in range(copies):
+        pchain(c)
+    torch.cuda.synchronize()
+    pbest = float("inf")
+    for _ in range(3):
+        e0.record()
+        for r in range(reps):
+            pchain(r % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        pbest = min(pbest, e0.elapsed_time(e1) / reps)
+    flops = 2.0 * n * sum(r * k for r, k in shapes)
     return {"workload": "q8_2f GEMVs on the decode frame's shapes (QKV, up, down, head), back to back",
             "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
             "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill64_us_per_frame": round(pbest * 1e3, 2),
+            "prefill64_weight_GB_s": round(nbytes / (pbest * 1e-3) / 1e9, 1),
+            "prefill64_TFLOP_s": round(flops / (pbest * 1e-3) / 1e12, 1)}
 
 
 def component_gemv_norm(torch, pg, synth, reps=200):

@@ -184,6 +184,27 @@ int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias, int3
 size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n);
 
 /*
+ * prefill_gemm_q82 — the batched prefill product on the q8_2f format
+ * (gemma_batch.rs, `encode_q82_mm` and the `q8_2f_mm_r2` epilogue: the column
+ * field scales the activation, the row scale the finished dot product):
+ *     Y[b][r] = act( f16(row_scale[r]) * sum_c q[r][c] * (f16(col_field[c]) * X[b][c]) ),
+ *     b < n, r < rows.
+ *   q [rows][cols] int8 row-major (16-byte aligned); row_scale [rows] and
+ *   col_field [cols] binary16 bits; X [n][cols] f32; Y [n][rows] f32 (must not
+ *   overlap X or the workspace); workspace as prefill_gemm_q8
+ *   (prefill_gemm_q8_workspace_bytes(rows, cols, n), contents on entry do not
+ *   matter).
+ * Arithmetic: f16(col_field[c]) * X[b][c] is formed in f32 and enters the
+ * matrix cores as an exact-to-2^-17 bf16 hi+lo pair, the int8 body as exact
+ * bf16 integers; the products accumulate in f32 (split partials added in split
+ * order) and the row scale multiplies the f32 total.
+ * PG_EUNSUPPORTED: cols % 32 != 0, n < 1 or n > 64.
+ */
+int prefill_gemm_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field,
+                     int32_t rows, int32_t cols, const float *X, int32_t n, float *Y, int32_t act,
+                     void *workspace, size_t workspace_bytes, pg_stream_t stream);
+
+/*
  * prefill_gemm_q8_addnorm — prefill_gemm_q8 on rmsnorm(H + delta) * w, the
  * add + norm done per position while the activations are staged for the
  * matrix cores (nemotron_prefill.rs `pb_add_rms`, add = 1, then the product):

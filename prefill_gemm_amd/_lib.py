@@ -81,7 +81,8 @@ def _declare(L):
     _q8p = ctypes.POINTER(PgQ8)
     L.decode_frame_q8.argtypes = [_q8p, _q8p, _q8p, _q8p, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     L.gemv_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -328,6 +329,27 @@ def prefill_gemm_q8(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor | None = None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
     _check("prefill_gemm_q8", lib().prefill_gemm_q8(
         _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return Y
+
+
+def prefill_gemm_q82(W: Q82Weight, X: torch.Tensor, Y: torch.Tensor | None = None, act: int = 0,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """Y [n][rows] = act(rs * ((cf * X) [n][cols] . q^T)) for one pass of n <= 64 positions
+    on a q8_2f matrix; the workspace is sized as for prefill_gemm_q8."""
+    W.validate()
+    _dev(X, torch.float32, "X")
+    n = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != W.cols:
+        raise ValueError("X must be [n][W.cols]")
+    if Y is None:
+        Y = torch.empty(n, W.rows, dtype=torch.float32, device=X.device)
+    _dev(Y, torch.float32, "Y")
+    need = prefill_gemm_q8_workspace_bytes(W.rows, W.cols, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check("prefill_gemm_q82", lib().prefill_gemm_q82(
+        _ptr(W.q), _ptr(W.rs), _ptr(W.cf), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return Y
 

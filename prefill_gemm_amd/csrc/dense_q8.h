@@ -75,6 +75,7 @@ struct DenseArgs {
     const int8_t *q;
     const float *scale;
     const float *bias;
+    const uint16_t *rs;  // q8_2f variant: binary16 row scales (scale and bias unused)
     int rows, cols;
     const u32x4 *xp;  // staged A fragments [nb][mts][4][64] (see stage_x_frag_kernel)
     const u32x4 *xs;  // staged block sums [ng][mts][2][64]
@@ -237,7 +238,7 @@ __device__ __forceinline__ int wq_slot(int row, int s) {
 // position m = t / 8 and the 16 rows 16 (t % 8) .. of the panel (threads 2i,
 // 2i + 1 hold the two halves of one 32-row block of the next product's
 // columns).
-template <int MT, int NK, int NX, int NW>
+template <int MT, int NK, int NX, int NW, bool Q82 = false>
 __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_base, u32x4 *lds) {
     using C = DenseCfg<MT, NK, NX, NW>;
     static_assert(C::kThreads == 512, "one thread per (position, 16 rows) of a 64 x 128 tile");
@@ -356,6 +357,14 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
         }
     };
     if (P.mode == kDensePlain) {
+        if (Q82) {
+            // q8_2f: the row scale multiplies the finished sum.
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = min(r0 + i, P.rows - 1);
+                v[i] *= (float)__builtin_bit_cast(_Float16, P.rs[r]);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = apply_act(P.act, v[i]);
         store16(v);
@@ -397,7 +406,7 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
     if ((t & 7) == 0 && r_base < P.hidden && m < P.n) P.sumsq[panel * P.n + m] = sq;
 }
 
-template <int MT, int NK, int NX, int NW>
+template <int MT, int NK, int NX, int NW, bool Q82 = false>
 __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base, const int kb0,
                                             const int kb1, u32x4 *lds) {
     using C = DenseCfg<MT, NK, NX, NW>;
@@ -415,8 +424,10 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // Copies for stages past the range go through empty resources: they
     // return zeros at once and move no memory.
     const i32x4 rq = buf_rsrc(P.q, (uint32_t)P.rows * (uint32_t)P.cols);
-    const i32x4 rs = buf_rsrc(P.scale, (uint32_t)P.rows * nb * 4u);
-    const i32x4 rb = buf_rsrc(P.bias, (uint32_t)P.rows * nb * 4u);
+    // q8_2f: no block scales or biases; their copies go through empty
+    // resources (zeros, no memory traffic), so every count of copies stays.
+    const i32x4 rs = buf_rsrc(P.scale, Q82 ? 0u : (uint32_t)P.rows * nb * 4u);
+    const i32x4 rb = buf_rsrc(P.bias, Q82 ? 0u : (uint32_t)P.rows * nb * 4u);
     const i32x4 rx = buf_rsrc(P.xp, (uint32_t)nb * P.mts * 4096u);
     const i32x4 rxs = buf_rsrc(P.xs, (uint32_t)ng * P.mts * 2048u);
     auto live_rsrc = [](i32x4 r, bool live) __attribute__((always_inline)) {
@@ -536,9 +547,30 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         const int row0 = 64 * rh + ml, row1 = row0 + 32;
         const u32x4 q0 = wst[wq_slot(row0, 2 * kbl + h)];
         const u32x4 q1 = wst[wq_slot(row1, 2 * kbl + h)];
+        bf16x8 b00, b01, b10, b11;
+        if constexpr (Q82) {
+            // q8_2f: no block factors, so both tiles accumulate straight into
+            // their sums (blocks past the range meet zero activations).
+            (void)live;
+            q16_to_bf16(q0, b00, b01);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[0][mt] = mfma_bf16(as_bf16x8(a[mt][0]), b00, acc[0][mt]);
+                acc[0][mt] = mfma_bf16(as_bf16x8(a[mt][1]), b01, acc[0][mt]);
+                acc[0][mt] = mfma_bf16(as_bf16x8(a[mt][2]), b00, acc[0][mt]);
+                acc[0][mt] = mfma_bf16(as_bf16x8(a[mt][3]), b01, acc[0][mt]);
+            }
+            q16_to_bf16(q1, b10, b11);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[1][mt] = mfma_bf16(as_bf16x8(a[mt][0]), b10, acc[1][mt]);
+                acc[1][mt] = mfma_bf16(as_bf16x8(a[mt][1]), b11, acc[1][mt]);
+                acc[1][mt] = mfma_bf16(as_bf16x8(a[mt][2]), b10, acc[1][mt]);
+                acc[1][mt] = mfma_bf16(as_bf16x8(a[mt][3]), b11, acc[1][mt]);
+            }
+        } else {
         const float sl0 = sst[4 * row0 + kbl], sl1 = sst[4 * row1 + kbl];
         const float s0 = live ? sl0 : 0.0f;
-        bf16x8 b00, b01, b10, b11;
         q16_to_bf16(q0, b00, b01);
         // tile 0 chain; previous tile 1 scale step; tile 1 weights converted
         f32x16 t0[MT];
@@ -567,6 +599,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[0][mt][v] = fmaf(s0, t0[mt][v], acc[0][mt][v]);
         s1 = live ? sl1 : 0.0f;
+        }
         // Issue order: LDS reads, tile 0's conversion, then each matrix-core
         // instruction followed by a slice of independent vector work.
         __builtin_amdgcn_sched_group_barrier(0x100, 4 * MT + 4, 0);
@@ -583,7 +616,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        if (u == C::kStagesPerGroup - 1 && kq == it % NK) {
+        if (!Q82 && u == C::kStagesPerGroup - 1 && kq == it % NK) {
             // Bias term of the group on one K wave (in turn); zero past kb1.
             const u32x4 *sf = lds + C::kSBase + (it & 1) * C::kSGroup + lane;
             const float *bg = reinterpret_cast<const float *>(lds + C::kBBase + (it & 1) * C::kBGroup);
@@ -616,10 +649,12 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         __builtin_amdgcn_s_barrier();
     }
 
+    if (!Q82) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[1][mt][v] = fmaf(s1, t1[mt][v], acc[1][mt][v]);
+            for (int v = 0; v < 16; ++v) acc[1][mt][v] = fmaf(s1, t1[mt][v], acc[1][mt][v]);
+    }
 
     // ------------------------------------------------------------ epilogue
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing refills
@@ -657,7 +692,9 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
                     if (direct) {
-                        if (r < P.rows && m < P.n) P.out[m * P.ldo + r] = apply_act(P.act, t[v]);
+                        if (r < P.rows && m < P.n)
+                            P.out[m * P.ldo + r] =
+                                apply_act(P.act, Q82 ? t[v] * (float)__builtin_bit_cast(_Float16, P.rs[r]) : t[v]);
                     } else {
                         tile[m * 128 + rl] = t[v];
                     }
@@ -666,7 +703,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         }
     }
     if (direct) return;
-    dense_finish<MT, NK, NX, NW>(P, r_base, lds);
+    dense_finish<MT, NK, NX, NW, Q82>(P, r_base, lds);
 }
 
 }  // namespace pg

@@ -22,7 +22,8 @@ __device__ __forceinline__ void clear_words(unsigned *zero, int nzero) {
 
 __global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
                                                            int cols, int mts, u32x4 *__restrict__ xp,
-                                                           __bf16 *__restrict__ xs, unsigned *zero, int nzero) {
+                                                           __bf16 *__restrict__ xs, unsigned *zero, int nzero,
+                                                           const uint16_t *__restrict__ cf) {
     clear_words(zero, nzero);
     const int nb = cols >> 5;
     const int ng = (nb + 15) >> 4;
@@ -40,6 +41,12 @@ __global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restri
         for (int j = 0; j < 4; ++j) {
             const float4 a = src[j];
             v[4 * j] = a.x; v[4 * j + 1] = a.y; v[4 * j + 2] = a.z; v[4 * j + 3] = a.w;
+        }
+        if (cf) {
+            // q8_2f: the column field folds into the staged activation.
+            const uint16_t *c = cf + 32 * blk + 16 * h;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] *= (float)__builtin_bit_cast(_Float16, c[i]);
         }
     } else {
 #pragma unroll
@@ -130,7 +137,7 @@ constexpr int kDNK = PG_DENSE_NK, kDNX = PG_DENSE_NX, kDNW = PG_DENSE_NW;
 template <int MT>
 using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
 
-template <int MT>
+template <int MT, bool Q82>
 __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int bps) {
     extern __shared__ u32x4 dlds[];
     const int id = blockIdx.x;
@@ -139,16 +146,16 @@ __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, 
     const int kb0 = split * bps;
     const int kb1 = min(nb, kb0 + bps);
     P.split = split;
-    dense_panel<MT, kDNK, kDNX, kDNW>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
+    dense_panel<MT, kDNK, kDNX, kDNW, Q82>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
 }
 
-template <int MT>
+template <int MT, bool Q82>
 static int launch_dense(const DenseArgs &P, int grid, int bps, hipStream_t s) {
     constexpr size_t lds = (size_t)DCfg<MT>::kLdsU4 * sizeof(u32x4);
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT, Q82>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL(dense_kernel<MT>, dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
+    hipLaunchKernelGGL((dense_kernel<MT, Q82>), dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
     return launch_status();
 }
 
@@ -216,19 +223,21 @@ static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
 }
 
 static int launch_stage_frag(const float *X, int n, int cols, void *xp, void *xs, unsigned *zero, int nzero,
-                             hipStream_t s) {
+                             hipStream_t s, const uint16_t *cf = nullptr) {
     const int mts = ceil_div(n, 32);
     const int nb = cols / 32, ng = (nb + 15) / 16;
     const long long threads = (long long)mts * 32 * ng * 32;
     hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, X, n, cols,
-                       mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), zero, nzero);
+                       mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), zero, nzero, cf);
     return launch_status();
 }
 
 // The dense pass over one product whose activations are staged at (xp, xs);
 // the epilogue fields of P are the caller's.  Split partials and tickets at
-// (parts, tickets); the tickets must be zero.
-static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, unsigned *tickets, hipStream_t s) {
+// (parts, tickets); the tickets must be zero.  q82: the weight is in the q8_2f
+// format (P.rs row scales; the column field is already in the staged activations).
+static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, unsigned *tickets, hipStream_t s,
+                     bool q82 = false) {
     P.xp = reinterpret_cast<const u32x4 *>(xp);
     P.xs = reinterpret_cast<const u32x4 *>(xs);
     P.mts = ceil_div(P.n, 32);
@@ -238,7 +247,8 @@ static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, 
     P.parts = parts;
     P.tickets = tickets;
     const int grid = dense_panels(P.rows) * P.splits;
-    return P.mts == 2 ? launch_dense<2>(P, grid, bps, s) : launch_dense<1>(P, grid, bps, s);
+    if (q82) return P.mts == 2 ? launch_dense<2, true>(P, grid, bps, s) : launch_dense<1, true>(P, grid, bps, s);
+    return P.mts == 2 ? launch_dense<2, false>(P, grid, bps, s) : launch_dense<1, false>(P, grid, bps, s);
 }
 
 // Staging (plain or normed) into the workspace, then the dense matrix-core pass
@@ -321,6 +331,42 @@ extern "C" int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, cons
         return PG_EINVAL;
     const StageNorm nm{H, delta, delta_stride, w, eps, H_out, X_out};
     return prefill_run(q, scale, bias, rows, cols, nullptr, &nm, n, Y, act, workspace, as_stream(stream));
+}
+
+// q8_2f prefill product (gemma_batch.rs, `encode_q82_mm`): the column field
+// multiplies the activations as they are staged, the int8 body goes through the
+// same matrix-core pass as the block format, and the f16 row scale multiplies
+// each finished dot product.  The workspace is the block format's.
+extern "C" int prefill_gemm_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field,
+                                int32_t rows, int32_t cols, const float *X, int32_t n, float *Y, int32_t act,
+                                void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+    if (!q || !row_scale || !col_field || !X || !Y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || n <= 0) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(X) || !aligned16(Y)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || n > 64) return PG_EUNSUPPORTED;
+    const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
+    const size_t yb = (size_t)n * rows * sizeof(float);
+    if (overlaps(Y, yb, workspace, need)) return PG_EINVAL;
+    hipStream_t s = as_stream(stream);
+    char *ws = static_cast<char *>(workspace);
+    const OneLayout L = one_layout(rows, cols, n);
+    void *xp = ws, *xs = ws + L.xs;
+    unsigned *tickets = reinterpret_cast<unsigned *>(ws + L.tickets);
+    int rc = launch_stage_frag(X, n, cols, xp, xs, tickets, dense_panels(rows), s, col_field);
+    if (rc) return rc;
+    DenseArgs P{};
+    P.q = q;
+    P.rs = row_scale;
+    P.rows = rows;
+    P.cols = cols;
+    P.n = n;
+    P.out = Y;
+    P.ldo = rows;
+    P.act = act;
+    P.mode = kDensePlain;
+    return run_dense(P, xp, xs, reinterpret_cast<float *>(ws + L.parts), tickets, s, true);
 }
 
 // ---------------------------------------------------------------- prefill frame

@@ -85,3 +85,91 @@ def test_gemv_q82_errors(pg):
     assert call(xp=P(x, 4)) == pg.PG_EINVAL               # misaligned x
     assert call(cfp=P(cf, 2)) == pg.PG_EINVAL             # column field not 8-byte aligned
     assert L.gemv_q82(None, P(rs), P(cf), 64, 1024, P(x), P(y), 0, s) == pg.PG_EINVAL
+
+
+# ------------------------------------------------------------------ prefill_gemm_q82
+
+@pytest.mark.parametrize("rows,cols,n", [(128, 512, 1), (300, 1056, 33), (37, 96, 64), (1000, 4096, 64),
+                                         (4096, 1024, 17), (2048, 14336, 64)])
+@pytest.mark.parametrize("act", [0, 1])
+def test_prefill_q82_parity(pg, oracle, rows, cols, n, act):
+    _case(f"prefill_gemm_q82 n={n} {rows}x{cols} act={act}")
+    rng = np.random.default_rng(rows * 7 + cols + n + act)
+    m = synth.q82(rng, rows, cols)
+    X = synth.normal(rng, (n, cols))
+    Y = pg.prefill_gemm_q82(_dev_q82(pg, m), to_dev(X, torch), act=act)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_q82(m.q, m.rs, m.cf, X, act=act)
+    err = oracle.rel_err(Y.cpu().numpy(), ref)
+    print(f"[info] rel err {err:.2e}", flush=True)
+    assert err <= TOL_Q8
+
+
+@pytest.mark.parametrize("rows,cols", [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)])
+def test_prefill_q82_frame_shapes_sampled(pg, oracle, rows, cols):
+    """The layer frame's shapes at 64 positions, checked on 96 sampled rows of every position."""
+    _case(f"prefill_gemm_q82 sampled {rows}x{cols}")
+    rng = np.random.default_rng(rows ^ cols)
+    m = synth.q82(rng, rows, cols)
+    X = synth.normal(rng, (64, cols))
+    Y = pg.prefill_gemm_q82(_dev_q82(pg, m), to_dev(X, torch)).cpu().numpy()
+    idx = np.unique(np.concatenate([rng.choice(rows, 94, replace=False), [0, rows - 1]]))
+    ref = oracle.gemm_q82(m.q[idx], m.rs[idx], m.cf, X)
+    assert oracle.rel_err(Y[:, idx], ref) <= TOL_Q8
+
+
+@pytest.mark.parametrize("rows,cols,n", [(300, 2048, 64), (4096, 4096, 5)])
+def test_prefill_q82_exact_bitwise(pg, oracle, rows, cols, n):
+    """Power-of-two scales, integer activations: every step is exact, the K splits included."""
+    _case(f"prefill_gemm_q82 exact n={n} {rows}x{cols}")
+    rng = np.random.default_rng(11 + n)
+    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
+    cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
+    X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
+    Y = pg.prefill_gemm_q82(_dev_q82(pg, synth.Q82(q, rs, cf)), to_dev(X, torch))
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), oracle.gemm_q82(q, rs, cf, X))
+
+
+def test_prefill_q82_rows_match_gemv(pg):
+    """Each position of the prefill product agrees with the decode product on that row."""
+    _case("prefill_gemm_q82 vs gemv_q82")
+    rng = np.random.default_rng(3)
+    m = synth.q82(rng, 2048, 4096)
+    W = _dev_q82(pg, m)
+    X = to_dev(synth.normal(rng, (9, 4096)), torch)
+    Y = pg.prefill_gemm_q82(W, X)
+    for b in range(9):
+        g = pg.gemv_q82(W, X[b].contiguous())
+        assert float((Y[b] - g).abs().max() / g.pow(2).mean().sqrt()) <= 2 * TOL_Q8
+
+
+def test_prefill_q82_errors(pg):
+    _case("prefill_gemm_q82 errors")
+    L = pg.lib()
+    rows, cols = 64, 1024
+    q = torch.zeros(rows * cols, dtype=torch.int8, device="cuda")
+    rs = torch.zeros(rows, dtype=torch.float16, device="cuda")
+    cf = torch.zeros(cols, dtype=torch.float16, device="cuda")
+    X = torch.zeros(64 * cols, device="cuda")
+    Y = torch.zeros(65 * rows, device="cuda")
+    need = pg.prefill_gemm_q8_workspace_bytes(rows, cols, 64)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+
+    def call(rows=rows, cols=cols, n=64, qp=None, xp=None, act=0, wsb=need):
+        return L.prefill_gemm_q82(qp or P(q), P(rs), P(cf), rows, cols, xp or P(X), n, P(Y), act,
+                                  P(ws), wsb, s)
+
+    assert call() == pg.PG_OK
+    torch.cuda.synchronize()
+    assert call(n=65) == pg.PG_EUNSUPPORTED
+    assert call(cols=1000) == pg.PG_EUNSUPPORTED
+    assert call(n=0) == pg.PG_EINVAL
+    assert call(act=3) == pg.PG_EINVAL
+    assert call(qp=P(q, 4)) == pg.PG_EINVAL
+    assert call(xp=P(X, 4)) == pg.PG_EINVAL
+    assert call(wsb=need - 1) == pg.PG_EWORKSPACE
+    assert L.prefill_gemm_q82(P(q), None, P(cf), rows, cols, P(X), 64, P(Y), 0, P(ws), need, s) == pg.PG_EINVAL
