@@ -56,6 +56,9 @@ def _declare(L):
     L.oracle_gemm_f16.argtypes = [_P, _I, _I, _P, _I, _i, _P]
     L.oracle_dequant_q82.argtypes = [_P, _P, _P, _I, _I, _P]
     L.oracle_gemm_q82.argtypes = [_P, _P, _P, _I, _I, _P, _I, _i, _P]
+    L.oracle_dequant_q4tp.argtypes = [_P, _P, _P, _I, _I, _P]
+    L.oracle_gemm_q4tp.argtypes = [_P, _P, _P, _I, _I, _P, _I, _i, _P]
+    L.oracle_argmax_rows.argtypes = [_P, _I, _I, _P]
     L.oracle_add_rmsnorm.argtypes = [_P, _P, _I, _P, _D, _I, _I, _P, _P]
     L.oracle_router_logits_f64.argtypes = [_P, _P, _I, _I, _I, _P]
     L.oracle_router_logits_f32.argtypes = [_P, _P, _I, _I, _I, _P]
@@ -156,6 +159,51 @@ def gemm_q82(q, rs, cf, X, act: int = 0) -> np.ndarray:
     Y = np.empty((X.shape[0], rows), np.float64)
     lib().oracle_gemm_q82(_p(q), _p(rb), _p(cb), rows, cols, _p(X), X.shape[0], act, _p(Y))
     return Y[0] if vec else Y
+
+
+def q4tp_code_bytes(cols: int) -> int:
+    """Bytes of 5-bit group codes in one q4tp row (cols / 32 codes, packed)."""
+    return (5 * (cols // 32) + 7) // 8
+
+
+def _q4tp_args(nib, params, codes):
+    nib = _c(nib, np.uint8)
+    rows, half = nib.shape
+    cols = 2 * half
+    params = _c(params, np.uint32)
+    codes = _c(codes, np.uint8)
+    assert cols % 32 == 0 and params.shape == (rows,) and codes.shape == (rows, q4tp_code_bytes(cols))
+    return nib, params, codes, rows, cols
+
+
+def dequant_q4tp(nib, params, codes) -> np.ndarray:
+    """w[r][c] = 2**(base_r + code_{r,c/32} step_r) (nib_r(c) - 8); nib uint8 [rows][cols/2]
+    (column c in the low half of byte c/2 when c is even), params uint32 [rows] (base f16 low
+    half, step f16 high half), codes uint8 [rows][ceil(5 cols/32 / 8)] (5-bit codes, LSB first)."""
+    nib, params, codes, rows, cols = _q4tp_args(nib, params, codes)
+    W = np.empty((rows, cols), np.float64)
+    lib().oracle_dequant_q4tp(_p(nib), _p(params), _p(codes), rows, cols, _p(W))
+    return W
+
+
+def gemm_q4tp(nib, params, codes, X, act: int = 0) -> np.ndarray:
+    """Y[b][r] = act(sum_c w[r][c] X[b][c]) with the q4tp weight of ``dequant_q4tp``."""
+    nib, params, codes, rows, cols = _q4tp_args(nib, params, codes)
+    vec = np.ndim(X) == 1
+    X = _c(np.atleast_2d(X), np.float32)
+    assert X.shape[1] == cols
+    Y = np.empty((X.shape[0], rows), np.float64)
+    lib().oracle_gemm_q4tp(_p(nib), _p(params), _p(codes), rows, cols, _p(X), X.shape[0], act, _p(Y))
+    return Y[0] if vec else Y
+
+
+def argmax_rows(L) -> np.ndarray:
+    """ids[b] = smallest i with L[b][i] the row's largest logit above -3.0e38 (0 if none)."""
+    vec = np.ndim(L) == 1
+    L = _c(np.atleast_2d(L), np.float32)
+    ids = np.empty(L.shape[0], np.uint32)
+    lib().oracle_argmax_rows(_p(L), L.shape[0], L.shape[1], _p(ids))
+    return ids[0] if vec else ids
 
 
 def add_rmsnorm(h, delta, w, eps: float, delta_stride: int | None = None):

@@ -159,6 +159,76 @@ void oracle_gemm_q82(const int8_t *q, const uint16_t *rs, const uint16_t *cf, in
     }
 }
 
+/* The pages' 4-bit format, q4tp (nemotron_prefill.rs, the q4tp expert bank
+ * `pb_q4_bank` and its nibble and code readers).  Per row r:
+ *  - a 4-bit code per column: byte c/2 of the row's nibble bytes holds column
+ *    c in its low half when c is even and in its high half when c is odd; the
+ *    weight integer is that code minus 8 (range -8 .. 7);
+ *  - two binary16 parameters in one 32-bit word: base in the low half, step in
+ *    the high half;
+ *  - a 5-bit log-scale code per 32-column group g, packed least significant
+ *    bit first: the code of g occupies bits 5g .. 5g+4 of the row's code
+ *    bytes (cstride = ceil(5 * cols/32 / 8) bytes a row);
+ *  - the group's scale is 2 ** (base + code * step).
+ * So   w[r][c] = 2 ** (base_r + code_{r, c/32} * step_r) * (nib_r(c) - 8). */
+static double q4tp_weight(const uint8_t *nib, const uint32_t *params, const uint8_t *codes,
+                          int64_t cols, int64_t r, int64_t c) {
+    const int64_t gpr = cols / 32, cstride = (5 * gpr + 7) / 8;
+    const uint8_t *cr = codes + r * cstride;
+    const int64_t bit = 5 * (c / 32);
+    unsigned field = 0;
+    for (int i = 0; i < 5; ++i) {
+        const int64_t k = bit + i;
+        field |= (unsigned)((cr[k / 8] >> (k % 8)) & 1u) << i;
+    }
+    const double base = oracle_f16_to_f64((uint16_t)(params[r] & 0xFFFFu));
+    const double step = oracle_f16_to_f64((uint16_t)(params[r] >> 16));
+    const uint8_t byte = nib[r * (cols / 2) + c / 2];
+    const int v = (int)((c % 2 == 0) ? (byte & 0xFu) : (byte >> 4)) - 8;
+    return exp2(base + (double)field * step) * (double)v;
+}
+
+void oracle_dequant_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes,
+                         int64_t rows, int64_t cols, double *w) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) w[r * cols + c] = q4tp_weight(nib, params, codes, cols, r, c);
+}
+
+/* Y[b][r] = act( sum_c w[r][c] * X[b][c] ) with the q4tp weight above. */
+void oracle_gemm_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int64_t rows,
+                      int64_t cols, const float *X, int64_t n, int act, double *Y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * rows; ++i) {
+        int64_t b = i / rows, r = i % rows;
+        double acc = 0.0;
+        for (int64_t c = 0; c < cols; ++c)
+            acc += q4tp_weight(nib, params, codes, cols, r, c) * (double)X[b * cols + c];
+        Y[b * rows + r] = act_apply(act, acc);
+    }
+}
+
+/* ------------------------------------------------------------ argmax */
+
+/* Token choice of every position (nemotron_prefill.rs, `pb_argmax`, the verify
+ * passes): ids[b] is the smallest index i whose logit L[b][i] is the largest
+ * of the row, where only logits above -3.0e38 take part (the search starts
+ * from that value at index 0, so a row with no such logit, or all NaN, gives
+ * 0).  Comparisons are in f32, the logits' own precision. */
+void oracle_argmax_rows(const float *L, int64_t n, int64_t vocab, uint32_t *ids) {
+    for (int64_t b = 0; b < n; ++b) {
+        float best = -3.0e38f;
+        uint32_t at = 0;
+        for (int64_t i = 0; i < vocab; ++i) {
+            const float v = L[b * vocab + i];
+            if (v > best) {
+                best = v;
+                at = (uint32_t)i;
+            }
+        }
+        ids[b] = at;
+    }
+}
+
 /* ------------------------------------------------------------ add + RMSNorm */
 
 /* Per position b:  h'[i] = h[b][i] + delta[b*delta_stride + i]   (no add if delta is NULL)

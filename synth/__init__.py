@@ -75,6 +75,41 @@ def q82(rng: np.random.Generator, rows: int, cols: int) -> Q82:
     return Q82(q, rs, cf)
 
 
+class Q4TP:
+    """A q4tp matrix: nib uint8 [rows][cols/2] (two 4-bit codes a byte), params uint32 [rows]
+    (binary16 base in the low half, step in the high half), codes uint8 [rows][ceil(5 cols/32 / 8)]
+    (one 5-bit log-scale code per 32 columns)."""
+
+    def __init__(self, nib: np.ndarray, params: np.ndarray, codes: np.ndarray):
+        self.nib, self.params, self.codes = nib, params, codes
+
+    @property
+    def rows(self) -> int:
+        return self.nib.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return 2 * self.nib.shape[1]
+
+
+def q4tp(rng: np.random.Generator, rows: int, cols: int) -> Q4TP:
+    """Draw a q4tp matrix: uniform random nibble and code bytes (every 4-bit weight code and
+    5-bit scale code equally likely), base U(-9, -7) and step U(0.05, 0.1) rounded to binary16,
+    so group scales span about 2^-9 .. 2^-4 (the pages fix no distribution)."""
+    assert cols % 32 == 0
+    nib = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    codes = rng.integers(0, 256, size=(rows, (5 * (cols // 32) + 7) // 8), dtype=np.uint8)
+    base = rng.uniform(-9.0, -7.0, rows).astype(np.float16)
+    step = rng.uniform(0.05, 0.1, rows).astype(np.float16)
+    params = base.view(np.uint16).astype(np.uint32) | (step.view(np.uint16).astype(np.uint32) << 16)
+    return Q4TP(nib, params.astype(np.uint32), codes)
+
+
+def logits(rng: np.random.Generator, n: int, vocab: int) -> np.ndarray:
+    """N(0, 4) logits [n][vocab] f32 (a head output's spread)."""
+    return (2.0 * rng.standard_normal((n, vocab))).astype(np.float32)
+
+
 def f16(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
     """N(0, 0.02) weights rounded to binary16 (round to nearest even)."""
     return rng.normal(0.0, 0.02, size=(rows, cols)).astype(np.float16)

@@ -517,3 +517,115 @@ def test_planted_wrong_tie_rule_is_caught(oracle):
     assert sel.tolist() == [[2, 6]]
     flipped = oracle.route(L[:, ::-1].copy(), 2)[0]
     assert (7 - flipped).tolist() != [[2, 6]]   # the mirrored walk prefers the other copy
+
+
+# ------------------------------------------------------------------ q4tp
+
+def _pack_q4tp(v, code, base, step):
+    """Independent packer (the inverse of the decoding): v int [-8, 7] [rows][cols],
+    code int [0, 31] [rows][cols/32], base/step binary16 [rows] -> (nib, params, codes)."""
+    rows, cols = v.shape
+    u = (v + 8).astype(np.uint8)
+    nib = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+    bits = ((code[:, :, None] >> np.arange(5)) & 1).astype(np.uint8).reshape(rows, -1)
+    codes = np.packbits(bits, axis=1, bitorder="little")
+    params = (base.view(np.uint16).astype(np.uint32) | (step.view(np.uint16).astype(np.uint32) << 16))
+    return nib, params.astype(np.uint32), codes
+
+
+def test_q4tp_hand_worked_example(oracle):
+    """One row of two groups worked out by hand: base -2, step 0.5; group 0 code 3 (scale
+    2^-0.5), group 1 code 21 (scale 2^8.5), whose 5 bits straddle the first two code bytes
+    (byte 0 = 3 | 5 << 5 = 163, byte 1 = 21 >> 3 = 2).  Nibble byte 0 = 0x1F holds columns 0
+    (low half, 15 - 8 = 7) and 1 (high half, 1 - 8 = -7); byte 16 = 0x80 holds column 32
+    (0 - 8 = -8) and 33 (8 - 8 = 0); every other byte is 0x88 (weights 0)."""
+    assert oracle.q4tp_code_bytes(64) == 2
+    nib = np.full((1, 32), 0x88, np.uint8)
+    nib[0, 0] = 0x1F
+    nib[0, 16] = 0x80
+    params = np.array([0xC000 | (0x3800 << 16)], np.uint32)   # f16 -2.0 low, f16 0.5 high
+    codes = np.array([[163, 2]], np.uint8)
+    W = oracle.dequant_q4tp(nib, params, codes)
+    want = np.zeros((1, 64))
+    want[0, 0], want[0, 1], want[0, 32] = 7 * 2 ** -0.5, -7 * 2 ** -0.5, -8 * 2 ** 8.5
+    np.testing.assert_array_equal(W, want)
+
+
+def test_q4tp_packer_round_trip(oracle):
+    """Random integers, codes and parameters packed by the test's own packer decode to
+    scale * integer, element by element; a swapped nibble half, a code bit order mistake or a
+    wrong group index fails."""
+    rng = np.random.default_rng(41)
+    rows, cols = 7, 160                          # 5 groups: 25 code bits, 4 bytes a row
+    v = rng.integers(-8, 8, size=(rows, cols))
+    code = rng.integers(0, 32, size=(rows, cols // 32))
+    base = rng.uniform(-12, -4, rows).astype(np.float16)
+    step = rng.uniform(0.05, 0.4, rows).astype(np.float16)
+    W = oracle.dequant_q4tp(*_pack_q4tp(v, code, base, step))
+    scale = np.exp2(base.astype(np.float64)[:, None] + code * step.astype(np.float64)[:, None])
+    np.testing.assert_allclose(W, np.repeat(scale, 32, axis=1) * v, rtol=1e-15, atol=0)
+
+
+def test_gemm_q4tp_equals_block_format(oracle):
+    """Integer base and step make every group scale a power of two (exact in f32): q4tp is then
+    the block format with q = nib - 8, that scale per 32-column block and zero bias, and the two
+    oracles agree."""
+    rng = np.random.default_rng(42)
+    rows, cols, n = 33, 256, 3
+    v = rng.integers(-8, 8, size=(rows, cols))
+    code = rng.integers(0, 32, size=(rows, cols // 32))
+    base = rng.integers(-20, -8, rows).astype(np.float16)
+    step = np.ones(rows, np.float16)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    s = np.exp2(base.astype(np.float64)[:, None] + code).astype(np.float32)
+    ref = oracle.gemm_q8(v.astype(np.int8), s, np.zeros_like(s), X)
+    np.testing.assert_allclose(oracle.gemm_q4tp(*_pack_q4tp(v, code, base, step), X), ref,
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_gemm_q4tp_textbook_numpy_and_act(oracle):
+    rng = np.random.default_rng(43)
+    rows, cols, n = 21, 96, 4
+    v = rng.integers(-8, 8, size=(rows, cols))
+    code = rng.integers(0, 32, size=(rows, cols // 32))
+    base = rng.uniform(-10, -6, rows).astype(np.float16)
+    step = rng.uniform(0.1, 0.3, rows).astype(np.float16)
+    X = rng.standard_normal((n, cols)).astype(np.float32)
+    W = np.repeat(np.exp2(base.astype(np.float64)[:, None] + code * step.astype(np.float64)[:, None]), 32, 1) * v
+    ref = X.astype(np.float64) @ W.T
+    packed = _pack_q4tp(v, code, base, step)
+    np.testing.assert_allclose(oracle.gemm_q4tp(*packed, X), ref, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(oracle.gemm_q4tp(*packed, X, act=1), np.maximum(ref, 0) ** 2,
+                               rtol=1e-12, atol=1e-20)
+
+
+# ------------------------------------------------------------------ argmax
+
+def test_argmax_matches_numpy_first_occurrence(oracle):
+    """Finite logits: numpy's argmax (first index of the maximum), with ties planted."""
+    rng = np.random.default_rng(51)
+    L = rng.standard_normal((40, 1000)).astype(np.float32)
+    for b in range(0, 40, 3):                    # duplicate each chosen row's maximum later on
+        m = L[b].max()
+        L[b, rng.choice(1000, 3, replace=False)] = m
+    np.testing.assert_array_equal(oracle.argmax_rows(L), np.argmax(L, axis=1))
+
+
+def test_argmax_nan_and_floor(oracle):
+    """NaN never wins (numpy's nanargmax); a logit must exceed -3.0e38 to be chosen, so rows
+    of -inf, of values at or below -3.0e38, or of NaN give 0."""
+    rng = np.random.default_rng(52)
+    L = rng.standard_normal((6, 64)).astype(np.float32)
+    L[0, ::5] = np.nan
+    L[1, :] = -np.inf
+    L[2, :] = np.float32(-3.0e38)
+    L[3, :] = np.nan
+    L[4, :] = -np.inf
+    L[4, 17] = np.float32(-3.05e38)
+    L[5, :] = -np.inf
+    L[5, 40] = np.float32(-2.9e38)
+    ids = oracle.argmax_rows(L)
+    assert ids[0] == np.nanargmax(L[0])
+    assert list(ids[1:]) == [0, 0, 0, 0, 40]
+    row = np.array([-np.inf, 5, np.nan, 5, 4], np.float32)
+    assert oracle.argmax_rows(row) == 1
