@@ -271,6 +271,57 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
             "prefill64_TFLOP_s": round(flops / (pbest * 1e-3) / 1e12, 1)}
 
 
+def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
+    """The pages' 4-bit format (q4tp) on the decode frame's four shapes, back to back over
+    eight rotated copies; and the per-position argmax over a 64 x 32000 head output."""
+    import numpy as np
+    shapes = [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)]
+    rng = synth.streams(13, host_copies * len(shapes) + len(shapes) + 1)
+    dev = lambda m: pg.Q4TPWeight(to_dev(torch, m.nib), to_dev(torch, m.params.view(np.int32)),
+                                  to_dev(torch, m.codes))
+    Ws = [[dev(synth.q4tp(rng[c * len(shapes) + i], r, k)) for i, (r, k) in enumerate(shapes)]
+          for c in range(host_copies)]
+    for c in range(host_copies, copies):
+        Ws.append([pg.Q4TPWeight(W.nib.clone(), W.params.clone(), W.codes.clone()) for W in Ws[c % host_copies]])
+    xs = [to_dev(torch, synth.normal(rng[host_copies * len(shapes) + i], k)) for i, (r, k) in enumerate(shapes)]
+    ys = [torch.empty(r, device="cuda") for r, k in shapes]
+
+    def chain(c):
+        for W, x, y in zip(Ws[c], xs, ys):
+            pg.gemv_q4tp(W, x, y)
+    for c in range(copies):
+        chain(c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        e0.record()
+        for r in range(reps):
+            chain(r % copies)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    nbytes = sum(W.nbytes() for W in Ws[0])
+
+    L = to_dev(torch, synth.logits(rng[-1], 64, 32000))
+    ids = torch.empty(64, dtype=torch.int32, device="cuda")
+    for _ in range(5):
+        pg.argmax_rows(L, ids)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(200):
+        pg.argmax_rows(L, ids)
+    e1.record()
+    torch.cuda.synchronize()
+    am = e0.elapsed_time(e1) / 200
+    return {"workload": "q4tp GEMVs on the decode frame's shapes (QKV, up, down, head), back to back",
+            "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
+            "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "argmax_64x32000_us": round(am * 1e3, 2),
+            "argmax_GB_s": round(64 * 32000 * 4 / (am * 1e-3) / 1e9, 1)}
+
+
 def component_gemv_norm(torch, pg, synth, reps=200):
     """The small q8 GEMV followed by add + RMSNorm, pairs back to back (steady
     state; the 1.3 MB of weights stay in cache), and one pair at a time."""
@@ -529,6 +580,7 @@ def main():
         comp["moe_pass"] = component_moe(torch, pg, synth)
         torch.cuda.empty_cache()
         comp["q82_gemv_frame_shapes"] = component_q82(torch, pg, synth)
+        comp["q4tp_gemv_frame_shapes"] = component_q4tp_argmax(torch, pg, synth)
         result["components"] = comp
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

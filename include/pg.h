@@ -161,6 +161,38 @@ int gemv_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_fie
              int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
 
 /*
+ * gemv_q4tp — the decode product on the pages' 4-bit format, q4tp
+ * (nemotron_prefill.rs, the q4tp expert bank `pb_q4_bank` and its nibble and
+ * code readers).  Per row r: 4-bit codes, two a byte (column c in the low half
+ * of byte c/2 when c is even, the high half when odd), the weight integer being
+ * the code minus 8; a 32-bit parameter word holding binary16 base (low half)
+ * and step (high half); a 5-bit log-scale code per 32-column group g, least
+ * significant bit first at bit 5g of the row's code bytes:
+ *     y[r] = act( sum_g 2^(base_r + code_{r,g} * step_r) * sum_{c in g} (nib_r(c) - 8) * x[c] ).
+ *   nib [rows][cols/2] bytes (16-byte aligned), params [rows] uint32 (4-byte
+ *   aligned), codes [rows][(5 * cols/32 + 7) / 8] bytes, x [cols] f32 (16-byte
+ *   aligned), y [rows] f32 (must not overlap x).  The pages keep the three
+ *   parts of an expert in one buffer in this order; here they are separate.
+ * Arithmetic: the group scale is exp2 in f32 of base + code * step (exact in
+ * f32); each group's sum is formed in f32 as sum nib * x - 8 * sum x.
+ * PG_EUNSUPPORTED: cols % 32 != 0, cols > 32768.
+ */
+int gemv_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t rows,
+              int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
+
+/*
+ * argmax_rows — the token chosen at each position (nemotron_prefill.rs,
+ * `pb_argmax`, the verify passes):
+ *     ids[b] = the smallest i with logits[b][i] the largest of row b,
+ * counting only logits above -3.0e38 (NaN never counts; a row with no such
+ * logit gives 0).  Comparisons in f32.
+ *   logits [n][vocab] f32 (4-byte aligned; 16-byte alignment and vocab % 4 == 0
+ *   take the vector path), ids [n] uint32 (must not overlap logits).
+ * PG_EINVAL: n < 1, vocab < 1, misaligned or overlapping pointers.
+ */
+int argmax_rows(const float *logits, int32_t n, int32_t vocab, uint32_t *ids, pg_stream_t stream);
+
+/*
  * prefill_gemm_q8 — batched prefill product over one pass of n positions,
  * every weight read from HBM once per pass (nemotron_prefill.rs, module doc:
  * up to PB_MAX = 64 positions a pass; gemma_batch.rs, `encode_q82_mm`:

@@ -82,7 +82,9 @@ def _declare(L):
     L.decode_frame_q8.argtypes = [_q8p, _q8p, _q8p, _q8p, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     L.gemv_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    L.gemv_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
+    L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -192,6 +194,63 @@ def gemv_q82(W: Q82Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: 
     _check("gemv_q82", lib().gemv_q82(_ptr(W.q), _ptr(W.rs), _ptr(W.cf), W.rows, W.cols, _ptr(x), _ptr(y),
                                       act, _stream(stream)))
     return y
+
+
+@dataclass
+class Q4TPWeight:
+    """A q4tp matrix on the device: nib uint8 [rows, cols/2], params int32 [rows] (binary16
+    base low, step high; int32 holds the bits), codes uint8 [rows, ceil(5 cols/32 / 8)]."""
+
+    nib: torch.Tensor
+    params: torch.Tensor
+    codes: torch.Tensor
+
+    @property
+    def rows(self) -> int:
+        return self.nib.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return 2 * self.nib.shape[1]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.nib, self.params, self.codes))
+
+    def validate(self, name="W"):
+        _dev(self.nib, torch.uint8, name + ".nib")
+        _dev(self.params, torch.int32, name + ".params")
+        _dev(self.codes, torch.uint8, name + ".codes")
+        if (self.nib.dim() != 2 or self.params.shape != (self.rows,)
+                or self.codes.shape != (self.rows, (5 * (self.cols // 32) + 7) // 8)):
+            raise ValueError(f"{name}: nib [rows, cols/2], params [rows], codes [rows, ceil(5 cols/32 / 8)]")
+
+
+def gemv_q4tp(W: Q4TPWeight, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):
+    """y = act(W x) for one position on a q4tp matrix."""
+    W.validate()
+    _dev(x, torch.float32, "x")
+    if x.numel() != W.cols:
+        raise ValueError("x length must equal W.cols")
+    if y is None:
+        y = torch.empty(W.rows, dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    _check("gemv_q4tp", lib().gemv_q4tp(_ptr(W.nib), _ptr(W.params), _ptr(W.codes), W.rows, W.cols, _ptr(x),
+                                        _ptr(y), act, _stream(stream)))
+    return y
+
+
+def argmax_rows(logits: torch.Tensor, ids: torch.Tensor | None = None, stream=None):
+    """ids[b] = smallest index of row b's largest logit above -3.0e38 (0 if none); int32 out."""
+    _dev(logits, torch.float32, "logits")
+    L2 = logits.view(1, -1) if logits.dim() == 1 else logits
+    if L2.dim() != 2:
+        raise ValueError("logits must be [n][vocab] or [vocab]")
+    n, vocab = L2.shape
+    if ids is None:
+        ids = torch.empty(n, dtype=torch.int32, device=logits.device)
+    _dev(ids, torch.int32, "ids")
+    _check("argmax_rows", lib().argmax_rows(_ptr(L2), n, vocab, _ptr(ids), _stream(stream)))
+    return ids
 
 
 def gemv_q8(W: Q8Weight, x: torch.Tensor, y: torch.Tensor | None = None, act: int = 0, stream=None):

@@ -432,6 +432,130 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_q82_kernel(
 // f16: one row per wave (4096-column rows: the whole row in one batch of 4 x 2 steps).
 constexpr int kF16Rw = 1, kF16U = 4;
 
+// q4tp weights (nemotron_prefill.rs, the q4tp expert bank `pb_q4_bank`): per
+// row, 4-bit codes two to a byte (column c in the low half of byte c/2 when c
+// is even), the integer weight being code - 8; a binary16 base and step in one
+// 32-bit word; a 5-bit code per 32-column group, least significant bit first,
+// giving the group scale 2^(base + code * step).  A lane's step covers one
+// group: 16 bytes of codes, the group scale from two code bytes, and
+//     acc += scale * (sum_c nib[c] * x[c] - 8 * sum_c x[c]),
+// the "- 8" folded into the group's activation sum (formed once per workgroup
+// while x is staged).  Each 32-bit word's nibbles are split into its even and
+// odd columns with two masks, and every byte becomes f32 in one conversion.
+constexpr int kQ4Rw = 2, kQ4U = 2;
+
+template <int RW, int U>
+__global__ __launch_bounds__(kGemvThreads) void gemv_q4tp_kernel(
+    const uint8_t *__restrict__ nib, const uint32_t *__restrict__ params, const uint8_t *__restrict__ codes,
+    int rows, int cols, const float *__restrict__ x, float *__restrict__ y, int act) {
+    extern __shared__ float4 sx[];
+    const int nseg = cols >> 5;  // groups per row
+    const int steps = (nseg + 63) >> 6;
+    const int cstride = (5 * nseg + 7) >> 3;
+    float *gsum = reinterpret_cast<float *>(sx + steps * 8 * 64);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r0 = (blockIdx.x * kGemvWaves + wave) * RW;
+    const uint8_t *nr[RW];
+    const uint8_t *cr[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        const long long r = min(r0 + rr, rows - 1);
+        nr[rr] = nib + r * (cols >> 1);
+        cr[rr] = codes + r * cstride;
+    }
+    u32x4 wa[U][RW], wb[U][RW];
+    uint32_t ca[U][RW], cb[U][RW];
+    // Weights and the two code bytes of each group, one batch of U steps.
+    auto load = [&](int i0, u32x4 (&w)[U][RW], uint32_t (&c)[U][RW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u < steps) {
+                const int s = min(lane + 64 * (i0 + u), nseg - 1);
+                const int byte = (5 * s) >> 3;
+                const int nxt = min(byte + 1, cstride - 1);
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    w[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(nr[rr] + 16 * s));
+                    c[u][rr] = (uint32_t)cr[rr][byte] | ((uint32_t)cr[rr][nxt] << 8);
+                }
+            }
+        }
+    };
+    load(0, wa, ca);
+    for (int s = threadIdx.x; s < steps * 64; s += kGemvThreads) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float4 a = make_float4(0, 0, 0, 0);
+            if (s < nseg) a = reinterpret_cast<const float4 *>(x)[8 * s + j];
+            sx[xslot<8>(s, j)] = a;
+            t += (a.x + a.y) + (a.z + a.w);
+        }
+        gsum[s] = t;
+    }
+    float base[RW], step[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        const uint32_t p = params[min(r0 + rr, rows - 1)];
+        base[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+        step[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+    }
+    __syncthreads();
+
+    float acc[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) acc[rr] = 0.0f;
+    auto compute = [&](int i0, const u32x4 (&w)[U][RW], const uint32_t (&c)[U][RW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u;
+            if (i < steps) {
+                const int s = lane + 64 * i;
+                float xv[32];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float4 a = sx[(i * 8 + j) * 64 + lane];
+                    xv[4 * j] = a.x; xv[4 * j + 1] = a.y; xv[4 * j + 2] = a.z; xv[4 * j + 3] = a.w;
+                }
+                const float xs8 = 8.0f * gsum[min(s, nseg - 1)];
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    const uint32_t word[4] = {w[u][rr].x, w[u][rr].y, w[u][rr].z, w[u][rr].w};
+                    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint32_t lo = word[k] & 0x0F0F0F0Fu, hi = (word[k] >> 4) & 0x0F0F0F0Fu;
+                        // Keep the two masked words whole so each byte converts with one
+                        // v_cvt_f32_ubyteN instead of an extract and a conversion.
+                        asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            d0 = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b], d0);
+                            d1 = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b + 1], d1);
+                        }
+                    }
+                    const uint32_t code = (c[u][rr] >> ((5 * s) & 7)) & 31u;
+                    // Hardware exp2 (exact at integer exponents; a scale below 2^-126 reads as 0).
+                    const float sc = s < nseg ? __builtin_amdgcn_exp2f(fmaf((float)code, step[rr], base[rr])) : 0.0f;
+                    acc[rr] = fmaf(sc, (d0 + d1) - xs8, acc[rr]);
+                }
+            }
+        }
+    };
+    for (int i0 = 0; i0 < steps; i0 += 2 * U) {
+        load(i0 + U, wb, cb);
+        compute(i0, wa, ca);
+        load(i0 + 2 * U, wa, ca);
+        compute(i0 + U, wb, cb);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        const float v = wave_sum(acc[rr]);
+        if (lane == rr && r0 + rr < rows) y[r0 + rr] = apply_act(act, v);
+    }
+}
+
 static int gemv_grid(int rows, int rw) { return ceil_div(rows, kGemvWaves * rw); }
 
 }  // namespace pg
@@ -567,6 +691,22 @@ extern "C" int gemv_q82(const int8_t *q, const uint16_t *row_scale, const uint16
     if (ok != PG_OK) return PG_ELAUNCH;
     hipLaunchKernelGGL((gemv_q82_kernel<kQ8Rw, kQ8U>), dim3(gemv_grid(rows, kQ8Rw)), dim3(kGemvThreads), lds,
                        as_stream(stream), q, row_scale, col_field, rows, cols, x, y, act);
+    return launch_status();
+}
+
+extern "C" int gemv_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t rows,
+                         int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream) {
+    if (!nib || !params || !codes || !x || !y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0) return PG_EINVAL;
+    if (!aligned16(nib) || !aligned16(x) || ((uintptr_t)params & 3)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
+    if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
+    auto bytes = [](int c) { return (size_t)ceil_div(c / 32, 64) * (8 * 64 * sizeof(float4) + 64 * sizeof(float)); };
+    static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q4tp_kernel<kQ4Rw, kQ4U>), bytes(32768));
+    if (ok != PG_OK) return PG_ELAUNCH;
+    hipLaunchKernelGGL((gemv_q4tp_kernel<kQ4Rw, kQ4U>), dim3(gemv_grid(rows, kQ4Rw)), dim3(kGemvThreads),
+                       bytes(cols), as_stream(stream), nib, params, codes, rows, cols, x, y, act);
     return launch_status();
 }
 
