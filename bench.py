@@ -172,26 +172,46 @@ def time_replays(torch, graphs, which, K):
 
 # ----------------------------------------------------------------- components
 
+def one_graph(torch, fns):
+    """All callables, in order, captured into ONE HIP graph (each run once eagerly first),
+    so that a replay pays one launch for many kernels."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, gs, K, tries=3):
+    """Best of ``tries`` runs of K replays back to back (graphs in rotation): ms per replay."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(tries):
+        e0.record()
+        for i in range(K):
+            gs[i % len(gs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / K)
+    return best
+
+
 def component_f16(torch, pg, synth, reps=100, copies=64, host_copies=16):
-    """The f16 GEMV repeated back to back (steady state), over rotated copies so
-    that the weights come from HBM; also one call at a time between events."""
+    """The f16 GEMV over 64 rotated copies (so that the weights come from HBM), the 64
+    launches captured in one graph and replayed back to back (steady state); also one
+    eager call at a time between events."""
     rng = synth.streams(7, host_copies + 1)
     Ws = [to_dev(torch, synth.f16(rng[i], 4096, 4096)) for i in range(host_copies)]
     Ws += [Ws[i % host_copies].clone() for i in range(host_copies, copies)]
     x = to_dev(torch, synth.normal(rng[host_copies], 4096))
     y = torch.empty(4096, device="cuda")
-    for i in range(copies):
-        pg.gemv_f16(Ws[i], x, y)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = float("inf")
-    for _ in range(3):
-        e0.record()
-        for r in range(reps):
-            pg.gemv_f16(Ws[r % copies], x, y)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1) / reps)
+    best = time_graphs(torch, [one_graph(torch, [lambda i=i: pg.gemv_f16(Ws[i], x, y) for i in range(copies)])],
+                       max(1, reps // copies)) / copies
     t = Timer(torch)
     for r in range(reps):
         s = t.start()
@@ -200,7 +220,7 @@ def component_f16(torch, pg, synth, reps=100, copies=64, host_copies=16):
     torch.cuda.synchronize()
     single = t.total_ms() / reps
     nbytes = 4096 * 4096 * 2
-    return {"workload": "f16 GEMV 4096x4096, 100 back-to-back launches over 64 rotated copies (2.1 GB)",
+    return {"workload": "f16 GEMV 4096x4096, 64 launches over 64 rotated copies (2.1 GB) in one graph, replayed back to back",
             "us_per_gemv": round(best * 1e3, 3), "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "us_per_isolated_call": round(single * 1e3, 3)}
@@ -208,7 +228,8 @@ def component_f16(torch, pg, synth, reps=100, copies=64, host_copies=16):
 
 def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
     """The pages' own int8 format (q8_2f) on the decode frame's four shapes: the four
-    GEMVs back to back, the weights rotating through 8 copies (2.2 GB)."""
+    GEMVs (and, separately, the four prefill products at 64 positions) for each of 8
+    weight copies (2.2 GB) captured in one graph, replayed back to back."""
     shapes = [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)]
     rng = synth.streams(11, host_copies * len(shapes) + len(shapes))
     Ws = []
@@ -226,18 +247,7 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
     def chain(c):
         for W, x, y in zip(Ws[c], xs, ys):
             pg.gemv_q82(W, x, y)
-    for c in range(copies):
-        chain(c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = float("inf")
-    for _ in range(3):
-        e0.record()
-        for r in range(reps):
-            chain(r % copies)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1) / reps)
+    best = time_graphs(torch, [one_graph(torch, [lambda c=c: chain(c) for c in range(copies)])], reps) / copies
     nbytes = sum(W.nbytes() for W in Ws[0])
 
     # The same four products over a pass of 64 positions (prefill_gemm_q82).
@@ -250,17 +260,7 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
     def pchain(c):
         for W, X, Y, ws in zip(Ws[c], Xs, Ys, wss):
             pg.prefill_gemm_q82(W, X, Y, workspace=ws)
-    for c in range(copies):
-        pchain(c)
-    torch.cuda.synchronize()
-    pbest = float("inf")
-    for _ in range(3):
-        e0.record()
-        for r in range(reps):
-            pchain(r % copies)
-        e1.record()
-        torch.cuda.synchronize()
-        pbest = min(pbest, e0.elapsed_time(e1) / reps)
+    pbest = time_graphs(torch, [one_graph(torch, [lambda c=c: pchain(c) for c in range(copies)])], reps) / copies
     flops = 2.0 * n * sum(r * k for r, k in shapes)
     return {"workload": "q8_2f GEMVs on the decode frame's shapes (QKV, up, down, head), back to back",
             "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
@@ -272,8 +272,9 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
 
 
 def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
-    """The pages' 4-bit format (q4tp) on the decode frame's four shapes, back to back over
-    eight rotated copies; and the per-position argmax over a 64 x 32000 head output."""
+    """The pages' 4-bit format (q4tp) on the decode frame's four shapes for each of eight
+    weight copies, captured in one graph and replayed back to back; and the per-position
+    argmax over a 64 x 32000 head output (50 launches in one graph)."""
     import numpy as np
     shapes = [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)]
     rng = synth.streams(13, host_copies * len(shapes) + len(shapes) + 1)
@@ -289,31 +290,12 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
     def chain(c):
         for W, x, y in zip(Ws[c], xs, ys):
             pg.gemv_q4tp(W, x, y)
-    for c in range(copies):
-        chain(c)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = float("inf")
-    for _ in range(3):
-        e0.record()
-        for r in range(reps):
-            chain(r % copies)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1) / reps)
+    best = time_graphs(torch, [one_graph(torch, [lambda c=c: chain(c) for c in range(copies)])], reps) / copies
     nbytes = sum(W.nbytes() for W in Ws[0])
 
     L = to_dev(torch, synth.logits(rng[-1], 64, 32000))
     ids = torch.empty(64, dtype=torch.int32, device="cuda")
-    for _ in range(5):
-        pg.argmax_rows(L, ids)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(200):
-        pg.argmax_rows(L, ids)
-    e1.record()
-    torch.cuda.synchronize()
-    am = e0.elapsed_time(e1) / 200
+    am = time_graphs(torch, [one_graph(torch, [lambda: pg.argmax_rows(L, ids)] * 50)], 10) / 50
     return {"workload": "q4tp GEMVs on the decode frame's shapes (QKV, up, down, head), back to back",
             "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
             "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
@@ -323,26 +305,19 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
 
 
 def component_gemv_norm(torch, pg, synth, reps=200):
-    """The small q8 GEMV followed by add + RMSNorm, pairs back to back (steady
-    state; the 1.3 MB of weights stay in cache), and one pair at a time."""
+    """The small q8 GEMV followed by add + RMSNorm: 50 pairs captured in one graph and
+    replayed (steady state; the 1.3 MB of weights stay in cache), and one eager pair at
+    a time."""
     c = synth.gemv_add_norm(0)
     W = q8_dev(torch, pg, c["W"])
     x, w = to_dev(torch, c["x"]), to_dev(torch, c["w"])
     h = to_dev(torch, c["h"]).view(1, -1)
     y = torch.empty(1024, device="cuda")
     out = torch.empty(1, 1024, device="cuda")
-    for _ in range(5):
+    def pair():
         pg.gemv_q8(W, x, y)
         pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        pg.gemv_q8(W, x, y)
-        pg.add_rmsnorm(h, y.view(1, -1), w, c["eps"], out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    back_to_back = e0.elapsed_time(e1) / reps
+    back_to_back = time_graphs(torch, [one_graph(torch, [pair] * 50)], max(1, reps // 50)) / 50
     t = Timer(torch)
     for _ in range(reps):
         s = t.start()

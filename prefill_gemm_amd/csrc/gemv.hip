@@ -442,121 +442,191 @@ constexpr int kF16Rw = 1, kF16U = 4;
 // the "- 8" folded into the group's activation sum (formed once per workgroup
 // while x is staged).  Each 32-bit word's nibbles are split into its even and
 // odd columns with two masks, and every byte becomes f32 in one conversion.
-constexpr int kQ4Rw = 2, kQ4U = 2;
+//
+// Persistent: a few workgroups per compute unit stage x once, then each wave
+// walks its items (RW rows x U steps; row block j of a wave is
+// gw + j * total_waves), requesting item t + 1 before it computes item t.
+// Loads go through buffer resources; an item past the wave's last one gets an
+// empty resource (zeros, no memory traffic), so every load is issued
+// unconditionally and each compute waits for exactly its own data.
+#ifndef PG_Q4_RW
+#define PG_Q4_RW 2
+#endif
+#ifndef PG_Q4_U
+#define PG_Q4_U 1
+#endif
+#ifndef PG_Q4_OCC
+#define PG_Q4_OCC 2
+#endif
+constexpr int kQ4Rw = PG_Q4_RW, kQ4U = PG_Q4_U, kQ4Occ = PG_Q4_OCC;
+constexpr int kQ4Threads = 512;
+constexpr int kQ4Waves = kQ4Threads / kWave;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t q4_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
 
 template <int RW, int U>
-__global__ __launch_bounds__(kGemvThreads) void gemv_q4tp_kernel(
+__global__ __launch_bounds__(kQ4Threads) void gemv_q4tp_kernel(
     const uint8_t *__restrict__ nib, const uint32_t *__restrict__ params, const uint8_t *__restrict__ codes,
     int rows, int cols, const float *__restrict__ x, float *__restrict__ y, int act) {
     extern __shared__ float4 sx[];
     const int nseg = cols >> 5;  // groups per row
     const int steps = (nseg + 63) >> 6;
+    const int nch = (steps + U - 1) / U;
     const int cstride = (5 * nseg + 7) >> 3;
     float *gsum = reinterpret_cast<float *>(sx + steps * 8 * 64);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r0 = (blockIdx.x * kGemvWaves + wave) * RW;
-    const uint8_t *nr[RW];
-    const uint8_t *cr[RW];
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-        const long long r = min(r0 + rr, rows - 1);
-        nr[rr] = nib + r * (cols >> 1);
-        cr[rr] = codes + r * cstride;
-    }
+    // Wave-uniform (the buffer resources below must be scalar).
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nrb = (rows + RW - 1) / RW;
+    const int gw = blockIdx.x * kQ4Waves + wave, tw = gridDim.x * kQ4Waves;
+    const int T = gw < nrb ? ((nrb - gw + tw - 1) / tw) * nch : 0;
+    const uint32_t half = (uint32_t)cols >> 1;
+    const uint32_t nbytes = (uint32_t)rows * half;
+
+    // A group's 5-bit code comes from one 4-byte window that starts at the
+    // byte holding its first bit, moved back to end inside the code buffer when
+    // needed (the field then still lies inside the window); the window's byte
+    // address need not be 4-aligned.  Dead items read the last row's window
+    // (cached).  The window's word stays as loaded until the compute, where the
+    // code is cut out of it (doing that at the load would wait for the load).
+    const uint32_t ctotal = (uint32_t)rows * (uint32_t)cstride;
     u32x4 wa[U][RW], wb[U][RW];
-    uint32_t ca[U][RW], cb[U][RW];
-    // Weights and the two code bytes of each group, one batch of U steps.
-    auto load = [&](int i0, u32x4 (&w)[U][RW], uint32_t (&c)[U][RW]) __attribute__((always_inline)) {
+    uint32_t ca[U][RW], cb[U][RW], pa[RW], pb[RW];
+    auto load = [&](int t, u32x4 (&w)[U][RW], uint32_t (&c)[U][RW], uint32_t (&p)[RW])
+                    __attribute__((always_inline)) {
+        const bool live = t < T;
+        const int tt = live ? t : 0;
+        const int rb = gw + (tt / nch) * tw, ch = tt % nch;
+        const __amdgpu_buffer_rsrc_t rn = q4_rsrc(nib, live ? nbytes : 0u);
+        const __amdgpu_buffer_rsrc_t rp = q4_rsrc(params, live ? (uint32_t)rows * 4u : 0u);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (i0 + u < steps) {
-                const int s = min(lane + 64 * (i0 + u), nseg - 1);
-                const int byte = (5 * s) >> 3;
-                const int nxt = min(byte + 1, cstride - 1);
+        for (int rr = 0; rr < RW; ++rr) {
+            const uint32_t r = (uint32_t)min(rb * RW + rr, rows - 1);
+            p[rr] = __builtin_amdgcn_raw_buffer_load_b32(rp, 4u * r, 0, 0);
 #pragma unroll
-                for (int rr = 0; rr < RW; ++rr) {
-                    w[u][rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(nr[rr] + 16 * s));
-                    c[u][rr] = (uint32_t)cr[rr][byte] | ((uint32_t)cr[rr][nxt] << 8);
-                }
+            for (int u = 0; u < U; ++u) {
+                const int s = min(lane + 64 * (ch * U + u), nseg - 1);
+                w[u][rr] = __builtin_amdgcn_raw_buffer_load_b128(rn, r * half + 16u * (uint32_t)s, 0, 0);
+                const uint32_t at = r * (uint32_t)cstride + ((5u * (uint32_t)s) >> 3);
+                uint32_t win;
+                __builtin_memcpy(&win, codes + min(at, ctotal - 4u), 4);
+                c[u][rr] = win;
             }
         }
     };
-    load(0, wa, ca);
-    for (int s = threadIdx.x; s < steps * 64; s += kGemvThreads) {
+    load(0, wa, ca, pa);
+    // Stage x: a thread's eight float4 are all requested before any is used
+    // (one round trip); groups past the row stage zeros.
+    for (int s = threadIdx.x; s < steps * 64; s += kQ4Threads) {
+        const float4 *xs4 = reinterpret_cast<const float4 *>(x) + 8 * min(s, nseg - 1);
+        float4 a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = xs4[j];
+        const bool in = s < nseg;
         float t = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float4 a = make_float4(0, 0, 0, 0);
-            if (s < nseg) a = reinterpret_cast<const float4 *>(x)[8 * s + j];
-            sx[xslot<8>(s, j)] = a;
-            t += (a.x + a.y) + (a.z + a.w);
+            if (!in) a[j] = make_float4(0, 0, 0, 0);
+            sx[xslot<8>(s, j)] = a[j];
+            t += (a[j].x + a[j].y) + (a[j].z + a[j].w);
         }
         gsum[s] = t;
-    }
-    float base[RW], step[RW];
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-        const uint32_t p = params[min(r0 + rr, rows - 1)];
-        base[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
-        step[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
     }
     __syncthreads();
 
     float acc[RW];
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) acc[rr] = 0.0f;
-    auto compute = [&](int i0, const u32x4 (&w)[U][RW], const uint32_t (&c)[U][RW]) __attribute__((always_inline)) {
+    // Item t: its chunk's U steps for the RW rows; the last chunk of a row
+    // block folds the sums across the wave and writes y.  An item past the
+    // wave's last one is computed on zeros and writes nothing (its rows are
+    // at or past `rows`).
+    auto compute = [&](int t, const u32x4 (&w)[U][RW], const uint32_t (&c)[U][RW], const uint32_t (&p)[RW])
+                       __attribute__((always_inline)) {
+        const int rb = gw + (t / nch) * tw, ch = t % nch;
+        float base[RW], step[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            base[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[rr] & 0xFFFFu));
+            step[rr] = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[rr] >> 16));
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int i = i0 + u;
-            if (i < steps) {
-                const int s = lane + 64 * i;
-                float xv[32];
+            const int i = ch * U + u;
+            const int ic = min(i, steps - 1);
+            const int s = lane + 64 * i;
+            float xv[32];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float4 a = sx[(i * 8 + j) * 64 + lane];
-                    xv[4 * j] = a.x; xv[4 * j + 1] = a.y; xv[4 * j + 2] = a.z; xv[4 * j + 3] = a.w;
-                }
-                const float xs8 = 8.0f * gsum[min(s, nseg - 1)];
+            for (int j = 0; j < 8; ++j) {
+                const float4 a = sx[(ic * 8 + j) * 64 + lane];
+                xv[4 * j] = a.x; xv[4 * j + 1] = a.y; xv[4 * j + 2] = a.z; xv[4 * j + 3] = a.w;
+            }
+            const float xs8 = 8.0f * gsum[min(s, nseg - 1)];
 #pragma unroll
-                for (int rr = 0; rr < RW; ++rr) {
-                    const uint32_t word[4] = {w[u][rr].x, w[u][rr].y, w[u][rr].z, w[u][rr].w};
-                    float d0 = 0.0f, d1 = 0.0f;
+            for (int rr = 0; rr < RW; ++rr) {
+                const uint32_t word[4] = {w[u][rr].x, w[u][rr].y, w[u][rr].z, w[u][rr].w};
+                float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        uint32_t lo = word[k] & 0x0F0F0F0Fu, hi = (word[k] >> 4) & 0x0F0F0F0Fu;
-                        // Keep the two masked words whole so each byte converts with one
-                        // v_cvt_f32_ubyteN instead of an extract and a conversion.
-                        asm volatile("" : "+v"(lo), "+v"(hi));
+                for (int k = 0; k < 4; ++k) {
+                    uint32_t lo = word[k] & 0x0F0F0F0Fu, hi = (word[k] >> 4) & 0x0F0F0F0Fu;
+                    // Keep the two masked words whole so each byte converts with one
+                    // v_cvt_f32_ubyteN instead of an extract and a conversion.
+                    asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            d0 = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b], d0);
-                            d1 = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b + 1], d1);
-                        }
+                    for (int b = 0; b < 4; ++b) {
+                        d0 = fmaf((float)((lo >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b], d0);
+                        d1 = fmaf((float)((hi >> (8 * b)) & 0xFFu), xv[8 * k + 2 * b + 1], d1);
                     }
-                    const uint32_t code = (c[u][rr] >> ((5 * s) & 7)) & 31u;
-                    // Hardware exp2 (exact at integer exponents; a scale below 2^-126 reads as 0).
-                    const float sc = s < nseg ? __builtin_amdgcn_exp2f(fmaf((float)code, step[rr], base[rr])) : 0.0f;
-                    acc[rr] = fmaf(sc, (d0 + d1) - xs8, acc[rr]);
                 }
+                uint32_t win = c[u][rr];
+                asm volatile("" : "+v"(win));  // cut the code here, not where the window loads
+                const uint32_t r = (uint32_t)min(rb * RW + rr, rows - 1);
+                const uint32_t at = r * (uint32_t)cstride + ((5u * (uint32_t)min(s, nseg - 1)) >> 3);
+                const uint32_t sh = 8u * (at - min(at, ctotal - 4u)) + ((5u * (uint32_t)s) & 7u);
+                const uint32_t code = (win >> sh) & 31u;
+                // Hardware exp2 (exact at integer exponents; a scale below 2^-126 reads as
+                // 0).  Groups past the row (s >= nseg) weigh nothing.
+                const float sc = s < nseg ? __builtin_amdgcn_exp2f(fmaf((float)code, step[rr], base[rr])) : 0.0f;
+                acc[rr] = fmaf(sc, (d0 + d1) - xs8, acc[rr]);
+            }
+        }
+        if (ch == nch - 1) {
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+                const float v = wave_sum(acc[rr]);
+                const int r = rb * RW + rr;
+                if (lane == rr && r < rows) y[r] = apply_act(act, v);
+                acc[rr] = 0.0f;
             }
         }
     };
-    for (int i0 = 0; i0 < steps; i0 += 2 * U) {
-        load(i0 + U, wb, cb);
-        compute(i0, wa, ca);
-        load(i0 + 2 * U, wa, ca);
-        compute(i0 + U, wb, cb);
-    }
-#pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-        const float v = wave_sum(acc[rr]);
-        if (lane == rr && r0 + rr < rows) y[r0 + rr] = apply_act(act, v);
+    for (int t = 0; t < T; t += 2) {
+        load(t + 1, wb, cb, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t, wa, ca, pa);
+        __builtin_amdgcn_sched_barrier(0);
+        load(t + 2, wa, ca, pa);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t + 1, wb, cb, pb);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 static int gemv_grid(int rows, int rw) { return ceil_div(rows, kGemvWaves * rw); }
+
+// Compute units of the current device (read once).
+static int device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
 
 }  // namespace pg
 
@@ -702,11 +772,14 @@ extern "C" int gemv_q4tp(const uint8_t *nib, const uint32_t *params, const uint8
     if (act != 0 && act != 1) return PG_EINVAL;
     if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
     if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
+    if ((size_t)rows * (size_t)cols / 2 > 0x7FFFFFFFu) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
+    if ((size_t)rows * (size_t)((5 * (cols / 32) + 7) / 8) < 4) return PG_EUNSUPPORTED;  // 4-byte code windows
     auto bytes = [](int c) { return (size_t)ceil_div(c / 32, 64) * (8 * 64 * sizeof(float4) + 64 * sizeof(float)); };
     static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q4tp_kernel<kQ4Rw, kQ4U>), bytes(32768));
     if (ok != PG_OK) return PG_ELAUNCH;
-    hipLaunchKernelGGL((gemv_q4tp_kernel<kQ4Rw, kQ4U>), dim3(gemv_grid(rows, kQ4Rw)), dim3(kGemvThreads),
-                       bytes(cols), as_stream(stream), nib, params, codes, rows, cols, x, y, act);
+    const int grid = std::min(ceil_div(ceil_div(rows, kQ4Rw), kQ4Waves), kQ4Occ * device_cus());
+    hipLaunchKernelGGL((gemv_q4tp_kernel<kQ4Rw, kQ4U>), dim3(grid), dim3(kQ4Threads), bytes(cols),
+                       as_stream(stream), nib, params, codes, rows, cols, x, y, act);
     return launch_status();
 }
 
