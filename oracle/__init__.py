@@ -67,7 +67,8 @@ def _declare(L):
     L.oracle_moe_experts_ungrouped.argtypes = [_P, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]
     L.oracle_moe_experts_grouped.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _I,
                                              _P, _P, _P, _P, _P, _P, _P, _P]
-    L.oracle_moe_combine.argtypes = [_P, _P, _P, _I, _I, _I, _P, _D, _P, _P]
+    L.oracle_moe_combine.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _D, _P, _P]
+    L.oracle_route_sigmoid.argtypes = [_P, _P, _I, _I, _I, _i, _D, _P, _P, _P]
     L.oracle_threads.restype = _i
 
 
@@ -258,6 +259,21 @@ def route(logits_f32, k: int, renorm: int = 0):
     return sel, rw, probs
 
 
+def route_sigmoid(logits_f32, bias, k: int, norm: int = 1, scale: float = 1.0):
+    """(sel int32 [n][k], rw f64 [n][k], choice f64 [n][E]): choice = sigmoid(l) + bias,
+    top k by choice (lower index on a tie), rw = sigmoid(l_sel) / den * scale with
+    den = sum_t sigmoid(l_sel) + 1e-20 when norm, else 1."""
+    L = _c(np.atleast_2d(logits_f32), np.float32)
+    n, E = L.shape
+    bias = _c(bias, np.float32)
+    assert bias.shape == (E,) and 1 <= k <= E
+    sel = np.empty((n, k), np.int32)
+    rw = np.empty((n, k), np.float64)
+    choice = np.empty((n, E), np.float64)
+    lib().oracle_route_sigmoid(_p(L), _p(bias), n, E, k, int(norm), float(scale), _p(sel), _p(rw), _p(choice))
+    return sel, rw, choice
+
+
 def group(sel, E: int, cap: int | None = None):
     """(counts int32 [E], lists int32 [E][cap]); unused list slots hold -1."""
     sel = _c(np.atleast_2d(sel), np.int32)
@@ -294,9 +310,11 @@ def moe_experts(X, sel, up, down, grouped: bool = False, E: int | None = None):
     return U, D
 
 
-def moe_combine(h, D, rw, w, eps: float):
-    """(h', out): h' = h + sum_t rw[b][t] D[b*k+t] (slot order), out = rmsnorm(h') * w."""
+def moe_combine(h, D, rw, w, eps: float, shared=None):
+    """(h', out): h' = h + shared[b] + sum_t rw[b][t] D[b*k+t] (slot order; shared optional),
+    out = rmsnorm(h') * w."""
     h = _c(np.atleast_2d(h), np.float32)
+    sh = None if shared is None else _c(np.atleast_2d(shared), np.float32)
     D = _c(D, np.float64)
     rw = _c(np.atleast_2d(rw), np.float64)
     n, H = h.shape
@@ -304,18 +322,25 @@ def moe_combine(h, D, rw, w, eps: float):
     w = _c(w, np.float32)
     h_out = np.empty((n, H), np.float64)
     out = np.empty((n, H), np.float64)
-    lib().oracle_moe_combine(_p(h), _p(D), _p(rw), n, k, H, _p(w), eps, _p(h_out), _p(out))
+    assert sh is None or sh.shape == (n, H)
+    lib().oracle_moe_combine(_p(h), None if sh is None else _p(sh), _p(D), _p(rw), n, k, H, _p(w), eps,
+                             _p(h_out), _p(out))
     return h_out, out
 
 
-def moe_pass(X, h, Wr, up, down, w, eps: float, k: int, renorm: int = 0):
-    """The whole routed-MoE pass; returns a dict of every stage."""
+def moe_pass(X, h, Wr, up, down, w, eps: float, k: int, renorm: int = 0, sigmoid=None, shared=None):
+    """The whole routed-MoE pass; returns a dict of every stage.  ``sigmoid`` = (bias, norm,
+    scale) selects the sigmoid router (``route_sigmoid``) instead of softmax; ``shared``
+    [n][H] is the dense term the combine adds before the slots."""
     logits = router_logits_f32(X, Wr)
-    sel, rw, probs = route(logits, k, renorm)
+    if sigmoid is None:
+        sel, rw, probs = route(logits, k, renorm)
+    else:
+        sel, rw, probs = route_sigmoid(logits, sigmoid[0], k, sigmoid[1], sigmoid[2])
     E = Wr.shape[0]
     counts, lists = group(sel, E)
     U, D = moe_experts(X, sel, up, down, grouped=True, E=E)
-    h_out, out = moe_combine(h, D, rw, w, eps)
+    h_out, out = moe_combine(h, D, rw, w, eps, shared=shared)
     return {"logits": logits, "logits_f64": router_logits_f64(X, Wr), "sel": sel, "rw": rw,
             "probs": probs, "counts": counts, "lists": lists, "U": U, "D": D,
             "h": h_out, "out": out}

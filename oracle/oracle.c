@@ -330,6 +330,40 @@ void oracle_route(const float *logits, int64_t n, int64_t E, int64_t k, int reno
     free(taken);
 }
 
+/* The sigmoid router with a selection bias (nemotron_prefill.rs, `pb_route`):
+ * per position b the choice value of expert e is
+ *     c_e = sigma(l_e) + bias[e],  sigma(x) = 1 / (1 + exp(-x)),
+ * and k rounds each take the largest remaining c (the lower index on a tie) and
+ * remove it.  The bias steers the choice only; the weight of slot t is
+ *     rw[b][t] = sigma(l_sel) / den * scale,
+ *     den = sum_t sigma(l_sel[t]) + 1e-20 when norm, else 1.
+ * All in f64 from the f32 logits; choice[b][e] receives c_e. */
+void oracle_route_sigmoid(const float *logits, const float *bias, int64_t n, int64_t E, int64_t k,
+                          int norm, double scale, int32_t *sel, double *rw, double *choice) {
+    char *taken = (char *)malloc((size_t)E);
+    for (int64_t b = 0; b < n; ++b) {
+        const float *l = logits + b * E;
+        double *c = choice + b * E;
+        for (int64_t e = 0; e < E; ++e) c[e] = 1.0 / (1.0 + exp(-(double)l[e])) + (double)bias[e];
+        memset(taken, 0, (size_t)E);
+        double sum = 0.0;
+        for (int64_t t = 0; t < k; ++t) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || c[e] > c[best]) best = e;   /* strict: lower index keeps a tie */
+            }
+            taken[best] = 1;
+            sel[b * k + t] = (int32_t)best;
+            sum += 1.0 / (1.0 + exp(-(double)l[best]));
+        }
+        const double den = norm ? sum + 1e-20 : 1.0;
+        for (int64_t t = 0; t < k; ++t)
+            rw[b * k + t] = (1.0 / (1.0 + exp(-(double)l[sel[b * k + t]]))) / den * scale;
+    }
+    free(taken);
+}
+
 /* Per expert e, the entries j = b*k + t (ascending) whose selection is e.
  * lists is [E][cap]; counts[e] = number of entries; entries past counts[e] are
  * left untouched. */
@@ -402,16 +436,18 @@ void oracle_moe_experts_grouped(const float *X, int64_t n, int64_t H, int64_t I,
         }
 }
 
-/* Combine into the residual and norm, per position b:
- *   m[i] = sum_{t=0..k-1} rw[b][t] * D[b*k+t][i]   (slot order)
+/* Combine into the residual and norm, per position b (nemotron_prefill.rs,
+ * `pb_add_rms` with add = 2; `shared` is its optional dense term, the output of
+ * a shared expert, which starts the sum before the slots; NULL: none):
+ *   m[i] = shared[b][i] + sum_{t=0..k-1} rw[b][t] * D[b*k+t][i]   (slot order)
  *   h'   = h[b] + m;   out[b] = w * h' / sqrt(mean(h'^2) + eps). */
-void oracle_moe_combine(const float *h, const double *D, const double *rw, int64_t n,
-                        int64_t k, int64_t H, const float *w, double eps,
+void oracle_moe_combine(const float *h, const float *shared, const double *D, const double *rw,
+                        int64_t n, int64_t k, int64_t H, const float *w, double eps,
                         double *h_out, double *out) {
     for (int64_t b = 0; b < n; ++b) {
         double ss = 0.0;
         for (int64_t i = 0; i < H; ++i) {
-            double m = 0.0;
+            double m = shared ? (double)shared[b * H + i] : 0.0;
             for (int64_t t = 0; t < k; ++t) m += rw[b * k + t] * D[(b * k + t) * H + i];
             double v = (double)h[b * H + i] + m;
             h_out[b * H + i] = v;

@@ -629,3 +629,66 @@ def test_argmax_nan_and_floor(oracle):
     assert list(ids[1:]) == [0, 0, 0, 0, 40]
     row = np.array([-np.inf, 5, np.nan, 5, 4], np.float32)
     assert oracle.argmax_rows(row) == 1
+
+
+# ------------------------------------------------------------------ sigmoid router
+
+def test_route_sigmoid_hand_worked(oracle):
+    """Four experts with equal logits 0 (sigmoid 1/2 each): the bias alone orders them,
+    bias [0.1, 0.3, 0.2, 0.0] -> experts 1 then 2; the bias does not enter the weights,
+    which are 1/2 * 2.5 = 1.25 without renormalisation, and 1/2 / (1 + 1e-20) * 2.5 = 1.25
+    with it (both halves equal)."""
+    L = np.zeros((1, 4), np.float32)
+    bias = np.array([0.1, 0.3, 0.2, 0.0], np.float32)
+    sel, rw, _ = oracle.route_sigmoid(L, bias, 2, norm=0, scale=2.5)
+    assert sel.tolist() == [[1, 2]] and rw.tolist() == [[1.25, 1.25]]
+    sel, rw, _ = oracle.route_sigmoid(L, bias, 2, norm=1, scale=2.5)
+    assert sel.tolist() == [[1, 2]] and rw.tolist() == [[1.25, 1.25]]
+
+
+def test_route_sigmoid_zero_bias_is_topk_of_logits(oracle):
+    """Zero bias: sigmoid is increasing, so the choice is the k largest logits in order
+    (numpy's stable argsort of -l), and the renormalised weights are scipy's expit of the
+    chosen logits over their sum, times scale."""
+    rng = np.random.default_rng(61)
+    L = rng.standard_normal((20, 128)).astype(np.float32)
+    sel, rw, choice = oracle.route_sigmoid(L, np.zeros(128, np.float32), 6, norm=1, scale=1.5)
+    want = np.argsort(-L.astype(np.float64), axis=1, kind="stable")[:, :6]
+    np.testing.assert_array_equal(sel, want)
+    s = scipy.special.expit(np.take_along_axis(L.astype(np.float64), want, 1))
+    np.testing.assert_allclose(rw, s / (s.sum(1, keepdims=True) + 1e-20) * 1.5, rtol=1e-14)
+    np.testing.assert_allclose(choice, scipy.special.expit(L.astype(np.float64)), rtol=1e-15)
+
+
+def test_route_sigmoid_bias_ties_and_unnormalised(oracle):
+    """A large bias forces experts in; exact ties go to the lower index; without
+    renormalisation the weight is sigmoid(l) * scale."""
+    rng = np.random.default_rng(62)
+    L = rng.standard_normal((5, 32)).astype(np.float32)
+    bias = np.zeros(32, np.float32)
+    bias[[30, 7]] = 5.0                       # always chosen first: 7 vs 30 by choice value
+    L[:, 3] = L[:, 9] = 10.0                  # equal choice values: 3 before 9
+    sel, rw, _ = oracle.route_sigmoid(L, bias, 4, norm=0, scale=0.75)
+    for b in range(5):
+        first = sorted([7, 30], key=lambda e: -(scipy.special.expit(float(L[b, e])) + 5.0))
+        assert sel[b].tolist() == first + [3, 9]
+    np.testing.assert_allclose(rw, scipy.special.expit(np.take_along_axis(L.astype(np.float64), sel, 1)) * 0.75,
+                               rtol=1e-14)
+
+
+def test_moe_combine_shared_term(oracle):
+    """The shared term adds to the residual with the slots: equals numpy's h + shared +
+    sum_t rw D, then the norm; and shared = 0 equals no shared term."""
+    rng = np.random.default_rng(63)
+    n, k, H = 3, 4, 64
+    h = rng.standard_normal((n, H)).astype(np.float32)
+    sh = rng.standard_normal((n, H)).astype(np.float32)
+    D = rng.standard_normal((n * k, H))
+    rw = rng.uniform(0, 1, (n, k))
+    w = rng.uniform(0.5, 1.5, H).astype(np.float32)
+    hp, out = oracle.moe_combine(h, D, rw, w, 1e-6, shared=sh)
+    ref = h.astype(np.float64) + sh + np.einsum("bt,bti->bi", rw, D.reshape(n, k, H))
+    np.testing.assert_allclose(hp, ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out, w * ref / np.sqrt((ref ** 2).mean(1, keepdims=True) + 1e-6), rtol=1e-12)
+    hp0, _ = oracle.moe_combine(h, D, rw, w, 1e-6, shared=np.zeros_like(sh))
+    np.testing.assert_array_equal(hp0, oracle.moe_combine(h, D, rw, w, 1e-6)[0])
