@@ -390,6 +390,39 @@ int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E
                 void *workspace, size_t workspace_bytes, pg_stream_t stream);
 size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, int32_t E, int32_t top_k);
 
+/*
+ * moe_route_sigmoid — the sigmoid router with a selection bias
+ * (nemotron_prefill.rs, `pb_route`), per position b of n:
+ *     c[e]          = sigmoid(logits[b][e]) + router_bias[e]       (f32)
+ *     sel[b][t]     = the t-th largest c (t < top_k), lower index wins a tie
+ *     route_w[b][t] = sigmoid(logits[b][sel]) / den * scale,
+ *     den           = sum_t sigmoid(logits[b][sel[b][t]]) + 1e-20 if renorm, else 1.
+ * The bias steers the choice only.  sigmoid(x) = 1 / (1 + exp(-x)) in f32.
+ *   logits [n][E] f32, router_bias [E] f32, sel [n][top_k] int32, route_w [n][top_k] f32.
+ * PG_EUNSUPPORTED: E > 1024, top_k > min(E, 16).
+ */
+int moe_route_sigmoid(const float *logits, const float *router_bias, int32_t n, int32_t E,
+                      int32_t top_k, int32_t renorm, float scale, int32_t *sel, float *route_w,
+                      pg_stream_t stream);
+
+/*
+ * moe_grouped_sigmoid — moe_grouped with the sigmoid + bias router of
+ * moe_route_sigmoid in place of softmax, and an optional dense term added with
+ * the slots (nemotron_prefill.rs `pb_add_rms`, add = 2: the shared expert's
+ * output starts the sum):
+ *     h[b] += shared[b] + sum_t route_w[b][t] * d_{b*top_k+t}   (shared first, then t ascending)
+ *     out[b] = w_norm * h[b] / sqrt(mean(h[b]^2) + eps)
+ *   shared [n][H] f32 (16-byte aligned; NULL: no dense term; must not overlap h or
+ *   out); every other argument, the workspace and the codes as moe_grouped.
+ */
+int moe_grouped_sigmoid(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
+                        int32_t top_k, const float *router_bias, int32_t renorm, float scale,
+                        const int8_t *up_q, const float *up_scale, const float *up_bias, int32_t I,
+                        const int8_t *down_q, const float *down_scale, const float *down_bias,
+                        const float *shared, float *h, const float *w_norm, float eps, float *out,
+                        float *logits, int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
+                        void *workspace, size_t workspace_bytes, pg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,7 +84,10 @@ def _declare(L):
     L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
     L.gemv_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
+    L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
+                                      _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -474,9 +477,13 @@ def moe_grouped_workspace_bytes(n: int, H: int, I: int, E: int, top_k: int) -> i
 
 def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight, h: torch.Tensor,
                 w_norm: torch.Tensor, eps: float, top_k: int, renorm: int = 0,
-                workspace: torch.Tensor | None = None, outputs: dict | None = None, stream=None) -> dict:
+                workspace: torch.Tensor | None = None, outputs: dict | None = None, stream=None,
+                router_bias: torch.Tensor | None = None, scale: float = 1.0,
+                shared: torch.Tensor | None = None) -> dict:
     """One routed-MoE pass; updates ``h`` in place and returns the outputs
-    {out, logits, sel, route_w, counts, lists} (pre-allocated ones may be passed in ``outputs``)."""
+    {out, logits, sel, route_w, counts, lists} (pre-allocated ones may be passed in ``outputs``).
+    With ``router_bias`` [E] the sigmoid + bias router routes (weights scaled by ``scale``,
+    renormalised when ``renorm``) and ``shared`` [n][H] (optional) is added with the slots."""
     _dev(X, torch.float32, "X")
     _dev(Wr, torch.float32, "Wr")
     _dev(h, torch.float32, "h")
@@ -499,12 +506,42 @@ def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight,
     need = moe_grouped_workspace_bytes(n, H, I, E, top_k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check("moe_grouped", lib().moe_grouped(
-        _ptr(X), n, H, _ptr(Wr), E, top_k, renorm, _ptr(up.q), _ptr(up.scale), _ptr(up.bias), I,
-        _ptr(down.q), _ptr(down.scale), _ptr(down.bias), _ptr(h), _ptr(w_norm), eps, _ptr(o["out"]),
+    if router_bias is None:
+        if shared is not None:
+            raise ValueError("shared needs the sigmoid router (router_bias)")
+        _check("moe_grouped", lib().moe_grouped(
+            _ptr(X), n, H, _ptr(Wr), E, top_k, renorm, _ptr(up.q), _ptr(up.scale), _ptr(up.bias), I,
+            _ptr(down.q), _ptr(down.scale), _ptr(down.bias), _ptr(h), _ptr(w_norm), eps, _ptr(o["out"]),
+            _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        return o
+    _dev(router_bias, torch.float32, "router_bias")
+    if router_bias.shape != (E,):
+        raise ValueError("router_bias must be [E]")
+    if shared is not None:
+        _dev(shared, torch.float32, "shared")
+        if shared.shape != (n, H):
+            raise ValueError("shared must be [n][H]")
+    _check("moe_grouped_sigmoid", lib().moe_grouped_sigmoid(
+        _ptr(X), n, H, _ptr(Wr), E, top_k, _ptr(router_bias), renorm, scale, _ptr(up.q), _ptr(up.scale),
+        _ptr(up.bias), I, _ptr(down.q), _ptr(down.scale), _ptr(down.bias),
+        None if shared is None else _ptr(shared), _ptr(h), _ptr(w_norm), eps, _ptr(o["out"]),
         _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o
+
+
+def moe_route_sigmoid(logits: torch.Tensor, router_bias: torch.Tensor, top_k: int, renorm: int = 1,
+                      scale: float = 1.0, stream=None):
+    """(sel int32 [n][k], route_w f32 [n][k]) of the sigmoid + bias router."""
+    _dev(logits, torch.float32, "logits")
+    _dev(router_bias, torch.float32, "router_bias")
+    n, E = logits.shape
+    sel = torch.empty(n, top_k, dtype=torch.int32, device=logits.device)
+    rw = torch.empty(n, top_k, dtype=torch.float32, device=logits.device)
+    _check("moe_route_sigmoid", lib().moe_route_sigmoid(_ptr(logits), _ptr(router_bias), n, E, top_k, renorm,
+                                                        scale, _ptr(sel), _ptr(rw), _stream(stream)))
+    return sel, rw
 
 
 def decode_frame_q8_workspace_bytes(hidden: int, inter: int) -> int:

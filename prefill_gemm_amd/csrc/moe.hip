@@ -11,13 +11,15 @@
 // instead of once per entry.
 #include <math.h>
 
+#include <type_traits>
+
 #include "expert_q8.h"
 #include "pg_device.h"
 #include "pg_host.h"
 
 namespace pg {
 
-int launch_moe_combine(float *h, const float *D, const float *rw, int n, int k, const float *w,
+int launch_moe_combine(float *h, const float *shared, const float *D, const float *rw, int n, int k, const float *w,
                        float eps, int hidden, float *out, hipStream_t s);
 
 constexpr int kRouterPos = 8;  // positions per router workgroup
@@ -87,28 +89,40 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
     }
 }
 
-// One wave per position: softmax over all E logits, then k rounds that take
-// the largest remaining logit (lower index on an exact tie) and mask it.
+// One wave per position.  Softmax router (SIG = false): softmax over all E
+// logits, then k rounds that take the largest remaining logit (lower index on
+// an exact tie) and mask it.  Sigmoid router (SIG = true; nemotron_prefill.rs,
+// `pb_route`): the choice value is sigmoid(l) + bias[e], the k rounds rank it
+// the same way, and slot t's weight is sigmoid(l_sel) / den * scale with
+// den = (sum of the chosen sigmoids in slot order) + 1e-20 if norm, else 1.
 // V = logits per lane (E <= 64 V); a lane's experts are lane, lane + 64, ...
-template <int V>
+template <int V, bool SIG>
 __global__ __launch_bounds__(64) void route_kernel(const float *__restrict__ logits, int E, int k,
-                                                   int renorm, int32_t *__restrict__ sel,
-                                                   float *__restrict__ rw) {
+                                                   int renorm, const float *__restrict__ bias, float scale,
+                                                   int32_t *__restrict__ sel, float *__restrict__ rw) {
     const int b = blockIdx.x, lane = threadIdx.x;
-    float v[V];
+    float v[V], sg[V];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? logits[(long long)b * E + e] : -INFINITY;
-        mx = fmaxf(mx, v[i]);
+        const float l = e < E ? logits[(long long)b * E + e] : -INFINITY;
+        if (SIG) {
+            sg[i] = 1.0f / (1.0f + expf(-l));
+            v[i] = e < E ? sg[i] + bias[e] : -INFINITY;
+        } else {
+            v[i] = l;
+            mx = fmaxf(mx, v[i]);
+        }
     }
-    mx = wave_max(mx);
     float z = 0.0f;
+    if (!SIG) {
+        mx = wave_max(mx);
 #pragma unroll
-    for (int i = 0; i < V; ++i)
-        if (lane + 64 * i < E) z += expf(v[i] - mx);
-    z = wave_sum(z);
+        for (int i = 0; i < V; ++i)
+            if (lane + 64 * i < E) z += expf(v[i] - mx);
+        z = wave_sum(z);
+    }
 
     uint32_t taken = 0;
     float psum = 0.0f;
@@ -133,15 +147,50 @@ __global__ __launch_bounds__(64) void route_kernel(const float *__restrict__ log
             }
         }
         if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        const float p = expf(bv - mx) / z;
+        float p;
+        if (SIG) {
+            float mine = 0.0f;  // the owner lane's sigmoid of the chosen expert
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                if (i == (bi >> 6)) mine = sg[i];
+            p = __shfl(mine, bi & 63, kWave);
+        } else {
+            p = expf(bv - mx) / z;
+        }
         psum += p;
         if (lane == 0) {
             sel[b * k + t] = bi;
             rw[b * k + t] = p;
         }
     }
-    if (renorm && lane == 0)
-        for (int t = 0; t < k; ++t) rw[b * k + t] = rw[b * k + t] / psum;
+    if (lane == 0) {
+        if (SIG) {
+            const float den = renorm ? psum + 1e-20f : 1.0f;
+            for (int t = 0; t < k; ++t) rw[b * k + t] = rw[b * k + t] / den * scale;
+        } else if (renorm) {
+            for (int t = 0; t < k; ++t) rw[b * k + t] = rw[b * k + t] / psum;
+        }
+    }
+}
+
+// Router kernel for E experts (softmax, or sigmoid + bias when bias is given).
+static int launch_route(const float *logits, int n, int E, int k, int renorm, const float *bias, float scale,
+                        int32_t *sel, float *rw, hipStream_t s) {
+    const bool sig = bias != nullptr;
+    auto go = [&](auto vtag) {
+        constexpr int V = decltype(vtag)::value;
+        if (sig)
+            hipLaunchKernelGGL((route_kernel<V, true>), dim3(n), dim3(64), 0, s, logits, E, k, renorm, bias, scale,
+                               sel, rw);
+        else
+            hipLaunchKernelGGL((route_kernel<V, false>), dim3(n), dim3(64), 0, s, logits, E, k, renorm, bias, scale,
+                               sel, rw);
+    };
+    if (E <= 64) go(std::integral_constant<int, 1>{});
+    else if (E <= 128) go(std::integral_constant<int, 2>{});
+    else if (E <= 256) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, kMaxExperts / kWave>{});
+    return launch_status();
 }
 
 // One wave per expert: walk the n*k entries in ascending order, 64 at a time,
@@ -190,13 +239,21 @@ extern "C" size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, i
     return moe_layout(n, H, I, top_k).total;
 }
 
-extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
-                           int32_t top_k, int32_t renorm, const int8_t *up_q,
-                           const float *up_scale, const float *up_bias, int32_t I,
-                           const int8_t *down_q, const float *down_scale, const float *down_bias,
-                           float *h, const float *w_norm, float eps, float *out, float *logits,
-                           int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
-                           void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x < y + bn && y < x + an;
+}
+
+// The pass behind moe_grouped (router_bias NULL: softmax router) and
+// moe_grouped_sigmoid (router_bias given: sigmoid + bias router; shared: the
+// dense term the combine adds before the slots, NULL: none).
+static int moe_run(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E, int32_t top_k,
+                   int32_t renorm, const float *router_bias, float scale, const int8_t *up_q,
+                   const float *up_scale, const float *up_bias, int32_t I, const int8_t *down_q,
+                   const float *down_scale, const float *down_bias, const float *shared, float *h,
+                   const float *w_norm, float eps, float *out, float *logits, int32_t *sel, float *route_w,
+                   int32_t *counts, int32_t *lists, void *workspace, size_t workspace_bytes,
+                   pg_stream_t stream) {
     if (!X || !Wr || !up_q || !up_scale || !up_bias || !down_q || !down_scale || !down_bias ||
         !h || !w_norm || !out || !logits || !sel || !route_w || !counts || !lists)
         return PG_EINVAL;
@@ -220,16 +277,7 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
                        dim3(256), 0, s, X, Wr, n, H, E, logits);
     int rc = launch_status();
     if (rc) return rc;
-    if (E <= 64)
-        hipLaunchKernelGGL(route_kernel<1>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
-    else if (E <= 128)
-        hipLaunchKernelGGL(route_kernel<2>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
-    else if (E <= 256)
-        hipLaunchKernelGGL(route_kernel<4>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm, sel, route_w);
-    else
-        hipLaunchKernelGGL(route_kernel<kMaxExperts / kWave>, dim3(n), dim3(64), 0, s, logits, E, top_k, renorm,
-                           sel, route_w);
-    if ((rc = launch_status())) return rc;
+    if ((rc = launch_route(logits, n, E, top_k, renorm, router_bias, scale, sel, route_w, s))) return rc;
     hipLaunchKernelGGL(group_kernel, dim3(ceil_div(E, 4)), dim3(256), 0, s, sel, nk, E, n, counts,
                        lists);
     if ((rc = launch_status())) return rc;
@@ -270,5 +318,43 @@ extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr
     dn.act = 0;
     if ((rc = launch_expert_bank(dn, s))) return rc;
 
-    return launch_moe_combine(h, D, route_w, n, top_k, w_norm, eps, H, out, s);
+    return launch_moe_combine(h, shared, D, route_w, n, top_k, w_norm, eps, H, out, s);
+}
+
+extern "C" int moe_grouped(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
+                           int32_t top_k, int32_t renorm, const int8_t *up_q,
+                           const float *up_scale, const float *up_bias, int32_t I,
+                           const int8_t *down_q, const float *down_scale, const float *down_bias,
+                           float *h, const float *w_norm, float eps, float *out, float *logits,
+                           int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
+                           void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+    return moe_run(X, n, H, Wr, E, top_k, renorm, nullptr, 1.0f, up_q, up_scale, up_bias, I, down_q, down_scale,
+                   down_bias, nullptr, h, w_norm, eps, out, logits, sel, route_w, counts, lists, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" int moe_grouped_sigmoid(const float *X, int32_t n, int32_t H, const float *Wr, int32_t E,
+                                   int32_t top_k, const float *router_bias, int32_t renorm, float scale,
+                                   const int8_t *up_q, const float *up_scale, const float *up_bias, int32_t I,
+                                   const int8_t *down_q, const float *down_scale, const float *down_bias,
+                                   const float *shared, float *h, const float *w_norm, float eps, float *out,
+                                   float *logits, int32_t *sel, float *route_w, int32_t *counts,
+                                   int32_t *lists, void *workspace, size_t workspace_bytes,
+                                   pg_stream_t stream) {
+    if (!router_bias) return PG_EINVAL;
+    if (shared && (!aligned16(shared) || overlaps(shared, (size_t)n * H * 4, out, (size_t)n * H * 4) ||
+                   overlaps(shared, (size_t)n * H * 4, h, (size_t)n * H * 4)))
+        return PG_EINVAL;
+    return moe_run(X, n, H, Wr, E, top_k, renorm, router_bias, scale, up_q, up_scale, up_bias, I, down_q,
+                   down_scale, down_bias, shared, h, w_norm, eps, out, logits, sel, route_w, counts, lists,
+                   workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_route_sigmoid(const float *logits, const float *router_bias, int32_t n, int32_t E,
+                                 int32_t top_k, int32_t renorm, float scale, int32_t *sel, float *route_w,
+                                 pg_stream_t stream) {
+    if (!logits || !router_bias || !sel || !route_w) return PG_EINVAL;
+    if (n <= 0 || E <= 0 || top_k <= 0) return PG_EINVAL;
+    if (E > kMaxExperts || top_k > kMaxTopK || top_k > E) return PG_EUNSUPPORTED;
+    return launch_route(logits, n, E, top_k, renorm, router_bias, scale, sel, route_w, as_stream(stream));
 }

@@ -62,8 +62,9 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     }
 }
 
-// MoE combine: h' = h + sum_t rw[b][t] * D[b*k + t] (slot order t ascending);
-// out = w * (h' * rsqrt(mean(h'^2) + eps)).
+// MoE combine: h' = h + (shared[b] + sum_t rw[b][t] * D[b*k + t]) (the sum
+// starting from the dense shared term when given, then slot order t ascending;
+// nemotron_prefill.rs `pb_add_rms`, add = 2); out = w * (h' * rsqrt(mean(h'^2) + eps)).
 // One workgroup of 1024 threads per position (a position's rows are few and
 // short, so every load of the position should be in flight at once): the
 // slots' rows come kCombT at a time, and each element adds them in slot order.
@@ -72,18 +73,20 @@ constexpr int kCombV = 4;  // float4 per thread: hidden <= 16384
 constexpr int kCombT = 4;  // slots requested together
 
 __global__ __launch_bounds__(kCombThreads) void moe_combine_kernel(
-    float *__restrict__ h, const float *__restrict__ D, const float *__restrict__ rw, int k,
-    const float *__restrict__ w, float eps, int hidden, float *__restrict__ out) {
+    float *__restrict__ h, const float *__restrict__ shared, const float *__restrict__ D,
+    const float *__restrict__ rw, int k, const float *__restrict__ w, float eps, int hidden,
+    float *__restrict__ out) {
     __shared__ float red[kCombThreads / kWave];
     const int b = blockIdx.x;
     const int h4 = hidden >> 2;
     float4 *hr = reinterpret_cast<float4 *>(h + (long long)b * hidden);
+    const float4 *sr = shared ? reinterpret_cast<const float4 *>(shared + (long long)b * hidden) : nullptr;
     float4 v[kCombV], m[kCombV];
 #pragma unroll
     for (int kk = 0; kk < kCombV; ++kk) {
         const int i = threadIdx.x + kk * kCombThreads;
         v[kk] = i < h4 ? hr[i] : make_float4(0, 0, 0, 0);
-        m[kk] = make_float4(0, 0, 0, 0);
+        m[kk] = sr && i < h4 ? sr[i] : make_float4(0, 0, 0, 0);
     }
     for (int t0 = 0; t0 < k; t0 += kCombT) {
         float c[kCombT];
@@ -135,9 +138,9 @@ __global__ __launch_bounds__(kCombThreads) void moe_combine_kernel(
     }
 }
 
-int launch_moe_combine(float *h, const float *D, const float *rw, int n, int k, const float *w,
+int launch_moe_combine(float *h, const float *shared, const float *D, const float *rw, int n, int k, const float *w,
                        float eps, int hidden, float *out, hipStream_t s) {
-    hipLaunchKernelGGL(moe_combine_kernel, dim3(n), dim3(kCombThreads), 0, s, h, D, rw, k, w, eps,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3(n), dim3(kCombThreads), 0, s, h, shared, D, rw, k, w, eps,
                        hidden, out);
     return launch_status();
 }

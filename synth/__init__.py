@@ -175,6 +175,12 @@ class MoEShape:
     top_k: int = 6
 
 
+def router_bias(rng: np.random.Generator, E: int) -> np.ndarray:
+    """Selection bias of the sigmoid router, U(-0.1, 0.1) per expert (the pages fix no
+    distribution; this range reorders experts whose sigmoids are close)."""
+    return rng.uniform(-0.1, 0.1, size=E).astype(np.float32)
+
+
 def moe(seed: int = 0, shape: MoEShape = MoEShape()) -> dict:
     """A routed-MoE pass: input, residual, router, up/down expert banks, norm weight."""
     r = streams(seed, 6)
