@@ -59,6 +59,7 @@ def _declare(L):
     L.oracle_dequant_q4tp.argtypes = [_P, _P, _P, _I, _I, _P]
     L.oracle_gemm_q4tp.argtypes = [_P, _P, _P, _I, _I, _P, _I, _i, _P]
     L.oracle_argmax_rows.argtypes = [_P, _I, _I, _P]
+    L.oracle_attn_prefill.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _P]
     L.oracle_add_rmsnorm.argtypes = [_P, _P, _I, _P, _D, _I, _I, _P, _P]
     L.oracle_router_logits_f64.argtypes = [_P, _P, _I, _I, _I, _P]
     L.oracle_router_logits_f32.argtypes = [_P, _P, _I, _I, _I, _P]
@@ -196,6 +197,29 @@ def gemm_q4tp(nib, params, codes, X, act: int = 0) -> np.ndarray:
     Y = np.empty((X.shape[0], rows), np.float64)
     lib().oracle_gemm_q4tp(_p(nib), _p(params), _p(codes), rows, cols, _p(X), X.shape[0], act, _p(Y))
     return Y[0] if vec else Y
+
+
+def kv_append(kc, vc, k, v, pos0: int):
+    """The caches with the pass's rows written at pos0 .. pos0 + n - 1 (copies; inputs kept)."""
+    kc, vc = np.array(kc, np.float32), np.array(vc, np.float32)
+    n = k.shape[0]
+    kc[pos0:pos0 + n] = np.asarray(k, np.float32).reshape(kc[pos0:pos0 + n].shape)
+    vc[pos0:pos0 + n] = np.asarray(v, np.float32).reshape(vc[pos0:pos0 + n].shape)
+    return kc, vc
+
+
+def attn_prefill(q, kc, vc, pos0: int, scale: float) -> np.ndarray:
+    """Causal GQA over a pass: q [n][nh][hd], caches [ctx][nkv][hd] (rows up to pos0 + n - 1
+    filled); o[b][h] = softmax_j(scale q[b][h] . kc[j][g]) . vc[j][g] over j <= pos0 + b,
+    g = h / (nh / nkv); f64."""
+    q = _c(q, np.float32)
+    kc, vc = _c(kc, np.float32), _c(vc, np.float32)
+    n, nh, hd = q.shape
+    nkv = kc.shape[1]
+    assert nh % nkv == 0 and kc.shape[2] == hd and vc.shape == kc.shape and kc.shape[0] >= pos0 + n
+    o = np.empty((n, nh, hd), np.float64)
+    lib().oracle_attn_prefill(_p(q), _p(kc), _p(vc), n, pos0, nh, nkv, hd, float(scale), _p(o))
+    return o
 
 
 def argmax_rows(L) -> np.ndarray:

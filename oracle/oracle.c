@@ -207,6 +207,45 @@ void oracle_gemm_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t 
     }
 }
 
+/* ------------------------------------------------------------ prefill attention */
+
+/* Causal grouped-query attention over one pass (nemotron_prefill.rs,
+ * `pb_kv_append` then `pb_attn` / `pb_attn_merge`).  The pass holds n positions
+ * at absolute positions pos0 .. pos0 + n - 1; their K and V rows are already in
+ * the caches kc, vc [pos][nkv][hd].  Query head h of position b reads KV head
+ * g = h / (nh / nkv) and every key position j <= pos0 + b:
+ *     s_j  = scale * sum_d q[b][h][d] * kc[j][g][d]
+ *     o[b][h][d] = sum_j exp(s_j - max_j s) vc[j][g][d] / sum_j exp(s_j - max_j s)
+ * in f64 from the f32 inputs. */
+void oracle_attn_prefill(const float *q, const float *kc, const float *vc, int64_t n, int64_t pos0,
+                         int64_t nh, int64_t nkv, int64_t hd, double scale, double *o) {
+    const int64_t rep = nh / nkv;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n * nh; ++i) {
+        const int64_t b = i / nh, h = i % nh, g = h / rep, J = pos0 + b + 1;
+        double *s = (double *)malloc((size_t)J * sizeof(double));
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < J; ++j) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < hd; ++d)
+                acc += (double)q[(b * nh + h) * hd + d] * (double)kc[(j * nkv + g) * hd + d];
+            s[j] = scale * acc;
+            if (s[j] > mx) mx = s[j];
+        }
+        double den = 0.0;
+        for (int64_t j = 0; j < J; ++j) {
+            s[j] = exp(s[j] - mx);
+            den += s[j];
+        }
+        for (int64_t d = 0; d < hd; ++d) {
+            double num = 0.0;
+            for (int64_t j = 0; j < J; ++j) num += s[j] * (double)vc[(j * nkv + g) * hd + d];
+            o[(b * nh + h) * hd + d] = num / den;
+        }
+        free(s);
+    }
+}
+
 /* ------------------------------------------------------------ argmax */
 
 /* Token choice of every position (nemotron_prefill.rs, `pb_argmax`, the verify

@@ -175,6 +175,22 @@ class MoEShape:
     top_k: int = 6
 
 
+def attn_pass(seed: int, n: int, pos0: int, nh: int = 32, nkv: int = 8, hd: int = 128,
+              ctx: int | None = None) -> dict:
+    """A prefill pass's attention inputs: q [n][nh][hd] and the pass's k, v [n][nkv][hd],
+    N(0, 1); caches [ctx][nkv][hd] holding N(0, 1) rows for the pos0 earlier positions and
+    zeros after (ctx defaults to pos0 + n).  The default heads follow the hidden-4096 frame's
+    QKV split (6144 = 32 query heads + 2 x 8 KV heads of 128)."""
+    r = streams(seed, 5)
+    ctx = pos0 + n if ctx is None else ctx
+    kc = np.zeros((ctx, nkv, hd), np.float32)
+    vc = np.zeros((ctx, nkv, hd), np.float32)
+    kc[:pos0] = normal(r[0], (pos0, nkv, hd))
+    vc[:pos0] = normal(r[1], (pos0, nkv, hd))
+    return {"q": normal(r[2], (n, nh, hd)), "k": normal(r[3], (n, nkv, hd)), "v": normal(r[4], (n, nkv, hd)),
+            "kc": kc, "vc": vc, "pos0": pos0, "scale": float(hd) ** -0.5}
+
+
 def router_bias(rng: np.random.Generator, E: int) -> np.ndarray:
     """Selection bias of the sigmoid router, U(-0.1, 0.1) per expert (the pages fix no
     distribution; this range reorders experts whose sigmoids are close)."""

@@ -692,3 +692,66 @@ def test_moe_combine_shared_term(oracle):
     np.testing.assert_allclose(out, w * ref / np.sqrt((ref ** 2).mean(1, keepdims=True) + 1e-6), rtol=1e-12)
     hp0, _ = oracle.moe_combine(h, D, rw, w, 1e-6, shared=np.zeros_like(sh))
     np.testing.assert_array_equal(hp0, oracle.moe_combine(h, D, rw, w, 1e-6)[0])
+
+
+# ------------------------------------------------------------------ prefill attention
+
+def _numpy_attention(q, kc, vc, pos0, scale):
+    """Textbook: per position and head, scipy's softmax of the masked scores times V."""
+    n, nh, hd = q.shape
+    nkv = kc.shape[1]
+    rep = nh // nkv
+    o = np.zeros((n, nh, hd))
+    for b in range(n):
+        J = pos0 + b + 1
+        for h in range(nh):
+            s = scale * (kc[:J, h // rep].astype(np.float64) @ q[b, h].astype(np.float64))
+            o[b, h] = scipy.special.softmax(s) @ vc[:J, h // rep].astype(np.float64)
+    return o
+
+
+def test_attn_single_key_and_uniform(oracle):
+    """Position 0 of the first pass sees one key: o = v_0 exactly.  q = 0 makes every score
+    equal: o is the plain mean of the visible V rows."""
+    rng = np.random.default_rng(71)
+    n, nh, nkv, hd = 5, 4, 2, 16
+    kc = rng.standard_normal((n, nkv, hd)).astype(np.float32)
+    vc = rng.standard_normal((n, nkv, hd)).astype(np.float32)
+    q = rng.standard_normal((n, nh, hd)).astype(np.float32)
+    o = oracle.attn_prefill(q, kc, vc, 0, 0.25)
+    for h in range(nh):
+        np.testing.assert_array_equal(o[0, h], vc[0, h // 2].astype(np.float64))
+    o0 = oracle.attn_prefill(np.zeros_like(q), kc, vc, 0, 0.25)
+    for b in range(n):
+        for h in range(nh):
+            np.testing.assert_allclose(o0[b, h], vc[:b + 1, h // 2].astype(np.float64).mean(0), rtol=1e-13, atol=1e-15)
+
+
+def test_attn_textbook_gqa_mapping_and_causality(oracle):
+    """scipy softmax per (position, head) with KV head h // rep over keys j <= pos0 + b; the
+    KV heads hold different values, so reading head h % nkv instead fails, and rows past the
+    causal limit hold large values that would show if they were read."""
+    rng = np.random.default_rng(72)
+    n, pos0, nh, nkv, hd = 6, 9, 8, 2, 32
+    ctx = pos0 + n + 3
+    kc = rng.standard_normal((ctx, nkv, hd)).astype(np.float32)
+    vc = rng.standard_normal((ctx, nkv, hd)).astype(np.float32)
+    kc[pos0 + n:] = 50.0
+    vc[pos0 + n:] = 1e6
+    vc[:, 1] += 3.0
+    q = rng.standard_normal((n, nh, hd)).astype(np.float32)
+    o = oracle.attn_prefill(q, kc, vc, pos0, hd ** -0.5)
+    np.testing.assert_allclose(o, _numpy_attention(q, kc, vc, pos0, hd ** -0.5), rtol=1e-11, atol=1e-12)
+    assert np.abs(o).max() < 100
+
+
+def test_kv_append(oracle):
+    rng = np.random.default_rng(73)
+    kc = np.zeros((10, 2, 4), np.float32)
+    vc = np.zeros((10, 2, 4), np.float32)
+    k = rng.standard_normal((3, 8)).astype(np.float32)
+    v = rng.standard_normal((3, 8)).astype(np.float32)
+    kc2, vc2 = oracle.kv_append(kc, vc, k, v, 4)
+    assert (kc2[:4] == 0).all() and (kc2[7:] == 0).all() and (kc == 0).all()
+    np.testing.assert_array_equal(kc2[4:7].reshape(3, 8), k)
+    np.testing.assert_array_equal(vc2[4:7].reshape(3, 8), v)
