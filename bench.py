@@ -304,6 +304,31 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
             "argmax_GB_s": round(64 * 32000 * 4 / (am * 1e-3) / 1e9, 1)}
 
 
+def component_attn(torch, pg, synth, reps=20):
+    """Causal GQA prefill attention (32 query heads, 8 KV heads of 128) over a 64-position
+    pass, first in its context and last in a 4096-position one: the KV append plus the
+    attention, 20 launches of each in one graph."""
+    out = {"workload": "causal GQA prefill attention, 64 positions, 32 q / 8 kv heads of 128"}
+    for pos0 in (0, 4032):
+        c = synth.attn_pass(17, 64, pos0)
+        kc, vc = to_dev(torch, c["kc"]), to_dev(torch, c["vc"])
+        k, v, q = to_dev(torch, c["k"]), to_dev(torch, c["v"]), to_dev(torch, c["q"])
+        o = torch.empty_like(q)
+        ws = torch.empty(max(4, pg.lib().attn_prefill_workspace_bytes(64, pos0, 32, 8, 128)), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            pg.attn_kv_append(k, v, kc, vc, pos0)
+            pg.attn_prefill(q, kc, vc, pos0, c["scale"], o=o, workspace=ws)
+        t = time_graphs(torch, [one_graph(torch, [step] * reps)], 3) / reps
+        keys = sum(pos0 + b + 1 for b in range(64))
+        flops = 4.0 * keys * 32 * 128
+        out[f"ctx{pos0 + 64}_us"] = round(t * 1e3, 2)
+        out[f"ctx{pos0 + 64}_TFLOP_s"] = round(flops / (t * 1e-3) / 1e12, 2)
+        out[f"ctx{pos0 + 64}_kv_MB"] = round((pos0 + 64) * 8 * 128 * 8 / 1e6, 2)
+    return out
+
+
 def component_gemv_norm(torch, pg, synth, reps=200):
     """The small q8 GEMV followed by add + RMSNorm: 50 pairs captured in one graph and
     replayed (steady state; the 1.3 MB of weights stay in cache), and one eager pair at
@@ -556,6 +581,7 @@ def main():
         torch.cuda.empty_cache()
         comp["q82_gemv_frame_shapes"] = component_q82(torch, pg, synth)
         comp["q4tp_gemv_frame_shapes"] = component_q4tp_argmax(torch, pg, synth)
+        comp["prefill_attention"] = component_attn(torch, pg, synth)
         result["components"] = comp
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -423,6 +423,33 @@ int moe_grouped_sigmoid(const float *X, int32_t n, int32_t H, const float *Wr, i
                         float *logits, int32_t *sel, float *route_w, int32_t *counts, int32_t *lists,
                         void *workspace, size_t workspace_bytes, pg_stream_t stream);
 
+/*
+ * attn_kv_append — the pass's K and V rows into the caches (nemotron_prefill.rs,
+ * `pb_kv_append`): kc[pos0 * width + i] = k[i], vc[...] = v[i] for i < n * width.
+ *   k, v [n][width] f32, kc, vc [cap][width] f32 (width = nkv * hd, a multiple of 4;
+ *   all 16-byte aligned).  PG_EINVAL: pos0 + n > cap.
+ */
+int attn_kv_append(const float *k, const float *v, int32_t n, int32_t width, int32_t pos0, float *kc,
+                   float *vc, int32_t cap, pg_stream_t stream);
+
+/*
+ * attn_prefill — causal grouped-query attention over one pass of n positions at
+ * absolute positions pos0 .. pos0 + n - 1 (nemotron_prefill.rs, `pb_attn` and
+ * `pb_attn_merge`; the rows of the pass must already be in the caches):
+ *     s_j        = (scale * q[b][h]) . kc[j][g],   g = h / (nh / nkv),  j <= pos0 + b
+ *     o[b][h][d] = sum_j exp(s_j - max s) vc[j][g][d] / sum_j exp(s_j - max s)
+ *   q [n][nh][hd] f32, kc, vc [>= pos0 + n][nkv][hd] f32 (16-byte aligned),
+ *   o [n][nh][hd] f32; workspace of attn_prefill_workspace_bytes(...) bytes
+ *   (split partials; contents on entry do not matter; must not overlap o).
+ * Arithmetic: f32 throughout; the keys are cut into splits, each with its own
+ * running maximum and sum, merged in split order.
+ * PG_EUNSUPPORTED: hd not 64 or 128, 64 % (nh / nkv) != 0, n > 64.
+ */
+int attn_prefill(const float *q, const float *kc, const float *vc, int32_t n, int32_t pos0, int32_t nh,
+                 int32_t nkv, int32_t hd, float scale, float *o, void *workspace, size_t workspace_bytes,
+                 pg_stream_t stream);
+size_t attn_prefill_workspace_bytes(int32_t n, int32_t pos0, int32_t nh, int32_t nkv, int32_t hd);
+
 #ifdef __cplusplus
 }
 #endif

@@ -84,10 +84,14 @@ def _declare(L):
     L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
     L.gemv_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
+    L.attn_kv_append.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _i32, _P]
+    L.attn_prefill.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _f, _P, _P, _sz, _P]
+    L.attn_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+    L.attn_prefill_workspace_bytes.restype = _sz
     L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
     L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -528,6 +532,39 @@ def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight,
         None if shared is None else _ptr(shared), _ptr(h), _ptr(w_norm), eps, _ptr(o["out"]),
         _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o
+
+
+def attn_kv_append(k: torch.Tensor, v: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pos0: int, stream=None):
+    """Write the pass's rows k, v [n][nkv][hd] into the caches [cap][nkv][hd] at pos0."""
+    for t, nm in ((k, "k"), (v, "v"), (kc, "kc"), (vc, "vc")):
+        _dev(t, torch.float32, nm)
+    n = k.shape[0]
+    width = k[0].numel()
+    if v.shape != k.shape or kc.shape != vc.shape or kc[0].numel() != width:
+        raise ValueError("k, v [n][...] and caches [cap][...] of the same row width")
+    _check("attn_kv_append", lib().attn_kv_append(_ptr(k), _ptr(v), n, width, pos0, _ptr(kc), _ptr(vc),
+                                                  kc.shape[0], _stream(stream)))
+
+
+def attn_prefill(q: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pos0: int, scale: float,
+                 o: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Causal GQA over a pass: q [n][nh][hd], caches [>= pos0 + n][nkv][hd] -> o [n][nh][hd]."""
+    for t, nm in ((q, "q"), (kc, "kc"), (vc, "vc")):
+        _dev(t, torch.float32, nm)
+    n, nh, hd = q.shape
+    nkv = kc.shape[1]
+    if kc.shape[2] != hd or vc.shape != kc.shape or kc.shape[0] < pos0 + n:
+        raise ValueError("caches must be [>= pos0 + n][nkv][hd]")
+    if o is None:
+        o = torch.empty(n, nh, hd, dtype=torch.float32, device=q.device)
+    _dev(o, torch.float32, "o")
+    need = lib().attn_prefill_workspace_bytes(n, pos0, nh, nkv, hd)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check("attn_prefill", lib().attn_prefill(_ptr(q), _ptr(kc), _ptr(vc), n, pos0, nh, nkv, hd, scale, _ptr(o),
+                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
     return o
 
 
