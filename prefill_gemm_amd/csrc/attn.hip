@@ -9,12 +9,12 @@
 // Work split: a workgroup takes one KV head, a block of 64 queries (64 / rep
 // positions times the rep query heads that share the KV head, so each K and V
 // row staged in LDS serves all of them) and one range of keys (a split).  Per
-// tile of 64 keys, K and V are staged in LDS; each wave scores its 16 queries
-// with one key per lane (q read from LDS by broadcast), keeps an online
-// softmax per query (running max m and sum l), and then accumulates p . V with
-// the lanes over the head dimensions.  A split writes (m, l, acc) per query;
-// the merge kernel rescales the splits to a common maximum and adds them in
-// split order.  Everything is f32, as on the pages.
+// tile of 64 keys, K and V are staged in LDS; each wave takes 16 queries,
+// forms their scores and p . V on the matrix cores in f32
+// (v_mfma_f32_16x16x4f32: products and sums in f32, as the pages' arithmetic),
+// and keeps an online softmax per query (running max m and sum l) on the vector
+// ALU in between.  A split writes (m, l, acc) per query; the merge kernel
+// rescales the splits to a common maximum and adds them in split order.
 #include <stdint.h>
 
 #include <algorithm>
@@ -31,9 +31,12 @@ constexpr int kAttnQW = kAttnQ / kAttnWaves;   // queries per wave
 constexpr int kAttnKT = 64;                    // keys per tile
 constexpr float kAttnNoMax = -1e30f;           // running max before any key
 
-// Maximum over the wave without LDS: quad, half-row and row exchanges by DPP,
-// then the four rows' results read out by readlane (wave-uniform result).
-__device__ __forceinline__ float wave_max_dpp(float v) {
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Reductions over the 16 lanes of one DPP row (quad, half-row and row
+// exchanges); every lane of the row receives the result.
+template <bool MAX>
+__device__ __forceinline__ float row16_reduce(float v) {
     auto dpp = [](float x, int ctrl) __attribute__((always_inline)) {
         switch (ctrl) {  // the control must be a constant expression
             case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
@@ -42,76 +45,88 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
             default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
         }
     };
-    v = fmaxf(v, dpp(v, 0));  // quad_perm [1, 0, 3, 2]
-    v = fmaxf(v, dpp(v, 1));  // quad_perm [2, 3, 0, 1]
-    v = fmaxf(v, dpp(v, 2));  // row_half_mirror
-    v = fmaxf(v, dpp(v, 3));  // row_mirror
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror, row_mirror
+        const float o = dpp(v, c);
+        v = MAX ? fmaxf(v, o) : v + o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 template <int HD>
 struct AttnCfg {
-    static constexpr int kKStride = HD + 4;    // floats; keeps lane-per-key reads off one bank
+    static constexpr int kKStride = HD + 4;        // floats per staged K row (padding spreads banks)
     static constexpr int kKFloats = kAttnKT * kKStride;
-    static constexpr int kVFloats = kAttnKT * HD;
-    static constexpr int kQFloats = kAttnQ * HD;
-    static constexpr int kPFloats = kAttnWaves * kAttnQW * kAttnKT;
-    static constexpr int kLdsFloats = kKFloats + kVFloats + kQFloats + kPFloats;
+    static constexpr int kVStride = kAttnKT + 4;   // V staged transposed: [dim][key]
+    static constexpr int kVFloats = HD * kVStride;
+    static constexpr int kPStride = kAttnKT + 4;   // p of a wave: [16 queries][key]
+    static constexpr int kPFloats = kAttnWaves * kAttnQW * kPStride;
+    static constexpr int kLdsFloats = kKFloats + kVFloats + kPFloats;
 };
 
 // Grid (split, query block, KV head).  part: [split][n][nh][hd + 2] (acc, m, l).
+//
+// Matrix-core fragments (v_mfma_f32_16x16x4f32: lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16], and holds D[4 (l / 16) + v][l % 16], v < 4).  A wave's
+// 16 queries are the rows.  q . k: step 4c + u contracts head dims
+// 16c + 4k + u (k = lane group l / 16), so a lane reads its q row and its key's
+// K row as float4 at dims 16c + 4k; q stays in registers.  p . V: step 4c + u
+// contracts keys 16c + 4k + u, p read back from LDS as float4 of its row and V
+// from its transposed copy as float4 of its dim.  The softmax runs in the D
+// layout: a row's 16 keys of a 16-key block sit in the 16 lanes of one DPP row.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc, int n, int pos0,
     int nh, int nkv, float scale, int chunk, float *__restrict__ part) {
     using C = AttnCfg<HD>;
+    constexpr int NC = HD / 16;   // 16-dim chunks (q . k) = 16-dim output blocks (p . V)
+    constexpr int NKB = kAttnKT / 16;
     extern __shared__ float lds[];
     float *sk = lds;
     float *sv = sk + C::kKFloats;
-    float *sq = sv + C::kVFloats;
-    float *sp = sq + C::kQFloats;
+    float *sp = sv + C::kVFloats;
     const int split = blockIdx.x, qblk = blockIdx.y, g = blockIdx.z;
     const int rep = nh / nkv, P = kAttnQ / rep;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, kg = lane >> 4;
     const int b0 = qblk * P;
     const int bl = min(n, b0 + P) - 1;                    // last position of the block
     const int j0 = split * chunk;
     const int j1 = min(j0 + chunk, pos0 + bl + 1);        // keys past the block's last limit add nothing
 
-    // Queries of the block, scaled: query i = position b0 + i / rep, head g * rep + i % rep.
-    for (int t = threadIdx.x; t < kAttnQ * (HD / 4); t += kAttnThreads) {
-        const int i = t / (HD / 4), d4 = t % (HD / 4);
+    // A fragments of q . k: query 16 wave + r16 (position b0 + i / rep, head g rep + i % rep), scaled.
+    f32x4 qf[NC];
+    {
+        const int i = kAttnQW * wave + r16;
         const int b = b0 + i / rep, h = g * rep + i % rep;
-        float4 v = make_float4(0, 0, 0, 0);
-        if (b < n) v = reinterpret_cast<const float4 *>(q + ((long long)b * nh + h) * HD)[d4];
-        reinterpret_cast<float4 *>(sq + i * HD)[d4] = make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
-    }
-
-    // The wave's queries: qi = wave * 16 + r.  Key limit of each: pos0 + its position.
-    int lim[kAttnQW];
 #pragma unroll
-    for (int r = 0; r < kAttnQW; ++r) {
-        const int i = wave * kAttnQW + r;
-        lim[r] = pos0 + b0 + i / rep;  // keys j <= lim (positions past n are never written)
+        for (int c = 0; c < NC; ++c) {
+            float4 v = make_float4(0, 0, 0, 0);
+            if (b < n) v = *reinterpret_cast<const float4 *>(q + ((long long)b * nh + h) * HD + 16 * c + 4 * kg);
+            qf[c] = f32x4{v.x * scale, v.y * scale, v.z * scale, v.w * scale};
+        }
     }
-    float m[kAttnQW], l[kAttnQW];
-    constexpr int DL = HD / 64;  // dims per lane in the p . V step
-    float acc[kAttnQW][DL];
+    // The lane's D rows: queries 16 wave + 4 kg + v; their key limits.
+    int lim[4];
+    float m[4], l[4];
+    f32x4 o[NC];
 #pragma unroll
-    for (int r = 0; r < kAttnQW; ++r) {
-        m[r] = kAttnNoMax;
-        l[r] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) acc[r][e] = 0.0f;
+    for (int v = 0; v < 4; ++v) {
+        lim[v] = pos0 + b0 + (kAttnQW * wave + 4 * kg + v) / rep;
+        m[v] = kAttnNoMax;
+        l[v] = 0.0f;
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float *pw = sp + wave * kAttnQW * C::kPStride;
 
     for (int t0 = j0; t0 < j1; t0 += kAttnKT) {
-        __syncthreads();  // the previous tile's K, V and p are no longer read
-        // Stage the tile's K and V rows (keys t0 .. t0 + 63; rows past j1 stage zeros).
+        __syncthreads();  // the previous tile's K and V are no longer read
+        // Stage keys t0 .. t0 + 63: K rows as they are, V transposed (rows past j1 zero).
         constexpr int kRow4 = HD / 4;
         for (int t = threadIdx.x; t < kAttnKT * kRow4; t += kAttnThreads) {
             const int kk = t / kRow4, d4 = t % kRow4;
@@ -122,76 +137,80 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
                 a = reinterpret_cast<const float4 *>(kc + off)[d4];
                 c = reinterpret_cast<const float4 *>(vc + off)[d4];
             }
-            reinterpret_cast<float4 *>(sk + kk * C::kKStride)[d4] = a;
-            reinterpret_cast<float4 *>(sv + kk * HD)[d4] = c;
+            *reinterpret_cast<float4 *>(sk + kk * C::kKStride + 4 * d4) = a;
+            sv[(4 * d4 + 0) * C::kVStride + kk] = c.x;
+            sv[(4 * d4 + 1) * C::kVStride + kk] = c.y;
+            sv[(4 * d4 + 2) * C::kVStride + kk] = c.z;
+            sv[(4 * d4 + 3) * C::kVStride + kk] = c.w;
         }
         __syncthreads();
 
-        // Scores: lane = key t0 + lane, 16 queries.
-        float s[kAttnQW];
+        // Scores of the wave's 16 queries against the tile's 4 blocks of 16 keys.
+        f32x4 sc[NKB];
 #pragma unroll
-        for (int r = 0; r < kAttnQW; ++r) s[r] = 0.0f;
-        const float *krow = sk + lane * C::kKStride;
-        const float *qw = sq + wave * kAttnQW * HD;
-        for (int d = 0; d < HD; d += 4) {
-            const float4 kv = *reinterpret_cast<const float4 *>(krow + d);
+        for (int kb = 0; kb < NKB; ++kb) {
+            sc[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float *krow = sk + (16 * kb + r16) * C::kKStride + 4 * kg;
 #pragma unroll
-            for (int r = 0; r < kAttnQW; ++r) {
-                const float4 qv = *reinterpret_cast<const float4 *>(qw + r * HD + d);
-                s[r] = fmaf(qv.x, kv.x, s[r]);
-                s[r] = fmaf(qv.y, kv.y, s[r]);
-                s[r] = fmaf(qv.z, kv.z, s[r]);
-                s[r] = fmaf(qv.w, kv.w, s[r]);
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 kf = *reinterpret_cast<const f32x4 *>(krow + 16 * c);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sc[kb] = mfma_f32_16x16x4(qf[c][u], kf[u], sc[kb]);
             }
         }
-        // Online softmax per query; masked keys (past the query's limit or the
-        // split) weigh exactly 0.  The running sum stays a per-lane partial
-        // (every lane rescales by the same factor) and is folded once at the end.
-        const int j = t0 + lane;
-        float *pw = sp + wave * kAttnQW * kAttnKT;
+        // Online softmax per row; masked keys weigh exactly 0.  Sums stay per lane.
 #pragma unroll
-        for (int r = 0; r < kAttnQW; ++r) {
-            const bool ok = j < j1 && j <= lim[r];
-            const float sc = ok ? s[r] : -INFINITY;
-            const float mn = fmaxf(m[r], wave_max_dpp(sc));
-            const float al = expf(m[r] - mn);
-            const float p = ok ? expf(sc - mn) : 0.0f;
-            l[r] = l[r] * al + p;
+        for (int v = 0; v < 4; ++v) {
+            float s[NKB], mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < DL; ++e) acc[r][e] *= al;
-            m[r] = mn;
-            pw[r * kAttnKT + lane] = p;
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int j = t0 + 16 * kb + r16;
+                s[kb] = (j < j1 && j <= lim[v]) ? sc[kb][v] : -INFINITY;
+                mx = fmaxf(mx, s[kb]);
+            }
+            const float mn = fmaxf(m[v], row16_reduce<true>(mx));
+            const float al = expf(m[v] - mn);
+            float ps = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const float p = s[kb] == -INFINITY ? 0.0f : expf(s[kb] - mn);
+                ps += p;
+                pw[(4 * kg + v) * C::kPStride + 16 * kb + r16] = p;
+            }
+            l[v] = l[v] * al + ps;
+            m[v] = mn;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) o[c][v] *= al;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's p writes land before its reads (lgkmcnt 0)
         __builtin_amdgcn_wave_barrier();
-        // p . V: lane owns dims lane * DL .. lane * DL + DL - 1.
-        for (int kk = 0; kk < kAttnKT; ++kk) {
-            float vv[DL];
+        // o += p . V over the tile's keys.
 #pragma unroll
-            for (int e = 0; e < DL; ++e) vv[e] = sv[kk * HD + lane * DL + e];
+        for (int c2 = 0; c2 < NKB; ++c2) {
+            const f32x4 pf = *reinterpret_cast<const f32x4 *>(pw + r16 * C::kPStride + 16 * c2 + 4 * kg);
 #pragma unroll
-            for (int r = 0; r < kAttnQW; ++r) {
-                const float p = pw[r * kAttnKT + kk];
+            for (int c = 0; c < NC; ++c) {
+                const f32x4 vf = *reinterpret_cast<const f32x4 *>(sv + (16 * c + r16) * C::kVStride + 16 * c2 + 4 * kg);
 #pragma unroll
-                for (int e = 0; e < DL; ++e) acc[r][e] = fmaf(p, vv[e], acc[r][e]);
+                for (int u = 0; u < 4; ++u) o[c] = mfma_f32_16x16x4(pf[u], vf[u], o[c]);
             }
         }
+        __builtin_amdgcn_wave_barrier();  // p is rewritten by the next tile only after these reads
     }
 
-    // Partials of the wave's queries for this split.
+    // Partials of the lane's rows for this split: o[c][v] is (query 16 wave + 4 kg + v, dim 16 c + r16).
 #pragma unroll
-    for (int r = 0; r < kAttnQW; ++r) l[r] = wave_sum(l[r]);
-#pragma unroll
-    for (int r = 0; r < kAttnQW; ++r) {
-        const int i = wave * kAttnQW + r;
+    for (int v = 0; v < 4; ++v) {
+        const float lsum = row16_reduce<false>(l[v]);
+        const int i = kAttnQW * wave + 4 * kg + v;
         const int b = b0 + i / rep, h = g * rep + i % rep;
         if (b >= n) continue;
-        float *o = part + (((long long)split * n + b) * nh + h) * (HD + 2);
+        float *dst = part + (((long long)split * n + b) * nh + h) * (HD + 2);
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[lane * DL + e] = acc[r][e];
-        if (lane == 0) {
-            o[HD] = m[r];
-            o[HD + 1] = l[r];
+        for (int c = 0; c < NC; ++c) dst[16 * c + r16] = o[c][v];
+        if (r16 == 0) {
+            dst[HD] = m[v];
+            dst[HD + 1] = lsum;
         }
     }
 }
