@@ -124,26 +124,42 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
     for (int c = 0; c < NC; ++c) o[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float *pw = sp + wave * kAttnQW * C::kPStride;
 
-    for (int t0 = j0; t0 < j1; t0 += kAttnKT) {
-        __syncthreads();  // the previous tile's K and V are no longer read
-        // Stage keys t0 .. t0 + 63: K rows as they are, V transposed (rows past j1 zero).
-        constexpr int kRow4 = HD / 4;
-        for (int t = threadIdx.x; t < kAttnKT * kRow4; t += kAttnThreads) {
-            const int kk = t / kRow4, d4 = t % kRow4;
-            const int j = t0 + kk;
-            float4 a = make_float4(0, 0, 0, 0), c = make_float4(0, 0, 0, 0);
+    // K and V of a tile come into registers one tile ahead (each thread NR
+    // float4 of each), so their memory latency hides behind the previous
+    // tile's arithmetic; keys past j1 read as zeros.
+    constexpr int kRow4 = HD / 4;
+    constexpr int NR = kAttnKT * kRow4 / kAttnThreads;
+    float4 ka[NR], va[NR];
+    auto fetch = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int t = threadIdx.x + r * kAttnThreads;
+            const int j = t0 + t / kRow4, d4 = t % kRow4;
+            ka[r] = va[r] = make_float4(0, 0, 0, 0);
             if (j < j1) {
                 const long long off = ((long long)j * nkv + g) * HD;
-                a = reinterpret_cast<const float4 *>(kc + off)[d4];
-                c = reinterpret_cast<const float4 *>(vc + off)[d4];
+                ka[r] = reinterpret_cast<const float4 *>(kc + off)[d4];
+                va[r] = reinterpret_cast<const float4 *>(vc + off)[d4];
             }
-            *reinterpret_cast<float4 *>(sk + kk * C::kKStride + 4 * d4) = a;
-            sv[(4 * d4 + 0) * C::kVStride + kk] = c.x;
-            sv[(4 * d4 + 1) * C::kVStride + kk] = c.y;
-            sv[(4 * d4 + 2) * C::kVStride + kk] = c.z;
-            sv[(4 * d4 + 3) * C::kVStride + kk] = c.w;
+        }
+    };
+    if (j0 < j1) fetch(j0);
+
+    for (int t0 = j0; t0 < j1; t0 += kAttnKT) {
+        __syncthreads();  // the previous tile's K and V are no longer read
+        // Stage keys t0 .. t0 + 63: K rows as they are, V transposed.
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int t = threadIdx.x + r * kAttnThreads;
+            const int kk = t / kRow4, d4 = t % kRow4;
+            *reinterpret_cast<float4 *>(sk + kk * C::kKStride + 4 * d4) = ka[r];
+            sv[(4 * d4 + 0) * C::kVStride + kk] = va[r].x;
+            sv[(4 * d4 + 1) * C::kVStride + kk] = va[r].y;
+            sv[(4 * d4 + 2) * C::kVStride + kk] = va[r].z;
+            sv[(4 * d4 + 3) * C::kVStride + kk] = va[r].w;
         }
         __syncthreads();
+        if (t0 + kAttnKT < j1) fetch(t0 + kAttnKT);
 
         // Scores of the wave's 16 queries against the tile's 4 blocks of 16 keys.
         f32x4 sc[NKB];
