@@ -65,7 +65,8 @@ struct AttnCfg {
     static constexpr int kVFloats = HD * kVStride;
     static constexpr int kPStride = kAttnKT + 4;   // p of a wave: [16 queries][key]
     static constexpr int kPFloats = kAttnWaves * kAttnQW * kPStride;
-    static constexpr int kLdsFloats = kKFloats + kVFloats + kPFloats;
+    static_assert(kPFloats <= kKFloats, "p reuses the K tile's space");
+    static constexpr int kLdsFloats = kKFloats + kVFloats;
 };
 
 // Grid (split, query block, KV head).  part: [split][n][nh][hd + 2] (acc, m, l).
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
     extern __shared__ float lds[];
     float *sk = lds;
     float *sv = sk + C::kKFloats;
-    float *sp = sv + C::kVFloats;
+    float *sp = sk;  // p takes the K tile's space once every wave has its scores
     const int split = blockIdx.x, qblk = blockIdx.y, g = blockIdx.z;
     const int rep = nh / nkv, P = kAttnQ / rep;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
                 for (int u = 0; u < 4; ++u) sc[kb] = mfma_f32_16x16x4(qf[c][u], kf[u], sc[kb]);
             }
         }
+        __syncthreads();  // every wave is done with K: its space takes p
         // Online softmax per row; masked keys weigh exactly 0.  Sums stay per lane.
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -211,7 +213,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
                 for (int u = 0; u < 4; ++u) o[c] = mfma_f32_16x16x4(pf[u], vf[u], o[c]);
             }
         }
-        __builtin_amdgcn_wave_barrier();  // p is rewritten by the next tile only after these reads
     }
 
     // Partials of the lane's rows for this split: o[c][v] is (query 16 wave + 4 kg + v, dim 16 c + r16).
