@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-components", action="store_true", help="only the timed steps")
     ap.add_argument("--moe-only", action="store_true",
                     help="run only the routed-MoE pass component (for profiling its kernels)")
+    ap.add_argument("--formats-only", action="store_true",
+                    help="run only the q8_2f, q4tp/argmax and attention components (for profiling their kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -505,6 +507,11 @@ def main():
     import synth
     if args.moe_only:
         print(json.dumps({"moe_pass": component_moe(torch, pg, synth)}), flush=True)
+        return
+    if args.formats_only:
+        print(json.dumps({"q82_gemv_frame_shapes": component_q82(torch, pg, synth),
+                          "q4tp_gemv_frame_shapes": component_q4tp_argmax(torch, pg, synth),
+                          "prefill_attention": component_attn(torch, pg, synth)}), flush=True)
         return
 
     log("building inputs ...")

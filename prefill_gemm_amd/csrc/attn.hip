@@ -233,7 +233,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
 }
 
 // One wave per (position, query head): the splits rescaled to their common
-// maximum and added in split order.
+// maximum and added in split order.  Lane s fetches split s's maximum and sum
+// (splits <= 64), so the maximum and the denominator are one wave reduction
+// each; the partial rows are requested eight splits at a time.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *__restrict__ part, int n, int nh,
                                                                   int splits, float *__restrict__ o) {
@@ -241,19 +243,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *_
     const int i = blockIdx.x * kAttnWaves + (threadIdx.x >> 6);  // b * nh + h
     if (i >= n * nh) return;
     constexpr int DL = HD / 64;
+    constexpr int kBatch = 8;
     const long long stride = (long long)n * nh * (HD + 2);
     const float *p0 = part + (long long)i * (HD + 2);
-    float mx = kAttnNoMax;
-    for (int s = 0; s < splits; ++s) mx = fmaxf(mx, p0[s * stride + HD]);
+    const bool mine = lane < splits;
+    const float ms = mine ? p0[lane * stride + HD] : kAttnNoMax;
+    const float ls = mine ? p0[lane * stride + HD + 1] : 0.0f;
+    const float mx = wave_max(ms);
+    const float f = mine ? expf(ms - mx) : 0.0f;  // split `lane`'s factor
     float den = 0.0f, num[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) num[e] = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-        const float *ps = p0 + s * stride;
-        const float f = expf(ps[HD] - mx);
-        den = fmaf(ps[HD + 1], f, den);
+    for (int s0 = 0; s0 < splits; s0 += kBatch) {
+        float a[kBatch][DL];
 #pragma unroll
-        for (int e = 0; e < DL; ++e) num[e] = fmaf(ps[lane * DL + e], f, num[e]);
+        for (int k = 0; k < kBatch; ++k) {
+            const int sk = min(s0 + k, splits - 1);
+#pragma unroll
+            for (int e = 0; e < DL; ++e) a[k][e] = p0[sk * stride + lane * DL + e];
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (s0 + k >= splits) break;
+            const float fk = __shfl(f, s0 + k, kWave);
+            const float lk = __shfl(ls, s0 + k, kWave);
+            den = fmaf(lk, fk, den);
+#pragma unroll
+            for (int e = 0; e < DL; ++e) num[e] = fmaf(a[k][e], fk, num[e]);
+        }
     }
 #pragma unroll
     for (int e = 0; e < DL; ++e) o[(long long)i * HD + lane * DL + e] = num[e] / den;
@@ -268,11 +285,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const float4 *__restrict
     }
 }
 
-// Keys per split: a multiple of the tile, with enough splits that the grid
-// holds about two workgroups per compute unit.
+// Keys per split: a multiple of the tile, with enough splits (at most 64) that
+// the grid holds about two workgroups per compute unit.
 static int attn_chunk(int ctx, int blocks) {
     const int tiles = ceil_div(ctx, kAttnKT);
-    const int want = std::max(1, 512 / std::max(1, blocks));
+    const int want = std::min(64, std::max(1, 512 / std::max(1, blocks)));  // the merge takes <= 64 splits
     const int splits = std::min(tiles, want);
     return kAttnKT * ceil_div(tiles, splits);
 }
