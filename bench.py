@@ -13,7 +13,9 @@ rate (positions/s) is reported beside it.  After the timed steps (not part of
 ms_per_step) the other workloads are measured: the 1024x1024 GEMV + add +
 RMSNorm, the 4096x4096 f16 GEMV over 64 rotated copies, the 420-position
 prompt as 6 x 64 + 36, the decode frame as one persistent launch, the
-routed-MoE pass, and the q8_2f GEMVs on the frame's shapes.
+routed-MoE pass, the q8_2f GEMVs and prefill products and the q4tp GEMVs on
+the frame's shapes, the per-position argmax, and causal GQA prefill
+attention at context 64 and 4096.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
