@@ -424,6 +424,28 @@ int moe_grouped_sigmoid(const float *X, int32_t n, int32_t H, const float *Wr, i
                         void *workspace, size_t workspace_bytes, pg_stream_t stream);
 
 /*
+ * expert_bank_q82 — the grouped expert product on the q8_2f format
+ * (nemotron_prefill.rs, the q8_2f bank payload of `pb_q8_bank`'s pass: int8
+ * body, binary16 row scales, binary16 column field per expert).  For every
+ * expert e and every entry j in lists[e][0 .. counts[e]):
+ *     out[j][r] = act( rs[e][r] * sum_c q[e][r][c] * (cf[e][c] * x[j / src_div][c]) ),  r < rows.
+ * Each expert's weights are read once for all of its entries.
+ *   q [E][rows][cols] int8 (16-byte aligned), row_scale [E][rows] and
+ *   col_field [E][cols] binary16 bits (col_field 16-byte aligned), x rows ldx
+ *   floats apart (ldx % 4 == 0, 16-byte aligned), counts [E], lists [E][cap]
+ *   int32 (entries ascending, as moe_grouped's lists), out rows ldo floats apart
+ *   (rows of entries no expert lists are not written).
+ * Arithmetic as prefill_gemm_q82: cf * x in f32 entering the matrix cores as an
+ * exact-to-2^-17 bf16 hi + lo pair, int8 as exact bf16, f32 sums, the row scale
+ * on the total.
+ * PG_EUNSUPPORTED: cols % 32 != 0, cap > 64, E > 1024, rows * cols >= 2^31.
+ */
+int expert_bank_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field, int32_t E,
+                    int32_t rows, int32_t cols, const float *x, int64_t ldx, int32_t src_div,
+                    const int32_t *counts, const int32_t *lists, int32_t cap, float *out, int64_t ldo,
+                    int32_t act, pg_stream_t stream);
+
+/*
  * attn_kv_append — the pass's K and V rows into the caches (nemotron_prefill.rs,
  * `pb_kv_append`): kc[pos0 * width + i] = k[i], vc[...] = v[i] for i < n * width.
  *   k, v [n][width] f32, kc, vc [cap][width] f32 (width = nkv * hd, a multiple of 4;

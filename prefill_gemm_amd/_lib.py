@@ -84,6 +84,8 @@ def _declare(L):
     L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
     L.gemv_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
+    L.expert_bank_q82.argtypes = [_P, _P, _P, _i32, _i32, _i32, _P, ctypes.c_int64, _i32, _P, _P, _i32, _P,
+                                  ctypes.c_int64, _i32, _P]
     L.attn_kv_append.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _i32, _P]
     L.attn_prefill.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _f, _P, _P, _sz, _P]
     L.attn_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
@@ -91,7 +93,7 @@ def _declare(L):
     L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
     L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -533,6 +535,30 @@ def moe_grouped(X: torch.Tensor, Wr: torch.Tensor, up: Q8Weight, down: Q8Weight,
         _ptr(o["logits"]), _ptr(o["sel"]), _ptr(o["route_w"]), _ptr(o["counts"]), _ptr(o["lists"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o
+
+
+def expert_bank_q82(q: torch.Tensor, rs: torch.Tensor, cf: torch.Tensor, x: torch.Tensor, counts: torch.Tensor,
+                    lists: torch.Tensor, src_div: int = 1, act: int = 0, out: torch.Tensor | None = None,
+                    n_out: int | None = None, stream=None):
+    """Grouped q8_2f expert product: q int8 [E][rows][cols], rs f16 [E][rows], cf f16 [E][cols],
+    x f32 [*][cols], counts int32 [E], lists int32 [E][cap]; out f32 [n_out][rows] (rows of
+    entries listed by an expert are written)."""
+    _dev(q, torch.int8, "q")
+    _dev(rs, torch.float16, "rs")
+    _dev(cf, torch.float16, "cf")
+    _dev(x, torch.float32, "x")
+    _dev(counts, torch.int32, "counts")
+    _dev(lists, torch.int32, "lists")
+    E, rows, cols = q.shape
+    if rs.shape != (E, rows) or cf.shape != (E, cols) or x.shape[-1] != cols or lists.shape[0] != E:
+        raise ValueError("q [E][rows][cols], rs [E][rows], cf [E][cols], x [*][cols], lists [E][cap]")
+    if out is None:
+        out = torch.zeros(n_out if n_out is not None else lists.shape[1], rows, dtype=torch.float32, device=q.device)
+    _dev(out, torch.float32, "out")
+    _check("expert_bank_q82", lib().expert_bank_q82(_ptr(q), _ptr(rs), _ptr(cf), E, rows, cols, _ptr(x), cols,
+                                                    src_div, _ptr(counts), _ptr(lists), lists.shape[1], _ptr(out),
+                                                    rows, act, _stream(stream)))
+    return out
 
 
 def attn_kv_append(k: torch.Tensor, v: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, pos0: int, stream=None):

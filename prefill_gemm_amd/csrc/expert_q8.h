@@ -27,6 +27,11 @@ struct ExpertBank {
     float *out;
     long long ldo;
     int act;
+    // q8_2f banks (scale / bias unused): binary16 row scales [E][rows] and
+    // column fields [E][cols], rs_stride / cf_stride elements apart; NULL: q8 block.
+    const uint16_t *rs;
+    const uint16_t *cf;
+    long long rs_stride, cf_stride;
 };
 
 // Experts [0, experts); those with no entries are skipped.

@@ -120,9 +120,11 @@ __device__ __forceinline__ bf16x8 q8_to_bf16(uint32_t w0, uint32_t w1) {
 // it waits for any of them (the requests queue behind the weight stream).
 constexpr int kStageBatch = 6;
 
+// cf: the expert's binary16 column field (q8_2f), multiplied into the staged
+// activations; NULL for the block format.
 template <int MT>
 __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *list, int cnt, int cb0,
-                                          int kp, char *lds) {
+                                          int kp, char *lds, const uint16_t *cf) {
     const int nb = P.cols >> 5;
     const int kc = 2 * kp;
     const int pitch = 64 * kc + 16;
@@ -131,6 +133,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
     const int total = (cnt + 1) * 4 * kc;
     for (int base = 0; base < total; base += kStageBatch * kExpThreads) {
         float4 xa[kStageBatch][2];
+        u32x4 ca[kStageBatch];
 #pragma unroll
         for (int k = 0; k < kStageBatch; ++k) {
             const int it = base + k * kExpThreads + threadIdx.x;
@@ -138,11 +141,13 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
             const int qb = it - r * 4 * kc;
             const int blk = cb0 + (qb >> 2);
             xa[k][0] = xa[k][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            ca[k] = u32x4{0u, 0u, 0u, 0u};
             if (it < total && r < cnt && blk < nb) {
                 const long long src = list[r] / P.src_div;
                 const float4 *xp = reinterpret_cast<const float4 *>(P.x + src * P.ldx + 32 * blk + 8 * (qb & 3));
                 xa[k][0] = xp[0];
                 xa[k][1] = xp[1];
+                if (cf) ca[k] = *reinterpret_cast<const u32x4 *>(cf + 32 * blk + 8 * (qb & 3));
             }
         }
 #pragma unroll
@@ -154,8 +159,14 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
             const int r = it / (4 * kc);
             const int qb = it - r * 4 * kc;
             const int bl = qb >> 2, i = qb & 3;
-            const float v[8] = {xa[k][0].x, xa[k][0].y, xa[k][0].z, xa[k][0].w,
-                                xa[k][1].x, xa[k][1].y, xa[k][1].z, xa[k][1].w};
+            float v[8] = {xa[k][0].x, xa[k][0].y, xa[k][0].z, xa[k][0].w,
+                          xa[k][1].x, xa[k][1].y, xa[k][1].z, xa[k][1].w};
+            if (cf) {
+                _Float16 c[8];
+                __builtin_memcpy(c, &ca[k], 16);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] *= (float)c[j];
+            }
             __bf16 hi[8], lo[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -196,7 +207,7 @@ struct ExpTgt {
 // take more than one chunk), its steps, and its outputs.  The weight ring and
 // the scale windows come in holding this pass's first steps and leave holding
 // those of the pass after it (target tn).
-template <int MT, int D, int AL>
+template <int MT, int D, int AL, bool Q82>
 __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int cnt, int rb, bool fresh,
                                          const ExpTgt &tc, const ExpTgt &tn, u32x4 (&wq)[D][kExpTiles],
                                          float (&sw)[kExpTiles][D / 2], float (&bw)[kExpTiles][D / 2],
@@ -212,7 +223,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     const int np = (nb + 1) >> 1;
     const int npp = (np + D - 1) / D * D;
     const int q_bytes = P.rows * P.cols;
-    const int s_bytes = P.rows * nb * 4;
+    const int s_bytes = Q82 ? 0 : P.rows * nb * 4;  // q8_2f: no block factors, the windows move nothing
     const int32_t *list = P.lists + (long long)e * P.cap + m0;
     const int kp = exp_chunk_pairs(cnt, MT, D, np);
     const bool chunked = kp < npp;
@@ -329,10 +340,17 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float x = acc[k][mt][v];
-                    x = fmaf(s[k].x, d0[v], x);
-                    x = fmaf(s[k].y, d1[v], x);
-                    x = fmaf(b[k].x, xs0[v], x);
-                    x = fmaf(b[k].y, xs1[v], x);
+                    if constexpr (Q82) {
+                        (void)xs0;
+                        (void)xs1;
+                        x += d0[v];
+                        x += d1[v];
+                    } else {
+                        x = fmaf(s[k].x, d0[v], x);
+                        x = fmaf(s[k].y, d1[v], x);
+                        x = fmaf(b[k].x, xs0[v], x);
+                        x = fmaf(b[k].y, xs1[v], x);
+                    }
                     acc[k][mt][v] = x;
                 }
             }
@@ -346,7 +364,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     for (int c0 = 0; c0 < npp; c0 += kp) {
         if (c0 > 0 || chunked || fresh) {
             __syncthreads();
-            exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds);
+            exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds, Q82 ? P.cf + (long long)e * P.cf_stride : nullptr);
             __syncthreads();
         }
         const int c1 = min(npp, c0 + kp);
@@ -379,11 +397,14 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     for (int k = 0; k < T; ++k) {
         const int r = rb * kExpRows + (wave * T + k) * 16 + i16;
         if (r >= P.rows) continue;
+        // q8_2f: the row scale multiplies the finished sum.
+        const float rsc = Q82 ? (float)__builtin_bit_cast(_Float16, P.rs[(long long)e * P.rs_stride + r]) : 1.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (orow[mt][v] >= 0) P.out[(long long)orow[mt][v] * P.ldo + r] = apply_act(P.act, acc[k][mt][v]);
+                if (orow[mt][v] >= 0)
+                    P.out[(long long)orow[mt][v] * P.ldo + r] = apply_act(P.act, Q82 ? acc[k][mt][v] * rsc : acc[k][mt][v]);
     }
 }
 
@@ -393,7 +414,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 // once for all of that expert's items in its share, and its weight stream
 // runs from one item into the next without draining.  An expert with more
 // than kExpGroup entries takes one pass per group of kExpGroup over each item.
-template <int AL>
+template <int AL, bool Q82>
 __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
     extern __shared__ u32x4 exp_lds[];
     __shared__ int act[kExpMaxExperts];
@@ -450,8 +471,8 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
     float sw[T][V], bw[T][V], swn[T][V], bwn[T][V];
     {
         const ExpTgt t0 = target(i0);
-        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t0.s, P.rows * nb * 4);
-        const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t0.b, P.rows * nb * 4);
+        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t0.s, Q82 ? 0 : P.rows * nb * 4);
+        const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t0.b, Q82 ? 0 : P.rows * nb * 4);
 #pragma unroll
         for (int k = 0; k < T; ++k)
 #pragma unroll
@@ -483,9 +504,9 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
             const bool fresh = e != prev || groups > 1;
             const ExpTgt &nx = gi + 1 < groups ? tc : tn;
             if (kExpGroup <= 16 || cg <= 16)
-                exp_item<1, D, AL>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+                exp_item<1, D, AL, Q82>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
             else
-                exp_item<2, D, AL>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+                exp_item<2, D, AL, Q82>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
         }
         prev = e;
     }
@@ -502,12 +523,12 @@ static int exp_grid() {
     return cus;
 }
 
-template <int AL>
+template <int AL, bool Q82 = false>
 static int launch_bank(const ExpertBank &P, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL, Q82>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kExpLds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL(expert_bank_kernel<AL>, dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
+    hipLaunchKernelGGL((expert_bank_kernel<AL, Q82>), dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
     return launch_status();
 }
 
@@ -515,8 +536,13 @@ int launch_expert_bank(const ExpertBank &P, hipStream_t s) {
     if (P.rows < 1 || P.cols < 32 || P.cols % 32 || P.cap > kExpMaxCnt) return PG_EUNSUPPORTED;
     if (P.experts < 1 || P.experts > kExpMaxExperts) return PG_EUNSUPPORTED;
     if ((long long)P.rows * P.cols >= (1ll << 31)) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
-    // Widest scale / bias loads: a row's blocks must start on that boundary.
     const int nb = P.cols / 32;
+    if (P.rs) {  // q8_2f: the (empty) window loads take the widest form the block count allows
+        if (!P.cf) return PG_EINVAL;
+        return nb % 4 == 0 ? launch_bank<4, true>(P, s) : nb % 2 == 0 ? launch_bank<2, true>(P, s)
+                                                                       : launch_bank<1, true>(P, s);
+    }
+    // Widest scale / bias loads: a row's blocks must start on that boundary.
     const uintptr_t a = (uintptr_t)P.scale | (uintptr_t)P.bias;
     if (nb % 4 == 0 && (a & 15) == 0) return launch_bank<4>(P, s);
     if (nb % 2 == 0 && (a & 7) == 0) return launch_bank<2>(P, s);
@@ -525,3 +551,38 @@ int launch_expert_bank(const ExpertBank &P, hipStream_t s) {
 }
 
 }  // namespace pg
+
+using namespace pg;
+
+// The q8_2f expert bank over a pass (nemotron_prefill.rs, the q8_2f bank
+// payload: int8 body, f16 row scales, f16 column field per expert).
+extern "C" int expert_bank_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *col_field, int32_t E,
+                               int32_t rows, int32_t cols, const float *x, int64_t ldx, int32_t src_div,
+                               const int32_t *counts, const int32_t *lists, int32_t cap, float *out, int64_t ldo,
+                               int32_t act, pg_stream_t stream) {
+    if (!q || !row_scale || !col_field || !x || !counts || !lists || !out) return PG_EINVAL;
+    if (E <= 0 || rows <= 0 || cols <= 0 || cap <= 0 || src_div <= 0 || ldx < cols || ldo < rows) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(x) || !aligned16(col_field) || ldx % 4 || ((uintptr_t)row_scale & 1))
+        return PG_EINVAL;
+    ExpertBank P{};
+    P.q = q;
+    P.rows = rows;
+    P.cols = cols;
+    P.q_stride = (long long)rows * cols;
+    P.x = x;
+    P.ldx = ldx;
+    P.src_div = src_div;
+    P.counts = counts;
+    P.lists = lists;
+    P.cap = cap;
+    P.experts = E;
+    P.out = out;
+    P.ldo = ldo;
+    P.act = act;
+    P.rs = row_scale;
+    P.cf = col_field;
+    P.rs_stride = rows;
+    P.cf_stride = cols;
+    return launch_expert_bank(P, as_stream(stream));
+}

@@ -173,3 +173,64 @@ def test_prefill_q82_errors(pg):
     assert call(xp=P(X, 4)) == pg.PG_EINVAL
     assert call(wsb=need - 1) == pg.PG_EWORKSPACE
     assert L.prefill_gemm_q82(P(q), None, P(cf), rows, cols, P(X), 64, P(Y), 0, P(ws), need, s) == pg.PG_EINVAL
+
+
+# ------------------------------------------------------------------ expert_bank_q82
+
+def _bank_case(rng, E, rows, cols, n, k):
+    """q8_2f experts, n positions each choosing k distinct experts (the grouping from the
+    oracle), x [n][cols]."""
+    ms = [synth.q82(rng, rows, cols) for _ in range(E)]
+    sel = np.stack([rng.choice(E, k, replace=False) for _ in range(n)]).astype(np.int32)
+    return ms, sel, synth.normal(rng, (n, cols))
+
+
+@pytest.mark.parametrize("E,rows,cols,n,k,act", [(6, 320, 256, 40, 2, 0), (6, 320, 256, 40, 2, 1),
+                                                 (3, 100, 96, 64, 3, 1), (1, 33, 32, 1, 1, 0),
+                                                 (16, 1856, 2688, 64, 6, 1)])
+def test_expert_bank_q82_parity(pg, oracle, E, rows, cols, n, k, act):
+    """Each listed entry's row against the oracle's q8_2f product of its expert (x row j / k)."""
+    _case(f"expert_bank_q82 E={E} {rows}x{cols} n={n} k={k} act={act}")
+    rng = np.random.default_rng(E * rows + cols + n + act)
+    ms, sel, X = _bank_case(rng, E, rows, cols, n, k)
+    counts, lists = oracle.group(sel, E)
+    dev = lambda a: torch.as_tensor(np.ascontiguousarray(a)).cuda()
+    out = pg.expert_bank_q82(dev(np.stack([m.q for m in ms])), dev(np.stack([m.rs for m in ms])),
+                             dev(np.stack([m.cf for m in ms])), dev(X), dev(counts),
+                             dev(np.maximum(lists, 0).astype(np.int32)), src_div=k, act=act, n_out=n * k)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    worst = 0.0
+    for e in range(E):
+        js = lists[e, :counts[e]]
+        if len(js) == 0:
+            continue
+        ref = oracle.gemm_q82(ms[e].q, ms[e].rs, ms[e].cf, X[js // k], act=act)
+        worst = max(worst, oracle.rel_err(out[js], ref))
+    print(f"[info] worst rel err {worst:.2e}", flush=True)
+    assert worst <= TOL_Q8
+
+
+def test_expert_bank_q82_exact_bitwise(pg, oracle):
+    """Power-of-two scales and column field with integer x: exact on both sides."""
+    _case("expert_bank_q82 exact")
+    rng = np.random.default_rng(19)
+    E, rows, cols, n, k = 5, 200, 512, 24, 2
+    ms = []
+    for _ in range(E):
+        q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+        rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
+        cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
+        ms.append(synth.Q82(q, rs, cf))
+    sel = np.stack([rng.choice(E, k, replace=False) for _ in range(n)]).astype(np.int32)
+    X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
+    counts, lists = oracle.group(sel, E)
+    dev = lambda a: torch.as_tensor(np.ascontiguousarray(a)).cuda()
+    out = pg.expert_bank_q82(dev(np.stack([m.q for m in ms])), dev(np.stack([m.rs for m in ms])),
+                             dev(np.stack([m.cf for m in ms])), dev(X), dev(counts),
+                             dev(np.maximum(lists, 0).astype(np.int32)), src_div=k, n_out=n * k)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    for e in range(E):
+        js = lists[e, :counts[e]]
+        assert np.array_equal(out[js], oracle.gemm_q82(ms[e].q, ms[e].rs, ms[e].cf, X[js // k])), e
