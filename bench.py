@@ -308,6 +308,43 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
             "argmax_GB_s": round(64 * 32000 * 4 / (am * 1e-3) / 1e9, 1)}
 
 
+def component_q82_bank(torch, pg, synth, reps=10, host_experts=16):
+    """The q8_2f expert bank at the MoE pass's up shape: 128 experts of 1856 x 2688, the
+    top 6 of the MoE component's router logits at 64 positions, relu^2; the experts are 16
+    drawn on the host and device copies at other addresses."""
+    import numpy as np
+    c = synth.moe(0)
+    E, n, k, H, I = 128, 64, c["top_k"], 2688, 1856
+    rng = synth.streams(23, host_experts)
+    ms = [synth.q82(rng[i], I, H) for i in range(host_experts)]
+    q = torch.empty(E, I, H, dtype=torch.int8, device="cuda")
+    rs = torch.empty(E, I, dtype=torch.float16, device="cuda")
+    cf = torch.empty(E, H, dtype=torch.float16, device="cuda")
+    for e in range(E):
+        m = ms[e % host_experts]
+        q[e].copy_(torch.as_tensor(m.q))
+        rs[e].copy_(torch.as_tensor(m.rs))
+        cf[e].copy_(torch.as_tensor(m.cf))
+    X = to_dev(torch, c["X"])
+    logits = X @ to_dev(torch, c["Wr"]).t()
+    sel = torch.topk(logits, k, dim=1).indices.to(torch.int32).cpu().numpy()
+    counts = np.bincount(sel.reshape(-1), minlength=E).astype(np.int32)
+    lists = np.zeros((E, n), np.int32)
+    fill = np.zeros(E, np.int64)
+    for j, e in enumerate(sel.reshape(-1)):
+        lists[e, fill[e]] = j
+        fill[e] += 1
+    cnt, lst = to_dev(torch, counts), to_dev(torch, lists)
+    out = torch.empty(n * k, I, device="cuda")
+    t = time_graphs(torch, [one_graph(torch, [lambda: pg.expert_bank_q82(q, rs, cf, X, cnt, lst, src_div=k, act=1,
+                                                                          out=out)] * reps)], 3) / reps
+    active = int((counts > 0).sum())
+    nbytes = active * (I * H + 2 * I + 2 * H)
+    return {"workload": "q8_2f expert bank, MoE up shape: 128 experts 2688->1856, 64 positions top-6, relu^2",
+            "active_experts": active, "us": round(t * 1e3, 2), "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def component_attn(torch, pg, synth, reps=20):
     """Causal GQA prefill attention (32 query heads, 8 KV heads of 128) over a 64-position
     pass, first in its context and last in a 4096-position one: the KV append plus the
@@ -513,7 +550,8 @@ def main():
     if args.formats_only:
         print(json.dumps({"q82_gemv_frame_shapes": component_q82(torch, pg, synth),
                           "q4tp_gemv_frame_shapes": component_q4tp_argmax(torch, pg, synth),
-                          "prefill_attention": component_attn(torch, pg, synth)}), flush=True)
+                          "prefill_attention": component_attn(torch, pg, synth),
+                          "q82_expert_bank": component_q82_bank(torch, pg, synth)}), flush=True)
         return
 
     log("building inputs ...")
@@ -591,6 +629,7 @@ def main():
         comp["q82_gemv_frame_shapes"] = component_q82(torch, pg, synth)
         comp["q4tp_gemv_frame_shapes"] = component_q4tp_argmax(torch, pg, synth)
         comp["prefill_attention"] = component_attn(torch, pg, synth)
+        comp["q82_expert_bank"] = component_q82_bank(torch, pg, synth)
         result["components"] = comp
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
