@@ -12,6 +12,7 @@
 // which is sum_c (scale*q + bias)[r][c] * x[c] regrouped; the segment sums of
 // x are computed once per workgroup.
 #include <algorithm>
+#include <type_traits>
 
 #include "pg_device.h"
 #include "pg_host.h"
@@ -773,12 +774,17 @@ extern "C" int gemv_q82(const int8_t *q, const uint16_t *row_scale, const uint16
     if (cols % 16 || cols > 32768) return PG_EUNSUPPORTED;
     if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
     const size_t lds = (size_t)ceil_div(cols / 16, 64) * 4 * 64 * sizeof(float4);
-    static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q82_kernel<kQ8Rw, kQ8U>),
-                                    (size_t)ceil_div(32768 / 16, 64) * 4 * 64 * sizeof(float4));
-    if (ok != PG_OK) return PG_ELAUNCH;
-    hipLaunchKernelGGL((gemv_q82_kernel<kQ8Rw, kQ8U>), dim3(gemv_grid(rows, kQ8Rw)), dim3(kGemvThreads), lds,
-                       as_stream(stream), q, row_scale, col_field, rows, cols, x, y, act);
-    return launch_status();
+    auto go = [&](auto utag) {
+        constexpr int U = decltype(utag)::value;
+        static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_q82_kernel<kQ8Rw, U>),
+                                        (size_t)ceil_div(32768 / 16, 64) * 4 * 64 * sizeof(float4));
+        if (ok != PG_OK) return (int)PG_ELAUNCH;
+        hipLaunchKernelGGL((gemv_q82_kernel<kQ8Rw, U>), dim3(gemv_grid(rows, kQ8Rw)), dim3(kGemvThreads), lds,
+                           as_stream(stream), q, row_scale, col_field, rows, cols, x, y, act);
+        return launch_status();
+    };
+    // Steps per weight batch as for the block format (longer rows take more).
+    return cols > kQ8LongRow ? go(std::integral_constant<int, kQ8ULong>{}) : go(std::integral_constant<int, kQ8U>{});
 }
 
 extern "C" int gemv_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t rows,
