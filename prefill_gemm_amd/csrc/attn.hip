@@ -82,7 +82,7 @@ struct AttnCfg {
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
     const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc, int n, int pos0,
-    int nh, int nkv, float scale, int chunk, float *__restrict__ part) {
+    int nh, int nkv, float scale, int chunk, float *__restrict__ part, float *__restrict__ out) {
     using C = AttnCfg<HD>;
     constexpr int NC = HD / 16;   // 16-dim chunks (q . k) = 16-dim output blocks (p . V)
     constexpr int NKB = kAttnKT / 16;
@@ -222,6 +222,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
         const int i = kAttnQW * wave + 4 * kg + v;
         const int b = b0 + i / rep, h = g * rep + i % rep;
         if (b >= n) continue;
+        if (out) {  // one split: the result itself, no merge
+            float *dst = out + ((long long)b * nh + h) * HD;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) dst[16 * c + r16] = o[c][v] / lsum;
+            continue;
+        }
         float *dst = part + (((long long)split * n + b) * nh + h) * (HD + 2);
 #pragma unroll
         for (int c = 0; c < NC; ++c) dst[16 * c + r16] = o[c][v];
@@ -303,10 +309,11 @@ static int launch_attn(const float *q, const float *kc, const float *vc, int n, 
     if (attr != hipSuccess) return PG_ELAUNCH;
     const int rep = nh / nkv;
     const dim3 grid(splits, ceil_div(n, kAttnQ / rep), nkv);
+    // A single split writes the output itself (no merge launch).
     hipLaunchKernelGGL(attn_prefill_kernel<HD>, grid, dim3(kAttnThreads), lds, s, q, kc, vc, n, pos0, nh, nkv, scale,
-                       chunk, part);
+                       chunk, part, splits == 1 ? o : nullptr);
     int rc = launch_status();
-    if (rc) return rc;
+    if (rc || splits == 1) return rc;
     hipLaunchKernelGGL(attn_merge_kernel<HD>, dim3(ceil_div(n * nh, kAttnWaves)), dim3(kAttnThreads), 0, s, part, n,
                        nh, splits, o);
     return launch_status();
