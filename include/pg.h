@@ -378,7 +378,10 @@ int add_rmsnorm(float *h, const float *delta, int32_t delta_stride, const float 
  *   h [n][H] f32 in/out, w_norm [H] f32, out [n][H] f32,
  *   logits [n][E] f32, sel [n][top_k] int32, route_w [n][top_k] f32,
  *   counts [E] int32, lists [E][n] int32 (entries past counts[e] unspecified),
- *   workspace of at least moe_grouped_workspace_bytes(n, H, I, E, top_k) bytes.
+ *   workspace of at least moe_grouped_workspace_bytes(n, H, I, E, top_k) bytes
+ *   (16-byte aligned).  On return the workspace starts with the per-entry
+ *   expert outputs: u [n*top_k][I] f32 at byte 0, then d [n*top_k][H] f32 at
+ *   byte round_up(n*top_k*I*4, 256); row j is entry j = b*top_k + t.
  * PG_EUNSUPPORTED: n < 1 or n > 64, H % 32 or I % 32 != 0, H > 16384,
  *   E < 1 or E > 1024, top_k < 1 or top_k > min(E, 16).
  */
@@ -393,11 +396,18 @@ size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, int32_t E, i
 /*
  * moe_route_sigmoid — the sigmoid router with a selection bias
  * (nemotron_prefill.rs, `pb_route`), per position b of n:
- *     c[e]          = sigmoid(logits[b][e]) + router_bias[e]       (f32)
+ *     c[e]          = sigmoid32(logits[b][e]) + router_bias[e]     (one f32 add)
  *     sel[b][t]     = the t-th largest c (t < top_k), lower index wins a tie
- *     route_w[b][t] = sigmoid(logits[b][sel]) / den * scale,
- *     den           = sum_t sigmoid(logits[b][sel[b][t]]) + 1e-20 if renorm, else 1.
- * The bias steers the choice only.  sigmoid(x) = 1 / (1 + exp(-x)) in f32.
+ *     route_w[b][t] = sigmoid32(logits[b][sel]) / den * scale,
+ *     den           = sum_t sigmoid32(logits[b][sel[b][t]]) + 1e-20 if renorm, else 1.
+ * The bias steers the choice only.  sigmoid32 is one fixed sequence of
+ * correctly rounded binary32 operations, so the choice it decides is
+ * reproducible on any IEEE machine: x = clamp(-l, -80, 80);
+ * k = rint(x * f32(log2 e)); r = fma(-k, ln2_tail, fma(-k, ln2_head, x)) with
+ * ln2_head = 0.693145751953125 and ln2_tail = f32(ln 2 - ln2_head) (the
+ * Cody-Waite reduction); p = the Taylor polynomial sum_{i<=7} r^i / i! by
+ * Horner's rule from the r^7 term, one fma a term, coefficients f32(1/i!);
+ * sigmoid32 = 1 / (1 + ldexp(p, k)).  The weights use the same values.
  *   logits [n][E] f32, router_bias [E] f32, sel [n][top_k] int32, route_w [n][top_k] f32.
  * PG_EUNSUPPORTED: E > 1024, top_k > min(E, 16).
  */

@@ -70,6 +70,11 @@ def _declare(L):
                                              _P, _P, _P, _P, _P, _P, _P, _P]
     L.oracle_moe_combine.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _D, _P, _P]
     L.oracle_route_sigmoid.argtypes = [_P, _P, _I, _I, _I, _i, _D, _P, _P, _P]
+    L.oracle_exp_f32.argtypes = [ctypes.c_float]
+    L.oracle_exp_f32.restype = ctypes.c_float
+    L.oracle_sigmoid_f32.argtypes = [ctypes.c_float]
+    L.oracle_sigmoid_f32.restype = ctypes.c_float
+    L.oracle_sigmoid_f32_array.argtypes = [_P, _I, _P]
     L.oracle_threads.restype = _i
 
 
@@ -283,17 +288,31 @@ def route(logits_f32, k: int, renorm: int = 0):
     return sel, rw, probs
 
 
+def exp_f32(x) -> np.ndarray:
+    """exp in the fixed binary32 sequence the sigmoid router uses (see oracle.c)."""
+    x = _c(np.atleast_1d(x), np.float32)
+    return np.array([lib().oracle_exp_f32(float(v)) for v in x], np.float32)
+
+
+def sigmoid_f32(l) -> np.ndarray:
+    """sigma(l) = 1 / (1 + exp(-l)) as one fixed sequence of binary32 operations (see oracle.c)."""
+    l = _c(np.atleast_1d(l), np.float32)
+    out = np.empty(l.shape, np.float32)
+    lib().oracle_sigmoid_f32_array(_p(l), l.size, _p(out))
+    return out
+
+
 def route_sigmoid(logits_f32, bias, k: int, norm: int = 1, scale: float = 1.0):
-    """(sel int32 [n][k], rw f64 [n][k], choice f64 [n][E]): choice = sigmoid(l) + bias,
-    top k by choice (lower index on a tie), rw = sigmoid(l_sel) / den * scale with
-    den = sum_t sigmoid(l_sel) + 1e-20 when norm, else 1."""
+    """(sel int32 [n][k], rw f64 [n][k], choice f32 [n][E]): choice = sigmoid_f32(l) + bias
+    (binary32), top k by choice (lower index on a tie), rw = sigmoid(l_sel) / den * scale in
+    f64 with den = sum_t sigmoid(l_sel) + 1e-20 when norm, else 1."""
     L = _c(np.atleast_2d(logits_f32), np.float32)
     n, E = L.shape
     bias = _c(bias, np.float32)
     assert bias.shape == (E,) and 1 <= k <= E
     sel = np.empty((n, k), np.int32)
     rw = np.empty((n, k), np.float64)
-    choice = np.empty((n, E), np.float64)
+    choice = np.empty((n, E), np.float32)
     lib().oracle_route_sigmoid(_p(L), _p(bias), n, E, k, int(norm), float(scale), _p(sel), _p(rw), _p(choice))
     return sel, rw, choice
 

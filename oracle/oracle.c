@@ -7,10 +7,12 @@
  *
  * Every result is the plain definition written out in double precision from
  * the f32 / int8 / binary16 inputs: no blocking, no fusion, no reordering
- * beyond what the definition states.  The one exception is the f32 router
- * logit (oracle_router_logits_f32): an f32 value that decides an integer (the
- * chosen experts) is computed in f32, in the summation order the device uses,
- * so both sides take that decision on identical bits.
+ * beyond what the definition states.  The exceptions are the two binary32
+ * values that decide an integer (the chosen experts): the f32 router logit
+ * (oracle_router_logits_f32), summed in a fixed order, and the sigmoid
+ * router's choice value (oracle_sigmoid_f32), one fixed sequence of binary32
+ * operations; both are defined so that the device and this oracle take the
+ * decision on identical bits.
  *
  * Sources (cortiq-engine docs.rs source pages):
  *  - weights stay packed on the device and are decoded inside the product:
@@ -369,21 +371,71 @@ void oracle_route(const float *logits, int64_t n, int64_t E, int64_t k, int reno
     free(taken);
 }
 
+/* The sigmoid as one fixed sequence of IEEE binary32 operations, so that the
+ * expert choice it decides is taken on the same bits wherever the sequence is
+ * carried out (nemotron_prefill.rs, `pb_route`, takes its choice value in f32).
+ *
+ * exp(x) by the argument reduction of W. J. Cody and W. Waite, "Software
+ * Manual for the Elementary Functions" (1980): x = k ln2 + r with
+ * k = rint(x log2 e) and r = x - k ln2 taken in two steps with ln2 split into
+ * a head of 16 significant bits and the binary32 rounding of the remainder;
+ * e^r by its Taylor series through r^7 (|r| <= ln2 / 2, truncation below
+ * 1e-8 relative), evaluated by Horner's rule with one fused multiply-add a
+ * term; then e^x = 2^k e^r.  x is first clamped to [-80, 80], so that no
+ * value in the sequence below is subnormal or infinite (sigma(l) for
+ * |l| > 80 then differs from the true value by less than 2e-35).
+ * sigma(l) = 1 / (1 + exp(-l)): one binary32 add and one correctly rounded
+ * binary32 divide. */
+static const float kLog2e = 1.44269502162933349609375f;     /* binary32(log2 e) */
+static const float kLn2Hi = 0.693145751953125f;             /* ln 2, 16 significant bits */
+static const float kLn2Lo = 1.428606765330187045037746429443359375e-06f; /* binary32(ln 2 - head) */
+
+float oracle_exp_f32(float x) {
+    x = fminf(fmaxf(x, -80.0f), 80.0f);
+    const float k = rintf(x * kLog2e);
+    float r = fmaf(-k, kLn2Hi, x);
+    r = fmaf(-k, kLn2Lo, r);
+    /* 1/n!, n = 7 .. 0, each rounded to binary32 */
+    float p = 1.0f / 5040.0f;
+    p = fmaf(p, r, 1.0f / 720.0f);
+    p = fmaf(p, r, 1.0f / 120.0f);
+    p = fmaf(p, r, 1.0f / 24.0f);
+    p = fmaf(p, r, 1.0f / 6.0f);
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)k);
+}
+
+float oracle_sigmoid_f32(float l) {
+    const float e = oracle_exp_f32(-l);
+    const float d = 1.0f + e;
+    return 1.0f / d;
+}
+
+void oracle_sigmoid_f32_array(const float *l, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_sigmoid_f32(l[i]);
+}
+
 /* The sigmoid router with a selection bias (nemotron_prefill.rs, `pb_route`):
- * per position b the choice value of expert e is
- *     c_e = sigma(l_e) + bias[e],  sigma(x) = 1 / (1 + exp(-x)),
- * and k rounds each take the largest remaining c (the lower index on a tie) and
- * remove it.  The bias steers the choice only; the weight of slot t is
- *     rw[b][t] = sigma(l_sel) / den * scale,
+ * per position b the choice value of expert e is the binary32 value
+ *     c_e = sigma32(l_e) + bias[e]   (one binary32 add),
+ * with sigma32 the fixed-sequence sigmoid above, and k rounds each take the
+ * largest remaining c (the lower index on a tie) and remove it.  The bias
+ * steers the choice only; the weight of slot t is the definition in f64,
+ *     rw[b][t] = sigma(l_sel) / den * scale,  sigma(x) = 1 / (1 + exp(-x)),
  *     den = sum_t sigma(l_sel[t]) + 1e-20 when norm, else 1.
- * All in f64 from the f32 logits; choice[b][e] receives c_e. */
+ * choice[b][e] receives c_e. */
 void oracle_route_sigmoid(const float *logits, const float *bias, int64_t n, int64_t E, int64_t k,
-                          int norm, double scale, int32_t *sel, double *rw, double *choice) {
+                          int norm, double scale, int32_t *sel, double *rw, float *choice) {
     char *taken = (char *)malloc((size_t)E);
     for (int64_t b = 0; b < n; ++b) {
         const float *l = logits + b * E;
-        double *c = choice + b * E;
-        for (int64_t e = 0; e < E; ++e) c[e] = 1.0 / (1.0 + exp(-(double)l[e])) + (double)bias[e];
+        float *c = choice + b * E;
+        for (int64_t e = 0; e < E; ++e) {
+            const float sg = oracle_sigmoid_f32(l[e]);
+            c[e] = sg + bias[e];
+        }
         memset(taken, 0, (size_t)E);
         double sum = 0.0;
         for (int64_t t = 0; t < k; ++t) {

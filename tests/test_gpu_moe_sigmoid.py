@@ -2,15 +2,13 @@
 and a shared-expert term (moe_grouped_sigmoid), against the CPU oracle through
 the C ABI.
 
-The choice value sigmoid(l) + bias is an f32 value built on exp, whose last bit
-may differ between the device and the host library.  So where the oracle's
-(binary64) choice values of a position leave every gap among its top k + 1
-experts wider than 1e-5, the device's selection must equal the oracle's exactly
-(order included); elsewhere it must be a valid top k: distinct experts whose
-oracle choice values equal the oracle's top k values to 1e-5.  The tests also
-require that most positions take the exact comparison.  Weights, grouping and
-the pass's outputs are then checked against the oracle on the device's
-selection."""
+The choice value sigmoid(l) + bias decides integers, so both sides take it as
+the same fixed sequence of correctly rounded binary32 operations (a Cody-Waite
+reduced exp with a Taylor polynomial, one add, one divide, then the bias add);
+the selection must equal the oracle's bit for bit, order included, at every
+position.  The weights are held to the f32 tolerance against the f64
+definition; grouping is exact, and the pass's outputs are held to the q8
+tolerance on every position."""
 import ctypes
 
 import numpy as np
@@ -22,8 +20,6 @@ from helpers import TOL_F32, TOL_Q8, q8_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-
-GAP = 1e-5
 
 
 @pytest.fixture(scope="module")
@@ -42,21 +38,11 @@ def _sigmoid(x):
 
 
 def _check_selection(oracle, L, bias, k, norm, scale, sel, rw):
-    """Returns the fraction of positions compared exactly; asserts the rules above."""
-    sel_ref, rw_ref, choice = oracle.route_sigmoid(L, bias, k, norm, scale)
-    exact = 0
-    for b in range(L.shape[0]):
-        c = np.sort(choice[b])[::-1][:k + 1]
-        if len(c) <= k or np.min(c[:k] - c[1:k + 1]) > GAP:
-            assert np.array_equal(sel[b], sel_ref[b]), (b, sel[b], sel_ref[b])
-            exact += 1
-        else:
-            assert len(set(sel[b].tolist())) == k
-            np.testing.assert_allclose(np.sort(choice[b, sel[b]])[::-1], np.sort(choice[b])[::-1][:k], atol=GAP)
-    s = _sigmoid(np.take_along_axis(L.astype(np.float64), sel.astype(np.int64), 1))
-    want = s / ((s.sum(1, keepdims=True) + 1e-20) if norm else 1.0) * scale
-    assert oracle.rel_err(rw, want) <= TOL_F32
-    return exact / L.shape[0]
+    """Selection equal to the oracle's at every position; weights at the f32 tolerance."""
+    sel_ref, rw_ref, _ = oracle.route_sigmoid(L, bias, k, norm, scale)
+    bad = np.flatnonzero(~np.all(sel == sel_ref, axis=1))
+    assert bad.size == 0, (bad[:4], sel[bad[:4]], sel_ref[bad[:4]])
+    assert oracle.rel_err(rw, rw_ref) <= TOL_F32
 
 
 @pytest.mark.parametrize("E,k", [(6, 2), (64, 6), (128, 6), (256, 8), (1000, 16), (16, 16)])
@@ -69,9 +55,23 @@ def test_route_sigmoid_parity(pg, oracle, E, k, norm):
     bias = synth.router_bias(rng, E)
     sel, rw = pg.moe_route_sigmoid(to_dev(L, torch), to_dev(bias, torch), k, renorm=norm, scale=2.5)
     torch.cuda.synchronize()
-    frac = _check_selection(oracle, L, bias, k, norm, 2.5, sel.cpu().numpy(), rw.cpu().numpy())
-    print(f"[info] exact positions {frac:.2f}", flush=True)
-    assert frac >= 0.9
+    _check_selection(oracle, L, bias, k, norm, 2.5, sel.cpu().numpy(), rw.cpu().numpy())
+
+
+def test_route_sigmoid_wide_logits(pg, oracle):
+    """Logits over [-120, 120] (past the clamp at 80 on both sides, and where sigmoid
+    saturates), many near-equal values: still the oracle's selection bit for bit."""
+    _case("route_sigmoid wide logits")
+    rng = np.random.default_rng(77)
+    n, E, k = 64, 256, 8
+    L = (rng.standard_normal((n, E)) * 40.0).astype(np.float32)
+    L[:, :32] = rng.uniform(-120, 120, (n, 32)).astype(np.float32)
+    L[:, 32:64] = (L[:, 64:96] + np.float32(1e-6)).astype(np.float32)   # near ties
+    bias = synth.router_bias(rng, E)
+    bias[:16] = 0.0
+    sel, rw = pg.moe_route_sigmoid(to_dev(L, torch), to_dev(bias, torch), k, renorm=1, scale=1.0)
+    torch.cuda.synchronize()
+    _check_selection(oracle, L, bias, k, 1, 1.0, sel.cpu().numpy(), rw.cpu().numpy())
 
 
 def test_route_sigmoid_exact_ties(pg, oracle):
@@ -109,8 +109,7 @@ def _check_pass(oracle, c, o, bias, norm, scale, shared, pos=None):
     E = c["Wr"].shape[0]
     L = oracle.router_logits_f32(c["X"], c["Wr"])
     assert np.array_equal(o["logits"].view(np.uint32), L.view(np.uint32)), "logits bits"
-    frac = _check_selection(oracle, L, bias, c["top_k"], norm, scale, o["sel"], o["route_w"])
-    assert frac >= 0.9
+    _check_selection(oracle, L, bias, c["top_k"], norm, scale, o["sel"], o["route_w"])
     counts, lists = oracle.group(o["sel"], E)
     assert np.array_equal(o["counts"], counts), "counts"
     for e in range(E):
@@ -145,7 +144,7 @@ def test_moe_sigmoid_small(pg, oracle, shape, norm, shared):
 
 def test_moe_sigmoid_full_128_experts(pg, oracle):
     """The 64-position, 128-expert (2688 -> 1856 -> 2688, top-6) pass with the sigmoid router
-    and a shared term; residual and norm outputs on a sample of positions."""
+    and a shared term; residual and norm outputs on every position."""
     _case("moe sigmoid full")
     c = synth.moe(0)
     rng = np.random.default_rng(21)
@@ -153,7 +152,7 @@ def test_moe_sigmoid_full_128_experts(pg, oracle):
     sh = synth.normal(rng, c["h"].shape)
     o = _run(pg, c, bias, 1, 2.5, sh)
     print(f"[info] distinct experts selected: {int((o['counts'] > 0).sum())}", flush=True)
-    _check_pass(oracle, c, o, bias, 1, 2.5, sh, pos=np.sort(rng.choice(64, 6, replace=False)))
+    _check_pass(oracle, c, o, bias, 1, 2.5, sh)
 
 
 def test_moe_sigmoid_errors(pg):

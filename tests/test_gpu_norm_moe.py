@@ -3,12 +3,12 @@
 Routing is compared bit for bit (f32 logits in the shared fixed order, the
 selected experts, the per-expert counts and lists); floating outputs within
 tolerance.  The full 128-expert pass is checked on every routing output and on
-the residual/norm outputs of a sample of positions."""
+the residual/norm outputs of every position."""
 import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_F32, TOL_Q8, q8_dev, to_dev
+from helpers import TOL_F32, TOL_Q8, exact_q8, int_acts, plant_q8_edges, q8_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -125,6 +125,64 @@ def test_moe_router_ties(pg, oracle):
             assert 2 in pos and pos[2] < pos[7]
 
 
+def _moe_entries(pg, c, o, ws):
+    """U [n k][I] and D [n k][H]: the per-entry expert outputs moe_grouped leaves at the
+    start of its workspace."""
+    n, H = c["X"].shape
+    I = c["up"].q.shape[-2]
+    nk = n * c["top_k"]
+    U = ws[:nk * I * 4].view(torch.float32).view(nk, I).cpu().numpy()
+    d0 = -(-(nk * I * 4) // 256) * 256
+    D = ws[d0:d0 + nk * H * 4].view(torch.float32).view(nk, H).cpu().numpy()
+    return U, D
+
+
+@pytest.mark.parametrize("exact", [False, True])
+def test_moe_bank_edges(pg, oracle, exact):
+    """Both expert banks with the format's edges planted (q = -128 rows, blocks and entries;
+    scale-0 blocks holding their bias alone).  Routing exact; each entry's up row U against
+    the oracle on X (bit for bit in the exact case: scale 2^-3, biases multiples of 1/8,
+    activations in {-1, 0, 1}), its down row D against the oracle on the device's U, and the
+    pass's outputs at the q8 tolerance."""
+    _case(f"moe bank edges exact={exact}")
+    shape = synth.MoEShape(n=24, hidden=128, inter=96, experts=6, top_k=2)
+    c = synth.moe(5 + exact, shape)
+    rng = np.random.default_rng(93 + exact)
+    E, I, H = shape.experts, shape.inter, shape.hidden
+    if exact:
+        c["up"] = exact_q8(rng, I, H, lead=(E,))
+        c["down"] = exact_q8(rng, H, I, lead=(E,))
+        c["X"] = int_acts(rng, (shape.n, H), lim=1)
+    plant_q8_edges(c["up"], rng, exact=exact)
+    plant_q8_edges(c["down"], rng, exact=exact)
+    ws = torch.empty(pg.moe_grouped_workspace_bytes(shape.n, H, I, E, shape.top_k), dtype=torch.uint8,
+                     device="cuda")
+    up, down = q8_dev(c["up"], torch), q8_dev(c["down"], torch)
+    h = to_dev(c["h"], torch)
+    o = pg.moe_grouped(to_dev(c["X"], torch), to_dev(c["Wr"], torch), up, down, h, to_dev(c["w"], torch),
+                       c["eps"], c["top_k"], workspace=ws)
+    torch.cuda.synchronize()
+    o = {k: v.cpu().numpy() for k, v in o.items()}
+    o["h"] = h.cpu().numpy()
+    sel, rw = _check_routing(oracle, c, o)
+    U, D = _moe_entries(pg, c, o, ws)
+    t_up = (c["up"].q, c["up"].scale, c["up"].bias)
+    t_dn = (c["down"].q, c["down"].scale, c["down"].bias)
+    U_ref, _ = oracle.moe_experts(c["X"], sel, t_up, t_dn)
+    if exact:
+        assert np.max(U_ref) < 2.0 ** 18      # relu^2 of a multiple of 1/8 below 512: exact in f32
+        assert np.array_equal(U.astype(np.float64), U_ref)
+    else:
+        assert oracle.rel_err(U, U_ref) <= TOL_Q8
+    k = c["top_k"]
+    D_ref = np.stack([oracle.gemm_q8(*(a[sel.reshape(-1)[j]] for a in t_dn), U[j]) for j in range(U.shape[0])])
+    assert oracle.rel_err(D, D_ref) <= TOL_Q8
+    h_ref, out_ref = oracle.moe_combine(c["h"], D_ref, rw, c["w"], c["eps"])
+    assert oracle.rel_err(o["h"], h_ref) <= TOL_Q8
+    assert oracle.rel_err(o["out"], out_ref) <= TOL_Q8
+    assert k == sel.shape[1]
+
+
 def test_moe_full_128_experts(pg, oracle):
     """The full pass: 64 positions, hidden 2688, 128 experts of 2688 -> 1856 -> 2688, top-6."""
     _case("moe full")
@@ -133,11 +191,9 @@ def test_moe_full_128_experts(pg, oracle):
     sel, rw = _check_routing(oracle, c, o)
     distinct = int((o["counts"] > 0).sum())
     print(f"[info] distinct experts selected: {distinct}", flush=True)
-    rng = np.random.default_rng(4)
-    pos = np.sort(rng.choice(64, 6, replace=False))
     up = (c["up"].q, c["up"].scale, c["up"].bias)
     down = (c["down"].q, c["down"].scale, c["down"].bias)
-    _, D = oracle.moe_experts(c["X"][pos], sel[pos], up, down, grouped=False)
-    h_ref, out_ref = oracle.moe_combine(c["h"][pos], D, rw[pos], c["w"], c["eps"])
-    assert oracle.rel_err(o["h"][pos], h_ref) <= TOL_Q8
-    assert oracle.rel_err(o["out"][pos], out_ref) <= TOL_Q8
+    _, D = oracle.moe_experts(c["X"], sel, up, down, grouped=False)
+    h_ref, out_ref = oracle.moe_combine(c["h"], D, rw, c["w"], c["eps"])
+    assert oracle.rel_err(o["h"], h_ref) <= TOL_Q8
+    assert oracle.rel_err(o["out"], out_ref) <= TOL_Q8

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_F32, TOL_Q8, exact_q8, int_acts, q8_dev, to_dev
+from helpers import TOL_F32, TOL_Q8, exact_q8, int_acts, plant_q8_edges, q8_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +77,31 @@ def test_prefill_exact_bias_bitwise(pg, oracle):
     torch.cuda.synchronize()
     ref = oracle.gemm_q8(m.q, m.scale, m.bias, X)
     assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("rows,cols,n", [(200, 1024, 24), (640, 4096, 64), (300, 14336, 7)])
+def test_prefill_exact_edges_bitwise(pg, oracle, rows, cols, n):
+    """The exact case with the format's edges planted (q = -128 rows, blocks and entries;
+    scale-0 blocks holding their bias alone), K splits included: bit for bit."""
+    _case(f"prefill exact edges {rows}x{cols} n={n}")
+    rng = np.random.default_rng(rows + cols + n)
+    m = plant_q8_edges(exact_q8(rng, rows, cols), rng, exact=True)
+    X = int_acts(rng, (n, cols), lim=4)
+    Y = pg.prefill_gemm_q8(q8_dev(m, torch), to_dev(X, torch))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_q8(m.q, m.scale, m.bias, X)
+    assert np.array_equal(Y.cpu().numpy().astype(np.float64), ref)
+
+
+def test_prefill_edges_tolerance(pg, oracle):
+    """Random scales and biases with the edges planted: within the q8 tolerance."""
+    _case("prefill edges")
+    rng = np.random.default_rng(92)
+    m = plant_q8_edges(synth.q8(rng, 500, 4096), rng)
+    X = synth.normal(rng, (64, 4096))
+    Y = pg.prefill_gemm_q8(q8_dev(m, torch), to_dev(X, torch), act=1)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(Y.cpu().numpy(), oracle.gemm_q8(m.q, m.scale, m.bias, X, act=1)) <= TOL_Q8
 
 
 def test_prefill_rows_match_gemv(pg):

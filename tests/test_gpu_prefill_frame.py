@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from helpers import TOL_Q8, oracle_frame, q8_dev, to_dev
+from helpers import TOL_Q8, assert_staged, oracle_frame_staged, q8_dev, staged_errors, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -56,22 +56,22 @@ def _run(pg, W, f, x0, h0, ws=None):
 
 @pytest.mark.parametrize("name,n", [("h1024", 1), ("h1024", 5), ("h1024", 64), ("h2048", 33), ("full", 64)])
 def test_prefill_frame_parity(pg, oracle, name, n):
+    """Stage-isolated: every output of the one call is compared with the
+    definition applied to the device's own input to that stage (its qkv, u, d
+    and final residual), so the dense epilogues that only this call uses (the
+    residual add with the next product's staging, and the 1/rms scaling) are
+    each held to the q8 tolerance."""
     shape = SHAPES[name]
     _case(f"prefill_frame_q8 {name} n={n}")
     f = synth.frame_weights(21, shape)
     inp = synth.frame_inputs(21, n, shape.hidden)
-    ref = oracle_frame(oracle, f, inp["x0"], inp["h0"])
     out, h, _ = _run(pg, _weights(f), f, inp["x0"], inp["h0"])
-    errs = {"qkv": oracle.rel_err(out["qkv"].cpu().numpy(), ref["qkv"]),
-            "h2": oracle.rel_err(h.cpu().numpy(), ref["h2"]),
-            "u": oracle.rel_err(out["u"].cpu().numpy(), ref["u"]),
-            "d": oracle.rel_err(out["d"].cpu().numpy(), ref["d"]),
-            "logits": oracle.rel_err(out["logits"].cpu().numpy(), ref["logits"])}
+    dev = {k: v.cpu().numpy() for k, v in out.items()}
+    dev["h2"] = h.cpu().numpy()
+    ref = oracle_frame_staged(oracle, f, inp["x0"], inp["h0"], dev)
+    errs = staged_errors(oracle, ref, dev)
     print(f"[info] {name} n={n} rel errs " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    assert errs["qkv"] <= TOL_Q8
-    assert errs["h2"] <= TOL_Q8
-    for k in ("u", "d", "logits"):
-        assert errs[k] <= 4 * TOL_Q8, k
+    assert_staged(errs)
 
 
 def test_prefill_frame_repeat_and_vs_calls(pg):

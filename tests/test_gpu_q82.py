@@ -23,6 +23,14 @@ def pg():
     return pg
 
 
+def _plant_m128(rng, q):
+    """q = -128 (outside the generator's range; the int8 body decodes it as -128) on the
+    first row and on 2% of the entries."""
+    q[0, :] = -128
+    q[rng.random(q.shape) < 0.02] = -128
+    return q
+
+
 def _case(msg):
     print(f"[case] {msg}", flush=True)
 
@@ -53,7 +61,7 @@ def test_gemv_q82_exact_integer_case(pg, oracle):
     _case("gemv_q82 exact")
     rng = np.random.default_rng(5)
     rows, cols = 300, 2048
-    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    q = _plant_m128(rng, rng.integers(-127, 128, size=(rows, cols), dtype=np.int8))
     rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
     cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
     x = rng.integers(-8, 9, size=cols).astype(np.float32)
@@ -123,7 +131,7 @@ def test_prefill_q82_exact_bitwise(pg, oracle, rows, cols, n):
     """Power-of-two scales, integer activations: every step is exact, the K splits included."""
     _case(f"prefill_gemm_q82 exact n={n} {rows}x{cols}")
     rng = np.random.default_rng(11 + n)
-    q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+    q = _plant_m128(rng, rng.integers(-127, 128, size=(rows, cols), dtype=np.int8))
     rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
     cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
     X = rng.integers(-8, 9, size=(n, cols)).astype(np.float32)
@@ -218,7 +226,7 @@ def test_expert_bank_q82_exact_bitwise(pg, oracle):
     E, rows, cols, n, k = 5, 200, 512, 24, 2
     ms = []
     for _ in range(E):
-        q = rng.integers(-127, 128, size=(rows, cols), dtype=np.int8)
+        q = _plant_m128(rng, rng.integers(-127, 128, size=(rows, cols), dtype=np.int8))
         rs = (2.0 ** -rng.integers(2, 6, rows)).astype(np.float16)
         cf = (2.0 ** rng.integers(-1, 2, cols)).astype(np.float16)
         ms.append(synth.Q82(q, rs, cf))

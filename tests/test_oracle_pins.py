@@ -657,7 +657,86 @@ def test_route_sigmoid_zero_bias_is_topk_of_logits(oracle):
     np.testing.assert_array_equal(sel, want)
     s = scipy.special.expit(np.take_along_axis(L.astype(np.float64), want, 1))
     np.testing.assert_allclose(rw, s / (s.sum(1, keepdims=True) + 1e-20) * 1.5, rtol=1e-14)
-    np.testing.assert_allclose(choice, scipy.special.expit(L.astype(np.float64)), rtol=1e-15)
+    np.testing.assert_allclose(choice, scipy.special.expit(L.astype(np.float64)), rtol=4 * 2.0 ** -24)
+
+
+def test_exp_f32_within_one_ulp(oracle):
+    """The fixed binary32 exp is within one unit in the last place of the true value over the
+    whole clamped range (a wrong Taylor coefficient, a dropped reduction step or a sign slip
+    each break this by orders of magnitude)."""
+    rng = np.random.default_rng(64)
+    x = np.unique(np.concatenate([np.linspace(-80, 80, 320001), rng.uniform(-20, 20, 50000)]).astype(np.float32))
+    got = oracle.exp_f32(x).astype(np.float64)
+    ref = np.exp(x.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(got - ref) / ulp) <= 1.0
+    # clamped outside [-80, 80]: no subnormal, no infinity
+    edge = oracle.exp_f32(np.array([-1e4, -80, 80, 1e4], np.float32))
+    assert edge[0] == edge[1] and edge[2] == edge[3] and np.all(np.isfinite(edge)) and edge[0] >= 2.0 ** -126
+
+
+def test_sigmoid_f32_closed_forms(oracle):
+    """sigma(0) = 1/2 exactly (e^0 = 1 exactly: k = 0, r = 0, the polynomial's constant term);
+    sigma(l) + sigma(-l) = 1 to a few units in the last place; within 3 ulp of scipy's expit on
+    a sweep; saturates to 1 for large l and to a normal number near 0 for very negative l."""
+    assert oracle.sigmoid_f32([0.0])[0] == np.float32(0.5)
+    l = np.linspace(-30, 30, 200001).astype(np.float32)
+    s = oracle.sigmoid_f32(l).astype(np.float64)
+    ref = scipy.special.expit(l.astype(np.float64))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(s - ref) / ulp) <= 3.0
+    np.testing.assert_allclose(s + oracle.sigmoid_f32(-l).astype(np.float64), 1.0, atol=4 * 2.0 ** -24)
+    big = oracle.sigmoid_f32([100.0, 1e6, -100.0, -1e6])
+    assert big[0] == 1.0 and big[1] == 1.0 and 0 < big[2] < 2e-35 and big[2] == big[3]
+
+
+def _topk_f64(c, k):
+    return np.lexsort((np.arange(c.size), -c))[:k]
+
+
+def test_route_sigmoid_f32_choice_equals_f64_definition(oracle):
+    """The binary32 choice value (the fixed sigmoid plus one add) selects what the f64
+    definition sigma(l) + bias selects wherever the f64 values leave every gap among a
+    position's top k + 1 wider than the binary32 error (3 ulp of sigma plus the add's
+    rounding, both below 2^-22 for values below 2)."""
+    rng = np.random.default_rng(65)
+    n, E, k = 400, 128, 6
+    L = rng.standard_normal((n, E)).astype(np.float32)
+    bias = synth.router_bias(rng, E)
+    sel, _, _ = oracle.route_sigmoid(L, bias, k)
+    c64 = scipy.special.expit(L.astype(np.float64)) + bias.astype(np.float64)
+    bound = 2.0 ** -21
+    checked = 0
+    for b in range(n):
+        top = np.sort(c64[b])[::-1][:k + 1]
+        if np.min(top[:k] - top[1:]) > bound:
+            assert np.array_equal(sel[b], _topk_f64(c64[b], k)), b
+            checked += 1
+    assert checked >= 0.95 * n
+
+
+def test_route_f32_logits_select_as_f64_logits(oracle):
+    """Top-k on the fixed-order f32 logits equals top-k on the f64 logits wherever the f64
+    logits leave every gap among a position's top k + 1 wider than twice the f32 logits'
+    error bound (gamma of the chain length plus fold depth, times sum |x w|)."""
+    rng = np.random.default_rng(66)
+    n, H, E, k = 96, 2688, 128, 6
+    X = rng.standard_normal((n, H)).astype(np.float32)
+    Wr = synth.router_weight(rng, E, H)
+    f32 = oracle.router_logits_f32(X, Wr)
+    f64 = oracle.router_logits_f64(X, Wr)
+    sel, _, _ = oracle.route(f32, k)
+    depth = 4 * -(-(H // 4) // 64) + 6
+    u = 2.0 ** -24
+    bound = depth * u / (1 - depth * u) * (np.abs(X.astype(np.float64)) @ np.abs(Wr.astype(np.float64)).T)
+    checked = 0
+    for b in range(n):
+        order = _topk_f64(f64[b], k + 1)
+        top = f64[b][order]
+        if np.all(top[:k] - top[1:] > 2 * np.max(bound[b])):
+            assert np.array_equal(sel[b], order[:k]), b
+            checked += 1
+    assert checked >= 0.9 * n
 
 
 def test_route_sigmoid_bias_ties_and_unnormalised(oracle):
