@@ -216,6 +216,26 @@ int prefill_gemm_q8(const int8_t *q, const float *scale, const float *bias, int3
 size_t prefill_gemm_q8_workspace_bytes(int32_t rows, int32_t cols, int32_t n);
 
 /*
+ * prefill_gemm_q8_noalloc — prefill_gemm_q8 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same product, the same kernels and bits, with
+ * no workspace argument.  Its scratch is a fixed device array of
+ * PG_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library, one per device, held
+ * until the process ends; the call allocates and frees nothing.  Every call on
+ * one device shares that device's array, so calls that overlap in time on one
+ * device (two streams, two host threads) race: serialize them.
+ *   Arguments, layouts and codes as prefill_gemm_q8.
+ *   PG_EUNSUPPORTED also when prefill_gemm_q8_workspace_bytes(rows, cols, n)
+ *   exceeds PG_NOALLOC_SCRATCH_BYTES (nothing enqueued); every product of the
+ *   hidden-4096 layer frame (up to 32000 x 4096 and 4096 x 14336) fits at n = 64.
+ *   PG_ELAUNCH if the array's device address cannot be obtained.
+ */
+#define PG_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int prefill_gemm_q8_noalloc(const int8_t *q, const float *scale, const float *bias, int32_t rows,
+                            int32_t cols, const float *X, int32_t n, float *Y, int32_t act,
+                            pg_stream_t stream);
+
+/*
  * prefill_gemm_q82 — the batched prefill product on the q8_2f format
  * (gemma_batch.rs, `encode_q82_mm` and the `q8_2f_mm_r2` epilogue: the column
  * field scales the activation, the row scale the finished dot product):

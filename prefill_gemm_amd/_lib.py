@@ -58,6 +58,7 @@ def _declare(L):
     L.gemv_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.gemv_f16.argtypes = [_P, _i32, _i32, _P, _P, _i32, _P]
     L.prefill_gemm_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
+    L.prefill_gemm_q8_noalloc.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P]
     L.prefill_gemm_q8_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.prefill_gemm_q8_workspace_bytes.restype = _sz
     L.add_rmsnorm.argtypes = [_P, _P, _i32, _P, _f, _i32, _i32, _P, _P]
@@ -93,7 +94,7 @@ def _declare(L):
     L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
     L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "add_rmsnorm", "moe_grouped",
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
@@ -379,6 +380,21 @@ def gemv_f16(W: torch.Tensor, x: torch.Tensor, y: torch.Tensor | None = None, ac
 
 def prefill_gemm_q8_workspace_bytes(rows: int, cols: int, n: int) -> int:
     return lib().prefill_gemm_q8_workspace_bytes(rows, cols, n)
+
+
+def prefill_gemm_q8_noalloc(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor, act: int = 0, stream=None):
+    """prefill_gemm_q8 with the library's fixed per-device scratch array instead of a
+    workspace: Y [n][rows] (given, not allocated) = act(X [n][cols] . W^T).  Calls that
+    overlap in time on one device share that array and race."""
+    W.validate()
+    _dev(X, torch.float32, "X")
+    _dev(Y, torch.float32, "Y")
+    n = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != W.cols or tuple(Y.shape) != (n, W.rows):
+        raise ValueError("X must be [n][W.cols] and Y [n][W.rows]")
+    _check("prefill_gemm_q8_noalloc", lib().prefill_gemm_q8_noalloc(
+        _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(X), n, _ptr(Y), act, _stream(stream)))
+    return Y
 
 
 def prefill_gemm_q8(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor | None = None, act: int = 0,

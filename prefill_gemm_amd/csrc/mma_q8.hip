@@ -6,6 +6,7 @@
 // GEMM computes y[nb][rows] = x[nb][cols] . W^T and refuses (encodes nothing
 // for) shapes its tile does not cover.
 #include <algorithm>
+#include <mutex>
 
 #include "dense_q8.h"
 #include "pg_host.h"
@@ -296,6 +297,50 @@ extern "C" int prefill_gemm_q8(const int8_t *q, const float *scale, const float 
     const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
     return prefill_run(q, scale, bias, rows, cols, X, nullptr, n, Y, act, workspace, as_stream(stream));
+}
+
+// prefill_gemm_q8_noalloc: prefill_gemm_q8 with its workspace in a file-scope
+// device array instead of a caller's buffer, for callers that cannot allocate.
+// Each device holds its own copy of the array (allocated when the library's
+// code object is loaded on it, kept until the process ends).  Host code never
+// passes the array's name to a kernel: its device address is looked up once
+// per device with hipGetSymbolAddress, with that device current, and kept.
+// The staging launch clears the split tickets itself, so the array needs no
+// clearing between calls; calls that overlap on one device share the array
+// and race.
+static __device__ __align__(256) unsigned char scratch[PG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The current device's address of `scratch` (nullptr on failure).
+static void *scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+extern "C" int prefill_gemm_q8_noalloc(const int8_t *q, const float *scale, const float *bias,
+                                       int32_t rows, int32_t cols, const float *X, int32_t n, float *Y,
+                                       int32_t act, pg_stream_t stream) {
+    if (!q || !scale || !bias || !X || !Y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || n <= 0) return PG_EINVAL;
+    if (!aligned16(q) || !aligned16(X) || !aligned16(Y)) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || n > 64) return PG_EUNSUPPORTED;
+    if (prefill_gemm_q8_workspace_bytes(rows, cols, n) > PG_NOALLOC_SCRATCH_BYTES) return PG_EUNSUPPORTED;
+    void *ws = scratch_address();
+    if (!ws) return PG_ELAUNCH;
+    return prefill_run(q, scale, bias, rows, cols, X, nullptr, n, Y, act, ws, as_stream(stream));
 }
 
 extern "C" int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bias,

@@ -58,6 +58,10 @@ def test_argument_checks_return_before_launch(pg):
     assert L.gemv_q8(FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, 0, None) == pg.PG_EINVAL
     assert L.gemv_q8(FAKE, FAKE, FAKE, 8, 64, FAKE, FAKE, 2, None) == pg.PG_EINVAL
     assert L.gemv_q8(ODD, FAKE, FAKE, 8, 64, FAKE, FAKE, 0, None) == pg.PG_EINVAL
+    # the allocation-free prefill product: argument checks and its scratch limit
+    assert L.prefill_gemm_q8_noalloc(None, FAKE, FAKE, 8, 64, FAKE, 4, FAKE, 0, None) == pg.PG_EINVAL
+    assert L.prefill_gemm_q8_noalloc(FAKE, FAKE, FAKE, 8, 64, FAKE, 65, FAKE, 0, None) == pg.PG_EUNSUPPORTED
+    assert L.prefill_gemm_q8_noalloc(FAKE, FAKE, FAKE, 4096, 65536, FAKE, 64, FAKE, 0, None) == pg.PG_EUNSUPPORTED
     assert L.gemv_q8(FAKE, FAKE, FAKE, 8, 48, FAKE, FAKE, 0, None) == pg.PG_EUNSUPPORTED
     assert L.gemv_q8(FAKE, FAKE, FAKE, 8, 65536, FAKE, FAKE, 0, None) == pg.PG_EUNSUPPORTED
     assert L.gemv_f16(FAKE, 8, 12, FAKE, FAKE, 0, None) == pg.PG_EUNSUPPORTED
