@@ -10,7 +10,8 @@ Eight weight copies (8 x 342 MB, more than ten times the 256 MB Infinity
 Cache) rotate between steps so the weights stream from HBM.  `value` is the decode frame's
 weight-stream rate (weight bytes per frame / frame time, GB/s); the prefill
 rate (positions/s) is reported beside it.  After the timed steps (not part of
-ms_per_step) the other workloads are measured: the 1024x1024 GEMV + add +
+ms_per_step) the other workloads are measured: the HBM read ceiling
+(pg_stream_read over 2 GiB), the 1024x1024 GEMV + add +
 RMSNorm, the 4096x4096 f16 GEMV over 64 rotated copies, the 420-position
 prompt as 6 x 64 + 36, the decode frame as one persistent launch, the
 routed-MoE pass, the q8_2f GEMVs and prefill products and the q4tp GEMVs on
@@ -84,18 +85,36 @@ def file_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def recorded_traffic(kernel_src):
-    """HBM bytes per launch of the decode GEMV from the committed counter summary,
-    or None if missing or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", "gemv_q8_decode_frame_counters.md")
+def recorded_traffic(profile, key, sources):
+    """HBM bytes per launch recorded in a committed counter summary under profiles/
+    (the line "<key>: `<bytes>`"), or None if the summary is missing, has no such line,
+    or was taken on kernel sources other than the current ones (every
+    "`<sha256[:16]>` (`<file>`)" pair it lists must match)."""
+    path = os.path.join(ROOT, "profiles", profile)
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
-    t = re.search(r"HBM bytes per launch \(scaled\):\s*`?([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != file_hash(kernel_src):
+    hashes = dict((f, h) for h, f in re.findall(r"`([0-9a-f]{16})` \(`([^`]+)`\)", text))
+    if not hashes or set(hashes) != set(sources):
         return None
-    return float(t.group(1))
+    for f in sources:
+        if hashes[f] != file_hash(os.path.join(ROOT, "prefill_gemm_amd", "csrc", f)):
+            return None
+    t = re.search(re.escape(key) + r":\s*`?([0-9.eE+]+)", text)
+    return float(t.group(1)) if t else None
+
+
+def hbm_entry(kernel, nbytes, us, traffic=None, ceiling=None, **extra):
+    """A roofline entry for an HBM-bound kernel: algorithmic bytes per launch over the
+    average launch duration, against the published 8 TB/s (and the measured read ceiling)."""
+    gbs = nbytes / (us * 1e-6) / 1e9
+    e = {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "avg_launch_us": round(us, 3),
+         "algorithmic_bytes_per_launch": int(nbytes)}
+    if ceiling:
+        e["frac_of_read_ceiling"] = round(gbs / ceiling, 4)
+    e.update(extra)
+    return e
 
 
 def to_dev(torch, a):
@@ -341,7 +360,7 @@ def component_q82_bank(torch, pg, synth, reps=10, host_experts=16):
     active = int((counts > 0).sum())
     nbytes = active * (I * H + 2 * I + 2 * H)
     return {"workload": "q8_2f expert bank, MoE up shape: 128 experts 2688->1856, 64 positions top-6, relu^2",
-            "active_experts": active, "us": round(t * 1e3, 2), "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+            "active_experts": active, "us": round(t * 1e3, 2), "bytes": int(nbytes), "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
@@ -462,9 +481,46 @@ def component_decode_single_launch(torch, pg, synth, reps=40):
     torch.cuda.synchronize()
     us = t.total_ms() / reps * 1e3
     nbytes = sum(w.nbytes() for w in W0.values())
+    pg.decode_frame_q8_status(ws)   # raises (PG_ETIMEOUT) if a barrier wait gave up: the time would mean nothing
     return {"workload": "q8 decode frame (hidden 4096) as one persistent launch, graph replays over 8 weight copies",
             "us_per_frame": round(us, 2), "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1),
             "barrier_timeouts": pg.decode_frame_timeouts(ws)}
+
+
+def component_read_ceiling(torch, pg, reps=5):
+    """The achievable HBM read rate: pg_stream_read over 2 GiB (eight times the 256 MB
+    Infinity Cache), each workgroup reading one contiguous share, at several grid sizes;
+    the best grid's rate."""
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(8192, dtype=torch.float32, device="cuda")
+    rates = {}
+    for wg in (256, 512, 1024, 2048, 4096, 8192):
+        pg.stream_read(src, wg, sink)
+        torch.cuda.synchronize()
+        ms = time_graphs(torch, [one_graph(torch, [lambda wg=wg: pg.stream_read(src, wg, sink)] * reps)], 3) / reps
+        rates[wg] = nbytes / (ms * 1e-3) / 1e9
+    best = max(rates, key=rates.get)
+    del src
+    return {"workload": "pg_stream_read: 2 GiB read once with 16-byte non-temporal loads, one contiguous share "
+                        "per workgroup, 512 threads", "GB_s": round(rates[best], 1), "workgroups": best,
+            "frac_hbm_peak": round(rates[best] / HBM_PEAK_GBS, 4),
+            "GB_s_by_workgroups": {str(k): round(v, 1) for k, v in rates.items()}}
+
+
+def component_decode_eager(torch, frames, inp, reps=16):
+    """The decode frame's four GEMV calls issued eagerly (no graph), one frame at a time
+    between events, the weight copies in rotation: the time a caller sees without graphs."""
+    t = Timer(torch)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        dec = frames[1][r % len(frames[1])]
+        s = t.start()
+        for st in dec.stages(inp["x1"], inp["h1"]):
+            st()
+        t.stop(s)
+    torch.cuda.synchronize()
+    return round(t.total_ms() / reps * 1e3, 2)
 
 
 def component_moe(torch, pg, synth, reps=10):
@@ -491,7 +547,7 @@ def component_moe(torch, pg, synth, reps=10):
     per_expert = (I * H + H * I) * 1.25
     nbytes = distinct * per_expert + Wr.numel() * 4
     return {"workload": "routed MoE pass: 64 positions, hidden 2688, 128 experts 2688->1856->2688, top-6",
-            "distinct_experts": distinct, "ms": round(ms, 3),
+            "distinct_experts": distinct, "ms": round(ms, 3), "bytes_per_pass": int(nbytes),
             "positions_per_s": round(n / (ms * 1e-3), 1),
             "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -499,28 +555,49 @@ def component_moe(torch, pg, synth, reps=10):
 
 # ----------------------------------------------------------------- CPU baseline
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth):
     """The oracle (plain f64 C, OpenMP over outputs) on the decode frame's four
-    products at one position, repeated until about 10 s of CPU work."""
+    products at one position: repeated for about 10 s on every host thread it is
+    given, then for about 8 s on one thread."""
     import numpy as np
     import oracle
     f = synth.frame_weights(seed=0)
     rng = np.random.default_rng(0)
     xs = {k: synth.normal(rng, f[k].cols) for k in ("qkv", "up", "down", "head")}
     nbytes = sum(f[k].nbytes() for k in xs)
-    frames = 0
-    t0 = time.perf_counter()
-    while True:
-        for k, x in xs.items():
-            oracle.gemm_q8(f[k].q, f[k].scale, f[k].bias, x)
-        frames += 1
-        el = time.perf_counter() - t0
-        if el >= 10.0:
-            break
-    return {"value": round(frames * nbytes / el / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+
+    def run(seconds):
+        frames = 0
+        t0 = time.perf_counter()
+        while True:
+            for k, x in xs.items():
+                oracle.gemm_q8(f[k].q, f[k].scale, f[k].bias, x)
+            frames += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return frames, el
+    cores = oracle.threads()
+    frames, el = run(10.0)
+    oracle.set_threads(1)
+    frames1, el1 = run(8.0)
+    oracle.set_threads(cores)
+    return {"value": round(frames * nbytes / el / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{frames} decode frames (QKV, up, down, head q8 products at one position, "
-                      f"{nbytes / 1e6:.1f} MB of weights each) in {el:.1f} s"}
+                      f"{nbytes / 1e6:.1f} MB of weights each) in {el:.1f} s on {cores} threads; "
+                      f"{frames1} frames in {el1:.1f} s on 1 thread",
+            "single_thread_value": round(frames1 * nbytes / el1 / 1e9, 3),
+            "cpu_model": cpu_model()}
 
 
 # ----------------------------------------------------------------- main
@@ -578,16 +655,30 @@ def main():
     pre_ms = time_replays(torch, graphs, 1, args.steps)
     wall = time.perf_counter() - t0
     K = args.steps
-    gemv_avg_ms = dec_ms / 4           # the decode frame is four GEMV launches back to back
-    gemv_bytes_per_launch = frame_bytes / 4
-    achieved = gemv_bytes_per_launch / (gemv_avg_ms * 1e-3) / 1e9
-    value = frame_bytes / (dec_ms * 1e-3) / 1e9
     flops_pass = 2 * 64 * sum(w.rows * w.cols for w in frames[64][0].W.values())
-    traffic = recorded_traffic(os.path.join(ROOT, "prefill_gemm_amd", "csrc", "gemv.hip"))
+    # The prefill pass: the x0 staging launch (about 2 us) and four dense_kernel launches; the
+    # average dense launch is taken as the pass time over four (staging included).
+    dense_us = pre_ms * 1e3 / 4
+    dense_traffic = recorded_traffic("dense_prefill64_counters.md", "HBM bytes per dense launch (scaled)",
+                                     ["dense_q8.h", "mma_q8.hip"])
+    gemv_traffic = recorded_traffic("gemv_q8_decode_frame_counters.md", "HBM bytes per launch (scaled)",
+                                    ["gemv.hip"])
+    dense = hbm_entry("dense_kernel (prefill pass at 64 positions: one x0 staging launch and 4 matrix-core "
+                      "launches, QKV, up relu^2, down, head, the add + RMSNorm work in their epilogues)",
+                      frame_bytes / 4, dense_us, dense_traffic,
+                      mfma={"achieved": round(flops_pass / (pre_ms * 1e-3) / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(flops_pass / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                            "flops_per_pass": flops_pass,
+                            "note": "algorithmic flops (2 n rows cols); the bf16 hi + lo activation split runs "
+                                    "twice as many on the matrix cores"},
+                      arithmetic_intensity_flop_per_byte=round(flops_pass / frame_bytes, 1))
+    gemv = hbm_entry("gemv_q8_kernel (decode GEMV at 1 position; a frame is 4 launches back to back, "
+                     "QKV and down with the residual add, up and head with the 1/rms scaling)",
+                     frame_bytes / 4, dec_ms * 1e3 / 4, gemv_traffic)
 
     result = {
         "metric": "weight-stream HBM GB/s (q8 GEMV decode) + prefill positions/s at B=64",
-        "value": round(value, 1),
+        "value": round(frame_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
@@ -596,7 +687,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 weights (q8 block), f32 activations, f32 accumulate",
+        "dtype": "int8 weights (q8 block: int8 + f32 scale + f32 bias per 32); f32 activations. Decode: f32 FMA, "
+                 "f32 accumulate. Prefill: activations split into bf16 hi + lo on the bf16 matrix cores "
+                 "(exact int8 weights), f32 accumulate",
         "data": "synthetic (seeded numpy: q8 U[-127,127], scale U(1e-3,1e-2), bias N(0,1e-3); x,h N(0,1))",
         "config": {"workload": "q8 layer frame, hidden 4096 (QKV 6144, up 14336 relu^2, down, head 32000, "
                                "2x add+RMSNorm): decode at 1 position + prefill pass at 64 positions",
@@ -608,16 +701,14 @@ def main():
         "prefill_positions_per_s": round(64 / (pre_ms * 1e-3), 1),
         "prefill_frac_hbm_peak": round(frame_bytes / (pre_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "prefill_frac_mfma_bf16_peak": round(flops_pass / (pre_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"kernel": "gemv_q8_kernel (decode GEMV; a frame is 4 launches back to back, "
-                               "2 with add+RMSNorm fused in)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(gemv_avg_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": gemv_bytes_per_launch},
+        "roofline": dense,
+        "rooflines": {"dense_kernel": dense, "gemv_q8_kernel": gemv},
     }
+    result["decode_frame_eager_us"] = component_decode_eager(torch, frames, inp)
     if not args.no_components:
         log("components ...")
-        comp = {"gemv_add_norm_1024": component_gemv_norm(torch, pg, synth),
+        comp = {"hbm_read_ceiling": component_read_ceiling(torch, pg),
+                "gemv_add_norm_1024": component_gemv_norm(torch, pg, synth),
                 "f16_gemv_4096": component_f16(torch, pg, synth),
                 "prompt_420": component_prompt(torch, frames, inp)}
         del frames, graphs
@@ -631,6 +722,34 @@ def main():
         comp["prefill_attention"] = component_attn(torch, pg, synth)
         comp["q82_expert_bank"] = component_q82_bank(torch, pg, synth)
         result["components"] = comp
+        ceil = comp["hbm_read_ceiling"]["GB_s"]
+        for e in (dense, gemv):
+            e["frac_of_read_ceiling"] = round(e["achieved"] / ceil, 4)
+        R = result["rooflines"]
+        R["stream_read_kernel"] = hbm_entry("stream_read_kernel (the read ceiling itself)", 2 << 30,
+                                            (2 << 30) / (ceil * 1e9) * 1e6, None, ceil)
+        f16 = comp["f16_gemv_4096"]
+        R["gemv_f16_kernel"] = hbm_entry("gemv_f16_kernel (4096 x 4096 f16)", 4096 * 4096 * 2, f16["us_per_gemv"],
+                                         None, ceil)
+        moe = comp["moe_pass"]
+        R["expert_bank_kernel"] = hbm_entry(
+            "routed-MoE pass (router, route, group, the up and down expert_bank_kernel launches, combine); "
+            "bytes: each selected expert's up and down banks once plus the router", moe["bytes_per_pass"],
+            moe["ms"] * 1e3, None, ceil)
+        q82 = comp["q82_gemv_frame_shapes"]
+        R["gemv_q82_kernel"] = hbm_entry("gemv_q82_kernel (q8_2f GEMVs on the frame's four shapes, per launch)",
+                                         q82["weight_bytes"] / 4, q82["us_per_frame"] / 4, None, ceil)
+        q4 = comp["q4tp_gemv_frame_shapes"]
+        R["gemv_q4tp_kernel"] = hbm_entry("gemv_q4tp_kernel (q4tp GEMVs on the frame's four shapes, per launch)",
+                                          q4["weight_bytes"] / 4, q4["us_per_frame"] / 4, None, ceil)
+        bank = comp["q82_expert_bank"]
+        R["expert_bank_kernel_q82"] = hbm_entry("expert_bank_kernel<AL, true> (q8_2f bank, MoE up shape)",
+                                                bank["bytes"], bank["us"], None, ceil)
+        att = comp["prefill_attention"]
+        R["attn_prefill_kernel"] = {"kernel": "attn_prefill_kernel + merge (context 4096, f32 matrix cores)",
+                                    "bound": "mfma", "achieved": att["ctx4096_TFLOP_s"], "peak": 157.3,
+                                    "unit": "TFLOP/s", "frac": round(att["ctx4096_TFLOP_s"] / 157.3, 4),
+                                    "traffic": None, "avg_launch_us": att["ctx4096_us"]}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(synth)

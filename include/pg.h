@@ -12,8 +12,9 @@
  *
  * Conventions shared by every call
  *  - Pointers named as tensors are DEVICE pointers owned by the caller.  The
- *    library never allocates, frees or synchronizes; it enqueues kernels on
- *    `stream` (a hipStream_t; NULL is the null stream) and returns.
+ *    library never allocates or frees, and synchronizes only in
+ *    decode_frame_q8_status (a status query); every other call enqueues
+ *    kernels on `stream` (a hipStream_t; NULL is the null stream) and returns.
  *  - Return value: PG_OK, or a negative PG_E* code.  On any error other than
  *    PG_ELAUNCH nothing has been enqueued.  PG_ELAUNCH reports a failed kernel
  *    launch (hipGetLastError after the launch); faults during execution show
@@ -50,7 +51,8 @@ enum {
     PG_EINVAL = -1,        /* null pointer, non-positive size, misalignment, aliasing */
     PG_EUNSUPPORTED = -2,  /* shape outside what the kernels handle (listed per call) */
     PG_ELAUNCH = -3,       /* a kernel launch failed */
-    PG_EWORKSPACE = -4     /* workspace pointer NULL or smaller than the query returns */
+    PG_EWORKSPACE = -4,    /* workspace pointer NULL or smaller than the query returns */
+    PG_ETIMEOUT = -5       /* a device-wide barrier wait gave up (decode_frame_q8_status) */
 };
 
 /* A q8-block matrix on the device (the format above): q [rows][cols] int8,
@@ -307,8 +309,9 @@ int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bi
  *   once by decode_frame_q8_workspace_init before its first use (it holds
  *   the barrier counters, a launch counter, w * h and the norm sums).  The
  *   32-bit word at byte offset 8 counts barrier waits that gave up; non-zero
- *   means a launch's outputs are not to be trusted.  Launches that share a
- *   workspace must not overlap (same stream, or ordered streams).
+ *   means a launch's outputs are not to be trusted: decode_frame_q8_status
+ *   reports it.  Launches that share a workspace must not overlap (same
+ *   stream, or ordered streams).
  * PG_EUNSUPPORTED: a cols % 1024 != 0 or > 16384, a matrix of 2^31 or more
  *   bytes, or one with more than about 2047 rows per compute unit.
  *   PG_EINVAL: shapes that do not chain as above, null or misaligned
@@ -316,6 +319,12 @@ int prefill_gemm_q8_addnorm(const int8_t *q, const float *scale, const float *bi
  */
 size_t decode_frame_q8_workspace_bytes(int32_t hidden, int32_t inter);
 int decode_frame_q8_workspace_init(void *workspace, size_t workspace_bytes, pg_stream_t stream);
+/* decode_frame_q8_status — waits for `stream`, then returns PG_ETIMEOUT if any
+ * barrier wait of the launches on this workspace since its init gave up (their
+ * outputs are not trustworthy), else PG_OK.  The one call here that blocks the
+ * host.  PG_EWORKSPACE: workspace NULL, small or misaligned; PG_ELAUNCH: the
+ * copy or the wait failed. */
+int decode_frame_q8_status(const void *workspace, size_t workspace_bytes, pg_stream_t stream);
 int decode_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
                     const float *w1, const float *w2, float eps, const float *x0, float *h, float *qkv,
                     float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
@@ -501,6 +510,18 @@ int attn_prefill(const float *q, const float *kc, const float *vc, int32_t n, in
                  int32_t nkv, int32_t hd, float scale, float *o, void *workspace, size_t workspace_bytes,
                  pg_stream_t stream);
 size_t attn_prefill_workspace_bytes(int32_t n, int32_t pos0, int32_t nh, int32_t nkv, int32_t hd);
+
+/*
+ * pg_stream_read — a measurement call, not a product: reads `bytes` bytes at
+ * `src` once, with 16-byte non-temporal loads, workgroup g of `workgroups`
+ * reading the g-th contiguous share, and xors each workgroup's words into
+ * sink[g] (its value means nothing; it keeps the loads alive).  Its rate is the
+ * achievable HBM read ceiling the bandwidth-bound products are compared with
+ * (the published peak is 8 TB/s).
+ *   src 16-byte aligned, bytes a multiple of 16; sink [workgroups] 32-bit words.
+ *   PG_EINVAL: null pointers, bytes 0 or not a multiple of 16, workgroups < 1.
+ */
+int pg_stream_read(const void *src, size_t bytes, int32_t workgroups, float *sink, pg_stream_t stream);
 
 #ifdef __cplusplus
 }

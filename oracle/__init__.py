@@ -76,6 +76,7 @@ def _declare(L):
     L.oracle_sigmoid_f32.restype = ctypes.c_float
     L.oracle_sigmoid_f32_array.argtypes = [_P, _I, _P]
     L.oracle_threads.restype = _i
+    L.oracle_set_threads.argtypes = [_i]
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -88,6 +89,11 @@ def _p(a: np.ndarray):
 
 def threads() -> int:
     return lib().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's parallel loops (for timing it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def f16_to_f64(bits: int) -> float:

@@ -558,3 +558,13 @@ int oracle_threads(void) {
     return 1;
 #endif
 }
+
+/* Set the OpenMP thread count of the parallel loops above (timing only). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpg.so")
 
-PG_OK, PG_EINVAL, PG_EUNSUPPORTED, PG_ELAUNCH, PG_EWORKSPACE = 0, -1, -2, -3, -4
+PG_OK, PG_EINVAL, PG_EUNSUPPORTED, PG_ELAUNCH, PG_EWORKSPACE, PG_ETIMEOUT = 0, -1, -2, -3, -4, -5
 
 _lib = None
 
@@ -58,6 +58,8 @@ def _declare(L):
     L.gemv_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.gemv_f16.argtypes = [_P, _i32, _i32, _P, _P, _i32, _P]
     L.prefill_gemm_q8.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
+    L.decode_frame_q8_status.argtypes = [_P, _sz, _P]
+    L.pg_stream_read.argtypes = [_P, _sz, _i32, _P, _P]
     L.prefill_gemm_q8_noalloc.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P]
     L.prefill_gemm_q8_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.prefill_gemm_q8_workspace_bytes.restype = _sz
@@ -96,7 +98,7 @@ def _declare(L):
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
-                 "decode_frame_q8_workspace_init", "decode_frame_q8", "prefill_frame_q8"):
+                 "decode_frame_q8_workspace_init", "decode_frame_q8_status", "pg_stream_read", "decode_frame_q8", "prefill_frame_q8"):
         getattr(L, name).restype = ctypes.c_int
 
 
@@ -638,6 +640,19 @@ def decode_frame_q8_workspace(hidden: int, inter: int, device="cuda", stream=Non
 def decode_frame_timeouts(workspace: torch.Tensor) -> int:
     """Waits that gave up in launches on this workspace (the counter at byte 8)."""
     return int(workspace[8:12].view(torch.int32).item())
+
+
+def stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of ``src`` once (the HBM read-ceiling measurement; see pg_stream_read)."""
+    _check("pg_stream_read", lib().pg_stream_read(_ptr(src), src.numel() * src.element_size(), workgroups,
+                                                  _ptr(sink), _stream(stream)))
+
+
+def decode_frame_q8_status(workspace: torch.Tensor, stream=None) -> None:
+    """Wait for the stream; raise PGError (PG_ETIMEOUT) if a barrier wait of a launch on
+    this workspace gave up since its init (the outputs are then not trustworthy)."""
+    _check("decode_frame_q8_status", lib().decode_frame_q8_status(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def _q8struct(W: Q8Weight, name: str) -> PgQ8:

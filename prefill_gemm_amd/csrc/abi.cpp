@@ -8,6 +8,7 @@ extern "C" const char *pg_strerror(int code) {
         case PG_EUNSUPPORTED: return "shape not supported by the kernels (nothing enqueued)";
         case PG_ELAUNCH: return "kernel launch failed";
         case PG_EWORKSPACE: return "workspace missing or too small";
+        case PG_ETIMEOUT: return "a device-wide barrier wait gave up: the frame outputs since the workspace was set up are not trustworthy";
         default: return "unknown status";
     }
 }

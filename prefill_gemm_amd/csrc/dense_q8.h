@@ -50,11 +50,6 @@
 
 #include "pg_device.h"
 
-// Weight stream cache policy: non-temporal (used once; keeps the activations in L2).
-#ifndef PG_DENSE_WNT
-#define PG_DENSE_WNT true
-#endif
-
 namespace pg {
 
 // What the finished panel tile y[m][r] (positions m < n, the panel's rows)
@@ -486,7 +481,8 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         const uint32_t sq = (uint32_t)(c * KB) * 32u, ss = (uint32_t)(c * KB) * 4u;
         const i32x4 rqc = live_rsrc(rq, c < nst), rsc = live_rsrc(rs, c < nst);
 #pragma unroll
-        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, PG_DENSE_WNT>(rqc, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
+        // weights non-temporal: each is used once, which keeps the activations in L2
+        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, true>(rqc, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
 #pragma unroll
         for (int k = 0; k < C::kSPer; ++k)
             lds_copy<4>(rsc, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));

@@ -28,40 +28,22 @@
 #include "pg_device.h"
 #include "pg_host.h"
 
-#ifndef PG_EXP_D
-#define PG_EXP_D 8
-#endif
-#ifndef PG_EXP_LDS
-#define PG_EXP_LDS (148 * 1024)
-#endif
 
 namespace pg {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-#ifndef PG_EXP_SCHED
-#define PG_EXP_SCHED 0
-#endif
-#ifndef PG_EXP_THREADS
-#define PG_EXP_THREADS 512
-#endif
 // What the scheduler may move across a step boundary (never memory loads,
 // which keep their issue order).
-constexpr int kExpSched = PG_EXP_SCHED;
-constexpr int kExpThreads = PG_EXP_THREADS;
+constexpr int kExpSched = 0;
+constexpr int kExpThreads = 512;
 constexpr int kExpWaves = kExpThreads / kWave;
-#ifndef PG_EXP_T
-#define PG_EXP_T 1
-#endif
-constexpr int kExpDepth = PG_EXP_D;
-constexpr int kExpTiles = PG_EXP_T;                    // 16-row weight tiles per wave
+constexpr int kExpDepth = 8;
+constexpr int kExpTiles = 1;                    // 16-row weight tiles per wave
 constexpr int kExpRows = kExpWaves * 16 * kExpTiles;   // weight rows of one work item
-#ifndef PG_EXP_GROUP
-#define PG_EXP_GROUP 16
-#endif
-constexpr int kExpGroup = PG_EXP_GROUP;                // entries per pass over an item
-constexpr int kExpLds = PG_EXP_LDS;
+constexpr int kExpGroup = 16;                // entries per pass over an item
+constexpr int kExpLds = (148 * 1024);
 constexpr int kExpMaxCnt = 64;
 constexpr int kExpMaxExperts = 1024;
 
@@ -84,10 +66,7 @@ __device__ __forceinline__ int exp_chunk_pairs(int cnt, int mt, int d, int np) {
 static_assert(exp_chunk_bytes(kExpDepth, kExpGroup, kExpGroup / 16) <= kExpLds, "LDS budget");
 static_assert(kExpLds + kExpMaxExperts * 4 + 16 <= 160 * 1024, "LDS of a compute unit");
 
-#ifndef PG_EXP_NT
-#define PG_EXP_NT 0
-#endif
-constexpr int kExpNT = PG_EXP_NT;  // weight load cache policy (2: non-temporal)
+constexpr int kExpNT = 0;  // weight load cache policy (2: non-temporal)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t exp_rsrc(const void *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);

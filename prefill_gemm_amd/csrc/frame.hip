@@ -40,19 +40,10 @@
 
 namespace pg {
 
-#ifndef PG_FRAME_WAVES
-#define PG_FRAME_WAVES 8
-#endif
-#ifndef PG_FRAME_DEPTH
-#define PG_FRAME_DEPTH 8
-#endif
-constexpr int kFWaves = PG_FRAME_WAVES;
+constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;
-constexpr int kFD = PG_FRAME_DEPTH;  // ring depth, in steps
-#ifndef PG_FRAME_PRE
-#define PG_FRAME_PRE PG_FRAME_DEPTH
-#endif
-constexpr int kFPre = PG_FRAME_PRE;  // ring slots requested before a grid barrier
+constexpr int kFD = 8;  // ring depth, in steps
+constexpr int kFPre = 8;  // ring slots requested before a grid barrier
 constexpr int kFStep = 1024;       // columns per step
 constexpr int kFMaxCols = 16384;   // LDS holds one activation vector of this size
 constexpr int kFMaxShare = 2048;   // rows of one product per workgroup
@@ -587,6 +578,17 @@ extern "C" int decode_frame_q8_workspace_init(void *workspace, size_t workspace_
     return launch_status();
 }
 
+extern "C" int decode_frame_q8_status(const void *workspace, size_t workspace_bytes, pg_stream_t stream) {
+    if (!workspace || workspace_bytes < kSyncBytes || !aligned16(workspace)) return PG_EWORKSPACE;
+    unsigned gave_up = 0;
+    hipStream_t s = as_stream(stream);
+    if (hipMemcpyAsync(&gave_up, static_cast<const unsigned *>(workspace) + kSyncTimeouts, sizeof(gave_up),
+                       hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return PG_ELAUNCH;
+    return gave_up ? PG_ETIMEOUT : PG_OK;
+}
+
 extern "C" int decode_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
                                const float *w1, const float *w2, float eps, const float *x0, float *h, float *qkv,
                                float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
@@ -613,6 +615,13 @@ extern "C" int decode_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q
         if (ceil_div(W->rows, g) + 1 > kFMaxShare) return PG_EUNSUPPORTED;
     const size_t need = decode_frame_q8_workspace_bytes(H, up_w->rows);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
+    {   // workgroups write the outputs while others still read the inputs
+        const size_t hb = (size_t)H * sizeof(float);
+        const Span sp[] = {{x0, hb}, {h, hb}, {w1, hb}, {w2, hb}, {qkv, (size_t)qkv_w->rows * sizeof(float)},
+                           {u, (size_t)up_w->rows * sizeof(float)}, {d, hb},
+                           {logits, (size_t)head_w->rows * sizeof(float)}, {workspace, need}};
+        if (any_overlap(sp)) return PG_EINVAL;
+    }
 
     char *ws = static_cast<char *>(workspace);
     FrameArgs A{};

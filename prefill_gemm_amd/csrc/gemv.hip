@@ -330,16 +330,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_f16_kernel(
     }
 }
 
-#ifndef PG_GEMV_RW
-#define PG_GEMV_RW 2
-#endif
-#ifndef PG_GEMV_U
-#define PG_GEMV_U 1
-#endif
-#ifndef PG_GEMV_U_LONG
-#define PG_GEMV_U_LONG 2
-#endif
-constexpr int kQ8Rw = PG_GEMV_RW, kQ8U = PG_GEMV_U, kQ8ULong = PG_GEMV_U_LONG;
+constexpr int kQ8Rw = 2, kQ8U = 1, kQ8ULong = 2;
 constexpr int kQ8LongRow = 8192;  // columns above which a batch takes kQ8ULong steps
 // q8_2f weights (gemma_batch.rs, `q8_2f_mm_r2` doc comment and epilogue): the
 // column field folds into the staged activation, x'[c] = f16(cf[c]) * x[c],
@@ -454,16 +445,7 @@ constexpr int kF16Rw = 1, kF16U = 4;
 // Loads go through buffer resources; an item past the wave's last one gets an
 // empty resource (zeros, no memory traffic), so every load is issued
 // unconditionally and each compute waits for exactly its own data.
-#ifndef PG_Q4_RW
-#define PG_Q4_RW 2
-#endif
-#ifndef PG_Q4_U
-#define PG_Q4_U 1
-#endif
-#ifndef PG_Q4_OCC
-#define PG_Q4_OCC 2
-#endif
-constexpr int kQ4Rw = PG_Q4_RW, kQ4U = PG_Q4_U, kQ4Occ = PG_Q4_OCC;
+constexpr int kQ4Rw = 2, kQ4U = 1, kQ4Occ = 2;
 constexpr int kQ4Threads = 512;
 constexpr int kQ4Waves = kQ4Threads / kWave;
 
@@ -678,12 +660,6 @@ static int launch_mode(const int8_t *q, const float *scale, const float *bias, i
 }
 
 // [a, a + an) and [b, b + bn) bytes overlap.
-static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
-    if (!a || !b) return false;
-    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
-    return pa < pb + bn && pb < pa + an;
-}
-
 extern "C" int gemv_q8(const int8_t *q, const float *scale, const float *bias, int32_t rows,
                        int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream) {
     if (!q || !scale || !bias || !x || !y) return PG_EINVAL;
@@ -691,6 +667,7 @@ extern "C" int gemv_q8(const int8_t *q, const float *scale, const float *bias, i
     if (!aligned16(q) || !aligned16(x) || !aligned16(y)) return PG_EINVAL;
     if (act != 0 && act != 1) return PG_EINVAL;
     if (cols % 32 || cols > 32768) return PG_EUNSUPPORTED;
+    if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
     return launch_mode<kPlain>(q, scale, bias, rows, cols, x, y, act, Fuse{}, stream);
 }
 
@@ -813,6 +790,7 @@ extern "C" int gemv_f16(const uint16_t *w, int32_t rows, int32_t cols, const flo
     if (!aligned16(w) || !aligned16(x) || !aligned16(y)) return PG_EINVAL;
     if (act != 0 && act != 1) return PG_EINVAL;
     if (cols % 8 || cols > 32768) return PG_EUNSUPPORTED;
+    if (overlaps(y, (size_t)rows * sizeof(float), x, (size_t)cols * sizeof(float))) return PG_EINVAL;
     const size_t lds = (size_t)ceil_div(cols / 8, 64) * 2 * 64 * sizeof(float4);
     static const int ok = allow_lds(reinterpret_cast<const void *>(gemv_f16_kernel<kF16Rw, kF16U>),
                                     (size_t)ceil_div(32768 / 8, 64) * 2 * 64 * sizeof(float4));

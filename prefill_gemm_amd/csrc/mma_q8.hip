@@ -125,16 +125,7 @@ __global__ __launch_bounds__(256) void stage_norm_frag_kernel(
 // Dense pass: workgroup id -> (panel of 128 rows, K split).  Splits of one
 // panel take consecutive ids.  The activation ring is dynamic LDS (more than
 // the 64 KB a static array may take).
-#ifndef PG_DENSE_NX
-#define PG_DENSE_NX 2
-#endif
-#ifndef PG_DENSE_NW
-#define PG_DENSE_NW 4
-#endif
-#ifndef PG_DENSE_NK
-#define PG_DENSE_NK 4
-#endif
-constexpr int kDNK = PG_DENSE_NK, kDNX = PG_DENSE_NX, kDNW = PG_DENSE_NW;
+constexpr int kDNK = 4, kDNX = 2, kDNW = 4;
 template <int MT>
 using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
 
@@ -216,12 +207,6 @@ struct StageNorm {
     float *H_out;
     float *X_out;
 };
-
-static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
-    if (!a || !b) return false;
-    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
-    return pa < pb + bn && pb < pa + an;
-}
 
 static int launch_stage_frag(const float *X, int n, int cols, void *xp, void *xs, unsigned *zero, int nzero,
                              hipStream_t s, const uint16_t *cf = nullptr) {
@@ -482,6 +467,13 @@ extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_
         if (!aligned16(p)) return PG_EINVAL;
     const FrameLayout L = frame_layout(Hd, qkv_w->rows, I, head_w->rows, n);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return PG_EWORKSPACE;
+    {   // workgroups write the outputs while others still read the inputs
+        const size_t hb = (size_t)n * Hd * sizeof(float), vb = (size_t)Hd * sizeof(float);
+        const Span sp[] = {{X0, hb}, {H, hb}, {w1, vb}, {w2, vb}, {qkv, (size_t)n * qkv_w->rows * sizeof(float)},
+                           {u, (size_t)n * I * sizeof(float)}, {d, hb},
+                           {logits, (size_t)n * head_w->rows * sizeof(float)}, {workspace, L.total}};
+        if (any_overlap(sp)) return PG_EINVAL;
+    }
     char *ws = static_cast<char *>(workspace);
     hipStream_t s = as_stream(stream);
     auto at = [&](size_t off) { return static_cast<void *>(ws + off); };

@@ -267,11 +267,6 @@ extern "C" size_t moe_grouped_workspace_bytes(int32_t n, int32_t H, int32_t I, i
     return moe_layout(n, H, I, top_k).total;
 }
 
-static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
-    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
-    return x < y + bn && y < x + an;
-}
-
 // The pass behind moe_grouped (router_bias NULL: softmax router) and
 // moe_grouped_sigmoid (router_bias given: sigmoid + bias router; shared: the
 // dense term the combine adds before the slots, NULL: none).

@@ -149,11 +149,6 @@ int launch_moe_combine(float *h, const float *shared, const float *D, const floa
 
 using namespace pg;
 
-static bool overlaps(const void *a, size_t an, const void *b, size_t bn) {
-    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
-    return x < y + bn && y < x + an;
-}
-
 extern "C" int add_rmsnorm(float *h, const float *delta, int32_t delta_stride, const float *w,
                            float eps, int32_t hidden, int32_t n, float *out, pg_stream_t stream) {
     if (!h || !w || !out) return PG_EINVAL;

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(pg):
 
 def test_strerror_and_version(pg):
     assert pg.version().startswith("0.")
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert pg.strerror(code)
     assert pg.strerror(7) == "unknown status"
 
@@ -58,6 +58,10 @@ def test_argument_checks_return_before_launch(pg):
     assert L.gemv_q8(FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, 0, None) == pg.PG_EINVAL
     assert L.gemv_q8(FAKE, FAKE, FAKE, 8, 64, FAKE, FAKE, 2, None) == pg.PG_EINVAL
     assert L.gemv_q8(ODD, FAKE, FAKE, 8, 64, FAKE, FAKE, 0, None) == pg.PG_EINVAL
+    # y overlapping x (workgroups write y while others still read x)
+    assert L.gemv_q8(FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 0, None) == pg.PG_EINVAL
+    assert L.gemv_f16(FAKE, 64, 64, FAKE, ctypes.c_void_p(0x100000 + 128), 0, None) == pg.PG_EINVAL
+    assert L.decode_frame_q8_status(None, 4096, None) == pg.PG_EWORKSPACE
     # the allocation-free prefill product: argument checks and its scratch limit
     assert L.prefill_gemm_q8_noalloc(None, FAKE, FAKE, 8, 64, FAKE, 4, FAKE, 0, None) == pg.PG_EINVAL
     assert L.prefill_gemm_q8_noalloc(FAKE, FAKE, FAKE, 8, 64, FAKE, 65, FAKE, 0, None) == pg.PG_EUNSUPPORTED

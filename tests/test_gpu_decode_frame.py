@@ -61,6 +61,7 @@ def test_decode_frame_parity(pg, oracle, name):
     f = synth.frame_weights(11, shape)
     inp = synth.frame_inputs(11, 1, shape.hidden)
     _, out, h, ws = _run(pg, f, inp)
+    pg.decode_frame_q8_status(ws)          # raises PGError (PG_ETIMEOUT) if a barrier wait gave up
     assert pg.decode_frame_timeouts(ws) == 0
     dev = {k: v.cpu().numpy() for k, v in out.items()}
     dev["h2"] = h.cpu().numpy()
@@ -90,6 +91,7 @@ def test_decode_frame_repeat_and_vs_gemv_frame(pg):
         for k in out:
             assert torch.equal(out[k], first[k]), k
         assert torch.equal(h, h_first)
+    pg.decode_frame_q8_status(ws)
     assert pg.decode_frame_timeouts(ws) == 0
     fr = pg.Frame(W["qkv"], W["up"], W["down"], W["head"], w1, w2, f["eps"], n=1)
     h4 = h0.clone().view(1, -1)
@@ -135,4 +137,16 @@ def test_decode_frame_errors(pg):
     assert call(mat(1536, H), mat(2048, H), mat(H, 1024), mat(100, H)) == pg.PG_EINVAL   # down.cols != up.rows
     assert call(mat(512, H), mat(2048, H), mat(H, 2048), mat(100, H)) == pg.PG_EINVAL    # qkv rows < hidden
     assert call(mat(1536, 1056), mat(2048, 1056), mat(1056, 2048), mat(100, 1056)) == pg.PG_EUNSUPPORTED
+    # outputs overlapping inputs or each other
+    big = torch.zeros(4 * 4096, device=dev)
+    keep.append(big)
+    p0 = ctypes.c_void_p(big.data_ptr())
+    p1 = ctypes.c_void_p(big.data_ptr() + 4 * 1024)
+    args = [ctypes.byref(m) for m in ok]
+    assert L.decode_frame_q8(*args, vec(H), vec(H), 1e-6, p0, vec(H), p0, vec(2048), vec(H), vec(100),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), s) == pg.PG_EINVAL      # qkv == x0
+    assert L.decode_frame_q8(*args, vec(H), vec(H), 1e-6, vec(H), vec(H), p0, p1, vec(H), vec(100),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), s) == pg.PG_EINVAL      # u inside qkv
+    assert L.decode_frame_q8_status(ctypes.c_void_p(ws.data_ptr()), ws.numel(), s) == pg.PG_OK
+    assert L.decode_frame_q8_status(None, ws.numel(), s) == pg.PG_EWORKSPACE
     assert pg.decode_frame_timeouts(ws) == 0

@@ -147,3 +147,8 @@ def test_prefill_frame_errors(pg):
     assert call(mat(1536, H), mat(2048, H), mat(H, 1024), mat(1000, H)) == pg.PG_EINVAL  # down.cols != up.rows
     assert call(mat(1536, H), mat(2048, H), mat(H, 2048), mat(1000, H + 32)) == pg.PG_EINVAL  # head.cols != H
     assert call(mat(1536, H), mat(2048, H), mat(H, 2048 + 16), mat(1000, H)) == pg.PG_EUNSUPPORTED
+    # an output overlapping an input: refused before any launch
+    X0 = vec(n * H)
+    assert L.prefill_frame_q8(ctypes.byref(ok[0]), ctypes.byref(ok[1]), ctypes.byref(ok[2]), ctypes.byref(ok[3]),
+                              vec(H), vec(H), 1e-6, X0, vec(n * H), n, X0, vec(n * 2048), vec(n * H),
+                              vec(n * 1000), ctypes.c_void_p(ws.data_ptr()), ws.numel(), s) == pg.PG_EINVAL
