@@ -570,13 +570,16 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         q16_to_bf16(q0, b00, b01);
         // tile 0 chain; previous tile 1 scale step; tile 1 weights converted
         f32x16 t0[MT];
+        // the position tiles' chains interleaved: no matrix-core instruction
+        // waits on the one just issued
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            t0[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b00, zero);
-            t0[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b01, t0[mt]);
-            t0[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b00, t0[mt]);
-            t0[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b01, t0[mt]);
-        }
+        for (int mt = 0; mt < MT; ++mt) t0[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b00, zero);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t0[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b01, t0[mt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t0[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b00, t0[mt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t0[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b01, t0[mt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -584,12 +587,13 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         q16_to_bf16(q1, b10, b11);
         // tile 1 chain; tile 0 scale step
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            t1[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b10, zero);
-            t1[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b11, t1[mt]);
-            t1[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b10, t1[mt]);
-            t1[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b11, t1[mt]);
-        }
+        for (int mt = 0; mt < MT; ++mt) t1[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b10, zero);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t1[mt] = mfma_bf16(as_bf16x8(a[mt][1]), b11, t1[mt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t1[mt] = mfma_bf16(as_bf16x8(a[mt][2]), b10, t1[mt]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t1[mt] = mfma_bf16(as_bf16x8(a[mt][3]), b11, t1[mt]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -655,9 +659,11 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // ------------------------------------------------------------ epilogue
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing refills
     __builtin_amdgcn_s_barrier();
-    float *red = reinterpret_cast<float *>(lds);
-    auto red_at = [&](int k, int rt, int mt, int v) __attribute__((always_inline)) {
-        return ((((k - 1) * 2 + rh) * 2 + rt) * MT + mt) * 16 * 64 + v * 64 + lane;
+    // The K waves' partials meet in LDS as 16-byte pieces: piece (v / 4) of
+    // tile (rt, mt) of wave kq sits at red4[((kq - 1, rh, rt, mt), v / 4, lane)].
+    u32x4 *red4 = lds;
+    auto red_at = [&](int k, int rt, int mt, int v4) __attribute__((always_inline)) {
+        return (((((k - 1) * 2 + rh) * 2 + rt) * MT + mt) * 4 + v4) * 64 + lane;
     };
     if (kq > 0) {
 #pragma unroll
@@ -665,36 +671,58 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) red[red_at(kq, rt, mt, v)] = acc[rt][mt][v];
+                for (int v4 = 0; v4 < 4; ++v4)
+                    red4[red_at(kq, rt, mt, v4)] =
+                        u32x4{__float_as_uint(acc[rt][mt][4 * v4]), __float_as_uint(acc[rt][mt][4 * v4 + 1]),
+                              __float_as_uint(acc[rt][mt][4 * v4 + 2]), __float_as_uint(acc[rt][mt][4 * v4 + 3])};
     }
     __syncthreads();
-    // Tile by tile on the kq == 0 waves: add the other K waves' partials (in
-    // order).  Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h
-    // + (v % 4), row 64 rh + 32 rt + ml of the panel.
-    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);  // [m][128]
-    const bool direct = P.splits == 1 && P.mode == kDensePlain;
+    // On the kq == 0 waves: add the other K waves' partials (in order).
+    // Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h + (v %
+    // 4), row 64 rh + 32 rt + ml of the panel.
     if (kq == 0) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int rl = 64 * rh + 32 * rt + ml, r = r_base + rl;
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x16 t = acc[rt][mt];
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int k = 1; k < NK; ++k)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) t[v] += red[red_at(k, rt, mt, v)];
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (direct) {
-                        if (r < P.rows && m < P.n)
-                            P.out[m * P.ldo + r] =
-                                apply_act(P.act, Q82 ? t[v] * (float)__builtin_bit_cast(_Float16, P.rs[r]) : t[v]);
-                    } else {
-                        tile[m * 128 + rl] = t[v];
+                    for (int v4 = 0; v4 < 4; ++v4) {
+                        const u32x4 r = red4[red_at(k, rt, mt, v4)];
+                        acc[rt][mt][4 * v4] += __uint_as_float(r.x);
+                        acc[rt][mt][4 * v4 + 1] += __uint_as_float(r.y);
+                        acc[rt][mt][4 * v4 + 2] += __uint_as_float(r.z);
+                        acc[rt][mt][4 * v4 + 3] += __uint_as_float(r.w);
                     }
-                }
+    }
+    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);  // [m][128]
+    const bool direct = P.splits == 1 && P.mode == kDensePlain;
+    if (kq == 0) {
+        if (direct) {
+            // Plain, unsplit: straight to the output (bounds by predication).
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int r = r_base + 64 * rh + 32 * rt + ml;
+                const float rsc = Q82 ? (float)__builtin_bit_cast(_Float16, P.rs[min(r, P.rows - 1)]) : 1.0f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+                        const float y = apply_act(P.act, Q82 ? acc[rt][mt][v] * rsc : acc[rt][mt][v]);
+                        if (r < P.rows && m < P.n) P.out[m * P.ldo + r] = y;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int rl = 64 * rh + 32 * rt + ml;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        tile[(32 * mt + 8 * (v >> 2) + 4 * h + (v & 3)) * 128 + rl] = acc[rt][mt][v];
             }
         }
     }
