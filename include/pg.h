@@ -368,6 +368,29 @@ int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w,
                      pg_stream_t stream);
 
 /*
+ * prefill_frame_q8_meta — prefill_frame_q8 with the pass size on the device,
+ * so that one recorded launch sequence (a HIP graph) serves every pass of a
+ * prompt (nemotron_prefill.rs, module doc: the bind groups are built once and
+ * the pass's n and pos0 sit in the `Meta` uniform buffer):
+ *     meta[0] = n (1..64), meta[1] = pos0 (>= 0), read by the kernels at launch;
+ * the pass works on rows pos0 .. pos0 + n - 1 of X0 and H and writes the same
+ * rows of qkv, u, d and logits, each buffer holding rows_total rows:
+ *   X0, H [rows_total][H]; qkv [rows_total][rows_qkv]; u [rows_total][I];
+ *   d [rows_total][H]; logits [rows_total][V]; meta: 2 int32 in device memory
+ *   (8-byte aligned, not overlapping the rest).  The caller may change meta
+ *   between launches (for instance between replays of a graph that holds
+ *   this call); a pass with n outside 1..64, pos0 < 0 or pos0 + n > rows_total
+ *   does nothing (no output is written).  Arithmetic, order and results are
+ *   those of prefill_frame_q8 on the same n positions, bit for bit.
+ *   workspace: prefill_frame_q8_workspace_bytes(H, rows_qkv, I, V, 64) bytes.
+ * Codes as prefill_frame_q8 (rows_total < 1: PG_EINVAL; meta NULL: PG_EINVAL).
+ */
+int prefill_frame_q8_meta(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                          const float *w1, const float *w2, float eps, const float *X0, float *H,
+                          int32_t rows_total, const int32_t *meta, float *qkv, float *u, float *d, float *logits,
+                          void *workspace, size_t workspace_bytes, pg_stream_t stream);
+
+/*
  * add_rmsnorm — fused residual add + RMSNorm, per position b < n
  * (nemotron_prefill.rs `pb_add_rms` with add = 1; gemma_batch.rs
  * `g4_add_norm_b` without the layer scalar):

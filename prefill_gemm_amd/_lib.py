@@ -78,6 +78,8 @@ def _declare(L):
     L.prefill_frame_q8_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
     L.prefill_frame_q8_workspace_bytes.restype = _sz
     L.prefill_frame_q8.argtypes = [ctypes.POINTER(PgQ8)] * 4 + [_P, _P, _f, _P, _P, _i32, _P, _P, _P, _P, _P, _sz, _P]
+    L.prefill_frame_q8_meta.argtypes = [ctypes.POINTER(PgQ8)] * 4 + [_P, _P, _f, _P, _P, _i32, _P, _P, _P, _P, _P, _P,
+                                                                     _sz, _P]
     L.decode_frame_q8_workspace_bytes.argtypes = [_i32, _i32]
     L.decode_frame_q8_workspace_bytes.restype = _sz
     L.decode_frame_q8_workspace_init.argtypes = [_P, _sz, _P]
@@ -98,7 +100,7 @@ def _declare(L):
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
     for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
-                 "decode_frame_q8_workspace_init", "decode_frame_q8_status", "pg_stream_read", "decode_frame_q8", "prefill_frame_q8"):
+                 "decode_frame_q8_workspace_init", "decode_frame_q8_status", "pg_stream_read", "decode_frame_q8", "prefill_frame_q8", "prefill_frame_q8_meta"):
         getattr(L, name).restype = ctypes.c_int
 
 
@@ -705,4 +707,31 @@ def prefill_frame_q8(qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight
     _check("prefill_frame_q8", lib().prefill_frame_q8(
         *[ctypes.byref(W) for W in Ws], _ptr(w1), _ptr(w2), eps, _ptr(X0), _ptr(H), n, _ptr(out["qkv"]),
         _ptr(out["u"]), _ptr(out["d"]), _ptr(out["logits"]), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def prefill_frame_q8_meta(qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight, w1: torch.Tensor,
+                          w2: torch.Tensor, eps: float, X0: torch.Tensor, H: torch.Tensor, meta: torch.Tensor,
+                          out: dict, workspace: torch.Tensor, stream=None) -> dict:
+    """prefill_frame_q8 with the pass size on the device: meta = int32 tensor [n, pos0] on the
+    GPU, read at launch; the pass works on rows pos0 .. pos0 + n - 1 of the prompt's buffers
+    X0, H [rows][hidden] and out = {qkv, u, d, logits} ([rows][...])."""
+    Ws = [_q8struct(W, nm) for W, nm in ((qkv, "qkv"), (up, "up"), (down, "down"), (head, "head"))]
+    for t, nm in ((w1, "w1"), (w2, "w2"), (X0, "X0"), (H, "H")):
+        _dev(t, torch.float32, nm)
+    _dev(meta, torch.int32, "meta")
+    if meta.numel() != 2:
+        raise ValueError("meta must hold [n, pos0]")
+    rows, hidden = X0.shape
+    if H.shape != X0.shape or hidden != qkv.cols or w1.numel() != hidden or w2.numel() != hidden:
+        raise ValueError("X0 and H must be [rows][qkv.cols]; w1, w2 [qkv.cols]")
+    for k, cols in (("qkv", qkv.rows), ("u", up.rows), ("d", hidden), ("logits", head.rows)):
+        _dev(out[k], torch.float32, k)
+        if tuple(out[k].shape) != (rows, cols):
+            raise ValueError(f"out[{k!r}] must be [{rows}][{cols}]")
+    _dev(workspace, torch.uint8, "workspace")
+    _check("prefill_frame_q8_meta", lib().prefill_frame_q8_meta(
+        *[ctypes.byref(W) for W in Ws], _ptr(w1), _ptr(w2), eps, _ptr(X0), _ptr(H), rows, _ptr(meta),
+        _ptr(out["qkv"]), _ptr(out["u"]), _ptr(out["d"]), _ptr(out["logits"]), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
     return out

@@ -98,7 +98,27 @@ struct DenseArgs {
     u32x4 *nxp;             // next product's staged fragments (NULL: none)
     __bf16 *nxs;            // next product's staged block sums
     int nnb;                // next product's blocks (its cols / 32)
+    // Pass size on the device (nemotron_prefill.rs keeps n and pos0 in its
+    // `Meta` uniform so that the pass is built once): meta = {n, pos0}, read at
+    // launch; out and H then address row pos0 of the prompt's buffers, which
+    // hold rows_total rows.  NULL: n above is the pass size.
+    const int *meta;
+    int rows_total;
+    int nl;                 // positions the layouts of parts / sumsq are sized for
 };
+
+// Resolve a device-side pass size into P (n, out, H); false if the pass is
+// empty or outside the buffers (then nothing is to be done).
+__device__ __forceinline__ bool dense_resolve_meta(DenseArgs &P) {
+    if (!P.meta) return true;
+    const int n = __builtin_amdgcn_readfirstlane(P.meta[0]);
+    const int pos0 = __builtin_amdgcn_readfirstlane(P.meta[1]);
+    if (n < 1 || n > P.nl || pos0 < 0 || pos0 > P.rows_total - n) return false;
+    P.n = n;
+    P.out += (long long)pos0 * P.ldo;
+    if (P.H) P.H += (long long)pos0 * P.hidden;
+    return true;
+}
 
 // Fragment layout of the staged activations: the 64 lanes of one matrix-core
 // fragment are contiguous (one 1 KB load a fragment).
@@ -251,9 +271,9 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
         const int panels = (P.rows + C::kRows - 1) / C::kRows;
         const int chunks = P.n * 32;
         const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            P.parts, (short)0, P.splits * P.n * panels * C::kRows * 4, 0x00020000);
+            P.parts, (short)0, P.splits * P.nl * panels * C::kRows * 4, 0x00020000);
         auto chunk_off = [&](int sp, int c) __attribute__((always_inline)) {
-            return (((sp * P.n + (c >> 5)) * panels + panel) * C::kRows + 4 * (c & 31)) * 4;
+            return (((sp * P.nl + (c >> 5)) * panels + panel) * C::kRows + 4 * (c & 31)) * 4;
         };
         constexpr int kC = 64 * 32 / C::kThreads;  // chunks per thread (n <= 64)
         constexpr int kDev = 16;                    // buffer cache policy: device scope
@@ -313,7 +333,7 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
         for (int p0 = 0; p0 < np; p0 += 16) {
             float v[16];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = p0 + k < np ? P.sumsq_in[(p0 + k) * P.n + m] : 0.0f;
+            for (int k = 0; k < 16; ++k) v[k] = p0 + k < np ? P.sumsq_in[(p0 + k) * P.nl + m] : 0.0f;
 #pragma unroll
             for (int k = 0; k < 16; ++k) ss += v[k];
         }
@@ -398,7 +418,7 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
     sq += __shfl_xor(sq, 1, kWave);
     sq += __shfl_xor(sq, 2, kWave);
     sq += __shfl_xor(sq, 4, kWave);
-    if ((t & 7) == 0 && r_base < P.hidden && m < P.n) P.sumsq[panel * P.n + m] = sq;
+    if ((t & 7) == 0 && r_base < P.hidden && m < P.n) P.sumsq[panel * P.nl + m] = sq;
 }
 
 template <int MT, int NK, int NX, int NW, bool Q82 = false>

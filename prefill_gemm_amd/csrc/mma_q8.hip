@@ -21,11 +21,21 @@ __device__ __forceinline__ void clear_words(unsigned *zero, int nzero) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nzero; i += gridDim.x * blockDim.x) zero[i] = 0u;
 }
 
+// meta (device {n, pos0}, or NULL): the pass size read at launch; X then
+// addresses row pos0 of a buffer of rows_total rows.  A pass outside it stages
+// nothing (the products that follow return at once too).
 __global__ __launch_bounds__(256) void stage_x_frag_kernel(const float *__restrict__ X, int n,
                                                            int cols, int mts, u32x4 *__restrict__ xp,
                                                            __bf16 *__restrict__ xs, unsigned *zero, int nzero,
-                                                           const uint16_t *__restrict__ cf) {
+                                                           const uint16_t *__restrict__ cf,
+                                                           const int *__restrict__ meta, int rows_total) {
     clear_words(zero, nzero);
+    if (meta) {
+        n = __builtin_amdgcn_readfirstlane(meta[0]);
+        const int pos0 = __builtin_amdgcn_readfirstlane(meta[1]);
+        if (n < 1 || n > mts * 32 || pos0 < 0 || pos0 > rows_total - n) return;
+        X += (long long)pos0 * cols;
+    }
     const int nb = cols >> 5;
     const int ng = (nb + 15) >> 4;
     const int per_row = ng * 32;
@@ -138,6 +148,7 @@ __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, 
     const int kb0 = split * bps;
     const int kb1 = min(nb, kb0 + bps);
     P.split = split;
+    if (!dense_resolve_meta(P)) return;
     dense_panel<MT, kDNK, kDNX, kDNW, Q82>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
 }
 
@@ -209,12 +220,14 @@ struct StageNorm {
 };
 
 static int launch_stage_frag(const float *X, int n, int cols, void *xp, void *xs, unsigned *zero, int nzero,
-                             hipStream_t s, const uint16_t *cf = nullptr) {
+                             hipStream_t s, const uint16_t *cf = nullptr, const int *meta = nullptr,
+                             int rows_total = 0) {
     const int mts = ceil_div(n, 32);
     const int nb = cols / 32, ng = (nb + 15) / 16;
     const long long threads = (long long)mts * 32 * ng * 32;
     hipLaunchKernelGGL(stage_x_frag_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, X, n, cols,
-                       mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), zero, nzero, cf);
+                       mts, reinterpret_cast<u32x4 *>(xp), reinterpret_cast<__bf16 *>(xs), zero, nzero, cf, meta,
+                       rows_total);
     return launch_status();
 }
 
@@ -227,6 +240,7 @@ static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, 
     P.xp = reinterpret_cast<const u32x4 *>(xp);
     P.xs = reinterpret_cast<const u32x4 *>(xs);
     P.mts = ceil_div(P.n, 32);
+    if (!P.meta) P.nl = P.n;
     const int nb = P.cols / 32;
     const int bps = dense_blocks_per_split(P.rows, P.cols);
     P.splits = ceil_div(nb, bps);  // splits that hold at least one block
@@ -445,13 +459,16 @@ extern "C" size_t prefill_frame_q8_workspace_bytes(int32_t hidden, int32_t qkv_r
     return frame_layout(hidden, qkv_rows, inter, vocab, n).total;
 }
 
-extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
-                                const float *w1, const float *w2, float eps, const float *X0, float *H, int32_t n,
-                                float *qkv, float *u, float *d, float *logits, void *workspace,
-                                size_t workspace_bytes, pg_stream_t stream) {
+// The frame behind prefill_frame_q8 (meta NULL: n positions at X0, H and the
+// outputs) and prefill_frame_q8_meta (meta: device {n, pos0}; n here is the
+// largest pass, 64, and the buffers hold rows_total rows).
+static int frame_run(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                     const float *w1, const float *w2, float eps, const float *X0, float *H, int n,
+                     const int32_t *meta, int rows_total, float *qkv, float *u, float *d, float *logits,
+                     void *workspace, size_t workspace_bytes, pg_stream_t stream) {
     if (!qkv_w || !up_w || !down_w || !head_w || !w1 || !w2 || !X0 || !H || !qkv || !u || !d || !logits)
         return PG_EINVAL;
-    if (!(eps >= 0.0f) || n <= 0) return PG_EINVAL;
+    if (!(eps >= 0.0f) || n <= 0 || rows_total <= 0) return PG_EINVAL;
     const pg_q8 *Ws[4] = {qkv_w, up_w, down_w, head_w};
     for (const pg_q8 *W : Ws) {
         if (!W->q || !W->scale || !W->bias || W->rows <= 0 || W->cols <= 0) return PG_EINVAL;
@@ -465,13 +482,15 @@ extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_
     const float *ptrs[] = {w1, w2, X0, H, qkv, u, d, logits};
     for (const float *p : ptrs)
         if (!aligned16(p)) return PG_EINVAL;
+    if (meta && ((uintptr_t)meta & 7)) return PG_EINVAL;
     const FrameLayout L = frame_layout(Hd, qkv_w->rows, I, head_w->rows, n);
     if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return PG_EWORKSPACE;
     {   // workgroups write the outputs while others still read the inputs
-        const size_t hb = (size_t)n * Hd * sizeof(float), vb = (size_t)Hd * sizeof(float);
-        const Span sp[] = {{X0, hb}, {H, hb}, {w1, vb}, {w2, vb}, {qkv, (size_t)n * qkv_w->rows * sizeof(float)},
-                           {u, (size_t)n * I * sizeof(float)}, {d, hb},
-                           {logits, (size_t)n * head_w->rows * sizeof(float)}, {workspace, L.total}};
+        const size_t R = (size_t)rows_total;
+        const size_t hb = R * Hd * sizeof(float), vb = (size_t)Hd * sizeof(float);
+        const Span sp[] = {{X0, hb}, {H, hb}, {w1, vb}, {w2, vb}, {qkv, R * qkv_w->rows * sizeof(float)},
+                           {u, R * I * sizeof(float)}, {d, hb}, {logits, R * head_w->rows * sizeof(float)},
+                           {workspace, L.total}, {meta, meta ? 8u : 0u}};
         if (any_overlap(sp)) return PG_EINVAL;
     }
     char *ws = static_cast<char *>(workspace);
@@ -479,7 +498,7 @@ extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_
     auto at = [&](size_t off) { return static_cast<void *>(ws + off); };
     auto tick = [&](int i) { return reinterpret_cast<unsigned *>(ws + L.tickets[i]); };
     const int nzero = (int)((L.xs[3] + round_up(frag_s_bytes(n, Hd), 256) - L.tickets[0]) / 4);
-    int rc = launch_stage_frag(X0, n, Hd, at(L.xp[0]), at(L.xs[0]), tick(0), nzero, s);
+    int rc = launch_stage_frag(X0, n, Hd, at(L.xp[0]), at(L.xs[0]), tick(0), nzero, s, nullptr, meta, rows_total);
     if (rc) return rc;
     float *parts = reinterpret_cast<float *>(ws + L.parts);
     float *ss1 = reinterpret_cast<float *>(ws + L.sumsq1), *ss2 = reinterpret_cast<float *>(ws + L.sumsq2);
@@ -495,6 +514,9 @@ extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_
         P.ldo = W->rows;
         P.hidden = Hd;
         P.eps = eps;
+        P.meta = meta;
+        P.rows_total = rows_total;
+        P.nl = n;
         return P;
     };
     auto next = [&](DenseArgs &P, int i, int cols) {
@@ -530,4 +552,23 @@ extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_
     P.mode = kDenseScaled;
     P.sumsq_in = ss2;
     return run_dense(P, at(L.xp[3]), at(L.xs[3]), parts, tick(3), s);
+}
+
+extern "C" int prefill_frame_q8(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w, const pg_q8 *head_w,
+                                const float *w1, const float *w2, float eps, const float *X0, float *H, int32_t n,
+                                float *qkv, float *u, float *d, float *logits, void *workspace,
+                                size_t workspace_bytes, pg_stream_t stream) {
+    if (n <= 0) return PG_EINVAL;
+    return frame_run(qkv_w, up_w, down_w, head_w, w1, w2, eps, X0, H, n, nullptr, n, qkv, u, d, logits, workspace,
+                     workspace_bytes, stream);
+}
+
+extern "C" int prefill_frame_q8_meta(const pg_q8 *qkv_w, const pg_q8 *up_w, const pg_q8 *down_w,
+                                     const pg_q8 *head_w, const float *w1, const float *w2, float eps,
+                                     const float *X0, float *H, int32_t rows_total, const int32_t *meta, float *qkv,
+                                     float *u, float *d, float *logits, void *workspace, size_t workspace_bytes,
+                                     pg_stream_t stream) {
+    if (!meta) return PG_EINVAL;
+    return frame_run(qkv_w, up_w, down_w, head_w, w1, w2, eps, X0, H, 64, meta, rows_total, qkv, u, d, logits,
+                     workspace, workspace_bytes, stream);
 }

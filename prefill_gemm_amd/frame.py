@@ -19,15 +19,18 @@ prefill_frame_q8 call (five launches: the staging of x0 and the four
 matrix-core passes, each finishing the add + norm work around it in its
 epilogue).  ``capture()`` records
 the whole frame once into a HIP graph (through torch.cuda.CUDAGraph) so
-replays pay one launch for the frame (nemotron_prefill.rs builds its bind
-groups once and keeps the pass size in a device buffer for the same reason).
+replays pay one launch for the frame.  ``Prompt`` goes further: its frame
+reads the pass size {n, pos0} from a device buffer, so one recording serves
+every pass of a prompt (nemotron_prefill.rs builds its bind groups once and
+keeps n and pos0 in its `Meta` uniform for the same reason).
 """
 from __future__ import annotations
 
 import torch
 
 from ._lib import (Q8Weight, gemv_q8, gemv_q8_normed, gemv_q8_residual, norm_parts, prefill_frame_q8,
-                   prefill_frame_q8_workspace_bytes, prefill_gemm_q8, prefill_gemm_q8_workspace_bytes)
+                   prefill_frame_q8_meta, prefill_frame_q8_workspace_bytes, prefill_gemm_q8,
+                   prefill_gemm_q8_workspace_bytes)
 
 PB_MAX = 64
 
@@ -107,3 +110,64 @@ class Frame:
 
     def replay(self):
         self.graph.replay()
+
+
+class Prompt:
+    """A prompt of ``rows`` positions through the layer frame in passes of at most 64,
+    from ONE recorded launch sequence: the frame is captured once as
+    prefill_frame_q8_meta, whose kernels read the pass's {n, pos0} from a device
+    buffer at launch, and each pass is a replay after that buffer is set
+    (nemotron_prefill.rs, module doc: bind groups built once, n and pos0 in the
+    `Meta` uniform).  X0 and H are the prompt's [rows][hidden] buffers; H is the
+    residual, updated in place; ``buf`` holds qkv, u, d and logits for every row."""
+
+    def __init__(self, qkv: Q8Weight, up: Q8Weight, down: Q8Weight, head: Q8Weight,
+                 w1: torch.Tensor, w2: torch.Tensor, eps: float, X0: torch.Tensor, H: torch.Tensor):
+        self.W = {"qkv": qkv, "up": up, "down": down, "head": head}
+        self.w1, self.w2, self.eps = w1, w2, eps
+        self.X0, self.H = X0, H
+        self.rows, hidden = X0.shape
+        dev = X0.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        R = self.rows
+        self.buf = {"qkv": torch.empty(R, qkv.rows, **f32), "u": torch.empty(R, up.rows, **f32),
+                    "d": torch.empty(R, hidden, **f32), "logits": torch.empty(R, head.rows, **f32)}
+        self.workspace = torch.empty(prefill_frame_q8_workspace_bytes(hidden, qkv.rows, up.rows, head.rows, PB_MAX),
+                                     dtype=torch.uint8, device=dev)
+        self.passes = [(min(PB_MAX, R - p0), p0) for p0 in range(0, R, PB_MAX)]
+        # one {n, pos0} row per pass, on the device; the launch reads `meta`
+        self.metas = torch.tensor(self.passes, dtype=torch.int32, device=dev)
+        self.meta = self.metas[0].clone()
+        self.graph = None
+
+    def _call(self):
+        prefill_frame_q8_meta(self.W["qkv"], self.W["up"], self.W["down"], self.W["head"], self.w1, self.w2,
+                              self.eps, self.X0, self.H, self.meta, self.buf, self.workspace)
+
+    def capture(self):
+        """Record the frame once; the recording is replayed for every pass."""
+        self.meta.zero_()            # n = 0: the warm-up call below changes nothing
+        self._call()                 # outside the graph: kernel attributes, allocator
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self._call()
+        torch.cuda.current_stream().wait_stream(s)
+        self.graph = g
+        return g
+
+    def run_pass(self, i: int):
+        """Pass i (rows pos0 .. pos0 + n - 1): set the device meta, then replay (or call)."""
+        self.meta.copy_(self.metas[i])
+        if self.graph is not None:
+            self.graph.replay()
+        else:
+            self._call()
+
+    def run(self):
+        """Every pass in order (H ends as the residual after the frame for every row)."""
+        for i in range(len(self.passes)):
+            self.run_pass(i)
+        return self.buf["logits"]
