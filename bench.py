@@ -296,8 +296,9 @@ def component_q82(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
 
 def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=2):
     """The pages' 4-bit format (q4tp) on the decode frame's four shapes for each of eight
-    weight copies, captured in one graph and replayed back to back; and the per-position
-    argmax over a 64 x 32000 head output (50 launches in one graph)."""
+    weight copies, captured in one graph and replayed back to back (the GEMVs, and separately
+    the prefill products at 64 positions); and the per-position argmax over a 64 x 32000 head
+    output (50 launches in one graph)."""
     import numpy as np
     shapes = [(6144, 4096), (14336, 4096), (4096, 14336), (32000, 4096)]
     rng = synth.streams(13, host_copies * len(shapes) + len(shapes) + 1)
@@ -316,6 +317,19 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
     best = time_graphs(torch, [one_graph(torch, [lambda c=c: chain(c) for c in range(copies)])], reps) / copies
     nbytes = sum(W.nbytes() for W in Ws[0])
 
+    # The same four products over a pass of 64 positions (prefill_gemm_q4tp).
+    n = 64
+    Xs = [to_dev(torch, synth.normal(rng[host_copies * len(shapes) + i], (n, k))) for i, (r, k) in enumerate(shapes)]
+    Ys = [torch.empty(n, r, device="cuda") for r, k in shapes]
+    wss = [torch.empty(pg.prefill_gemm_q8_workspace_bytes(r, k, n), dtype=torch.uint8, device="cuda")
+           for r, k in shapes]
+
+    def pchain(c):
+        for W, X, Y, ws in zip(Ws[c], Xs, Ys, wss):
+            pg.prefill_gemm_q4tp(W, X, Y, workspace=ws)
+    pbest = time_graphs(torch, [one_graph(torch, [lambda c=c: pchain(c) for c in range(copies)])], reps) / copies
+    flops = 2.0 * n * sum(r * k for r, k in shapes)
+
     L = to_dev(torch, synth.logits(rng[-1], 64, 32000))
     ids = torch.empty(64, dtype=torch.int32, device="cuda")
     am = time_graphs(torch, [one_graph(torch, [lambda: pg.argmax_rows(L, ids)] * 50)], 10) / 50
@@ -323,6 +337,9 @@ def component_q4tp_argmax(torch, pg, synth, reps=20, copies=COPIES, host_copies=
             "us_per_frame": round(best * 1e3, 2), "weight_bytes": nbytes,
             "GB_s": round(nbytes / (best * 1e-3) / 1e9, 1),
             "frac_hbm_peak": round(nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill64_us_per_frame": round(pbest * 1e3, 2),
+            "prefill64_weight_GB_s": round(nbytes / (pbest * 1e-3) / 1e9, 1),
+            "prefill64_TFLOP_s": round(flops / (pbest * 1e-3) / 1e12, 1),
             "argmax_64x32000_us": round(am * 1e3, 2),
             "argmax_GB_s": round(64 * 32000 * 4 / (am * 1e-3) / 1e9, 1)}
 

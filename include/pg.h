@@ -183,6 +183,27 @@ int gemv_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, 
               int32_t cols, const float *x, float *y, int32_t act, pg_stream_t stream);
 
 /*
+ * prefill_gemm_q4tp — the batched prefill product on the q4tp format
+ * (nemotron_prefill.rs, `pb_q4_bank` and its nibble and code readers, applied
+ * to one pass of n <= 64 positions with every weight read once):
+ *     Y[b][r] = act( sum_c 2^(base_r + code_{r,c/32} step_r) (nib_r(c) - 8) X[b][c] )
+ * with the layout of gemv_q4tp (nibbles, parameter words, 5-bit group codes).
+ * On the bf16 matrix cores: the nibble n enters as itself (exact), X as bf16
+ * hi + lo, each 32-column group's sum scaled by its group scale (hardware
+ * exp2 of fma(code, step, base) in f32, as gemv_q4tp), and the - 8 through a
+ * contraction of -8 * scale with the groups' sums of X.
+ *   nib [rows][cols/2] (16-byte aligned), params [rows] u32 and codes
+ *   [rows][ceil(5 cols/32 / 8)] (4-byte aligned), X [n][cols] f32, Y [n][rows]
+ *   f32 (16-byte aligned, not overlapping X or the workspace), act 0 or 1;
+ *   workspace: prefill_gemm_q8_workspace_bytes(rows, cols, n) bytes.
+ * PG_EUNSUPPORTED: cols % 32 != 0, n > 64.  PG_EINVAL: null or misaligned
+ *   pointers, rows, cols or n < 1, act not 0/1, overlaps.  PG_EWORKSPACE.
+ */
+int prefill_gemm_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t rows,
+                      int32_t cols, const float *X, int32_t n, float *Y, int32_t act, void *workspace,
+                      size_t workspace_bytes, pg_stream_t stream);
+
+/*
  * argmax_rows — the token chosen at each position (nemotron_prefill.rs,
  * `pb_argmax`, the verify passes):
  *     ids[b] = the smallest i with logits[b][i] the largest of row b,

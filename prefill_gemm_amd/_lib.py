@@ -88,6 +88,7 @@ def _declare(L):
     L.gemv_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
     L.prefill_gemm_q82.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
     L.gemv_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _P, _i32, _P]
+    L.prefill_gemm_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _P, _i32, _P, _i32, _P, _sz, _P]
     L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
     L.expert_bank_q82.argtypes = [_P, _P, _P, _i32, _i32, _i32, _P, ctypes.c_int64, _i32, _P, _P, _i32, _P,
                                   ctypes.c_int64, _i32, _P]
@@ -98,7 +99,7 @@ def _declare(L):
     L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
     L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "prefill_gemm_q4tp", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8_status", "pg_stream_read", "decode_frame_q8", "prefill_frame_q8", "prefill_frame_q8_meta"):
         getattr(L, name).restype = ctypes.c_int
@@ -417,6 +418,27 @@ def prefill_gemm_q8(W: Q8Weight, X: torch.Tensor, Y: torch.Tensor | None = None,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
     _check("prefill_gemm_q8", lib().prefill_gemm_q8(
         _ptr(W.q), _ptr(W.scale), _ptr(W.bias), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return Y
+
+
+def prefill_gemm_q4tp(W: Q4TPWeight, X: torch.Tensor, Y: torch.Tensor | None = None, act: int = 0,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """Y [n][rows] = act(X [n][cols] . W^T) for one pass of n <= 64 positions on a q4tp
+    matrix (w = 2^(base + code step) (nib - 8)); the workspace is sized as for prefill_gemm_q8."""
+    W.validate()
+    _dev(X, torch.float32, "X")
+    n = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != W.cols:
+        raise ValueError("X must be [n][W.cols]")
+    if Y is None:
+        Y = torch.empty(n, W.rows, dtype=torch.float32, device=X.device)
+    _dev(Y, torch.float32, "Y")
+    need = prefill_gemm_q8_workspace_bytes(W.rows, W.cols, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check("prefill_gemm_q4tp", lib().prefill_gemm_q4tp(
+        _ptr(W.nib), _ptr(W.params), _ptr(W.codes), W.rows, W.cols, _ptr(X), n, _ptr(Y), act,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return Y
 

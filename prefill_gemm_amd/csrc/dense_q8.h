@@ -66,11 +66,29 @@ namespace pg {
 // epilogue and the second one's scaling, with no pass of its own.
 enum DenseMode { kDensePlain = 0, kDenseResid = 1, kDenseScaled = 2 };
 
+// Weight formats of the engine (template argument FMT):
+//  kFmtQ8   int8 + f32 scale + f32 bias per 32 columns (w = scale q + bias);
+//  kFmtQ82  q8_2f: int8 body, f16 row scale on the finished sum (the f16
+//           column field is already folded into the staged activations);
+//  kFmtQ4   q4tp: 4-bit codes (w = 2^(base + code_g step) (nib - 8)), the
+//           nibble n entering the matrix cores as the exact bf16 n, and the
+//           - 8 through the bias contraction: per group the bias is
+//           -8 * scale, so scale (sum n x) - 8 scale sum x = scale sum (n - 8) x.
+enum DenseFmt { kFmtQ8 = 0, kFmtQ82 = 1, kFmtQ4 = 2 };
+
 struct DenseArgs {
     const int8_t *q;
     const float *scale;
     const float *bias;
     const uint16_t *rs;  // q8_2f variant: binary16 row scales (scale and bias unused)
+    // q4tp variant (q, scale, bias unused): nibbles [rows][cols / 2], parameter
+    // words [rows] (binary16 base low, step high), 5-bit group codes
+    // [rows][code_stride] (least significant bit first, bit 5 g for group g)
+    const uint8_t *nib;
+    const uint32_t *params;
+    const uint8_t *codes;
+    int code_stride;
+    uint32_t code_bytes;  // rows * code_stride
     int rows, cols;
     const u32x4 *xp;  // staged A fragments [nb][mts][4][64] (see stage_x_frag_kernel)
     const u32x4 *xs;  // staged block sums [ng][mts][2][64]
@@ -253,9 +271,10 @@ __device__ __forceinline__ int wq_slot(int row, int s) {
 // position m = t / 8 and the 16 rows 16 (t % 8) .. of the panel (threads 2i,
 // 2i + 1 hold the two halves of one 32-row block of the next product's
 // columns).
-template <int MT, int NK, int NX, int NW, bool Q82 = false>
+template <int MT, int NK, int NX, int NW, int FMT = kFmtQ8>
 __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_base, u32x4 *lds) {
     using C = DenseCfg<MT, NK, NX, NW>;
+    constexpr bool Q82 = FMT == kFmtQ82;
     static_assert(C::kThreads == 512, "one thread per (position, 16 rows) of a 64 x 128 tile");
     float *tile = reinterpret_cast<float *>(lds + C::kTileBase);
     float *s_inv = reinterpret_cast<float *>(lds + C::kTileBase + C::kTileU4);  // [64]
@@ -421,10 +440,11 @@ __device__ __forceinline__ void dense_finish(const DenseArgs &P, const int r_bas
     if ((t & 7) == 0 && r_base < P.hidden && m < P.n) P.sumsq[panel * P.nl + m] = sq;
 }
 
-template <int MT, int NK, int NX, int NW, bool Q82 = false>
+template <int MT, int NK, int NX, int NW, int FMT = kFmtQ8>
 __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base, const int kb0,
                                             const int kb1, u32x4 *lds) {
     using C = DenseCfg<MT, NK, NX, NW>;
+    constexpr bool Q82 = FMT == kFmtQ82, Q4 = FMT == kFmtQ4;
     constexpr int KB = C::kKB;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -438,11 +458,18 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // that are weighted by zero; reads past a buffer's end return zero.
     // Copies for stages past the range go through empty resources: they
     // return zeros at once and move no memory.
-    const i32x4 rq = buf_rsrc(P.q, (uint32_t)P.rows * (uint32_t)P.cols);
     // q8_2f: no block scales or biases; their copies go through empty
     // resources (zeros, no memory traffic), so every count of copies stays.
-    const i32x4 rs = buf_rsrc(P.scale, Q82 ? 0u : (uint32_t)P.rows * nb * 4u);
-    const i32x4 rb = buf_rsrc(P.bias, Q82 ? 0u : (uint32_t)P.rows * nb * 4u);
+    // q4tp: the nibbles take the weight copies (one per wave carries data,
+    // 16 rows x 64 bytes), a 16-byte window of each row's group codes takes the
+    // scale copies, and there are no bias copies at all (the compute writes
+    // the group biases itself), so the memory-counter waits drop kBPer a stage.
+    const i32x4 rq = Q4 ? buf_rsrc(P.nib, (uint32_t)P.rows * (uint32_t)(P.cols >> 1))
+                        : buf_rsrc(P.q, (uint32_t)P.rows * (uint32_t)P.cols);
+    const i32x4 rs = Q4 ? buf_rsrc(P.codes, (uint32_t)P.rows * (uint32_t)P.code_stride)
+                        : buf_rsrc(P.scale, Q82 ? 0u : (uint32_t)P.rows * nb * 4u);
+    const i32x4 rb = buf_rsrc(P.bias, (Q82 || Q4) ? 0u : (uint32_t)P.rows * nb * 4u);
+    constexpr int kWaitF = Q4 ? C::kWait - C::kBPer : C::kWait;
     const i32x4 rx = buf_rsrc(P.xp, (uint32_t)nb * P.mts * 4096u);
     const i32x4 rxs = buf_rsrc(P.xs, (uint32_t)ng * P.mts * 2048u);
     auto live_rsrc = [](i32x4 r, bool live) __attribute__((always_inline)) {
@@ -458,9 +485,18 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
     for (int k = 0; k < C::kQPer; ++k) {
         const int i = C::kQPer * w + k;
-        const int r8 = (lane >> 3) ^ (i & 1);
-        const int s = (lane & 7) ^ r8;
-        oq[k] = (uint32_t)(r_base + 8 * i + r8) * (uint32_t)P.cols + (uint32_t)(kb0 * 32 + (s >> 1) * 32 + (s & 1) * 16);
+        if (Q4) {
+            // rows 16 w + lane / 4, block (lane & 3) of the stage (16 bytes of nibbles)
+            // position p = lane & 3 of row r's four slots holds block p ^ ((r % 16) / 4),
+            // so that the 32 rows a matrix-core read touches spread over the LDS banks
+            oq[k] = (uint32_t)(r_base + 16 * w + (lane >> 2)) * (uint32_t)(P.cols >> 1) +
+                    (uint32_t)(kb0 + ((lane & 3) ^ ((lane >> 4) & 3))) * 16u;
+        } else {
+            const int r8 = (lane >> 3) ^ (i & 1);
+            const int s = (lane & 7) ^ r8;
+            oq[k] = (uint32_t)(r_base + 8 * i + r8) * (uint32_t)P.cols +
+                    (uint32_t)(kb0 * 32 + (s >> 1) * 32 + (s & 1) * 16);
+        }
     }
 #pragma unroll
     for (int k = 0; k < C::kSPer; ++k)
@@ -492,9 +528,17 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // [row][16]) into bias slot (group + 1) % 2.
     const uint32_t ob = ((uint32_t)(r_base + (lane >> 4)) * (uint32_t)nb + (uint32_t)(kb0 + 16 + (lane & 15))) * 4u;
     auto copy_b = [&](int it, int p) __attribute__((always_inline)) {
+        if (Q4) return;  // q4tp: the group biases are written by the compute
         // rows 4p .. 4p + 3 of group it
         lds_copy<4>(live_rsrc(rb, it * C::kStagesPerGroup < nst), ob + (uint32_t)(4 * p) * (uint32_t)nb * 4u + (uint32_t)(16 * (it - 1)) * 4u,
                     laddr(C::kBBase + (it & 1) * C::kBGroup + p * 16));
+    };
+    // q4tp: lane l of the wave's code copy: row 16 w + l / 4, dword l & 3 of the
+    // 16 bytes from the aligned dword holding the row's first code bit of the stage.
+    const uint32_t crow = (uint32_t)(r_base + 16 * w + (lane >> 2)) * (uint32_t)P.code_stride;
+    auto code_off = [&](int c) __attribute__((always_inline)) {
+        const uint32_t byte = (uint32_t)(5 * (kb0 + c * KB)) >> 3;
+        return ((crow + byte) & ~3u) + 4u * (uint32_t)(lane & 3);
     };
     auto copy_w = [&](int c) __attribute__((always_inline)) {
         const int wslot = C::kWBase + (c % NW) * C::kWStage;
@@ -502,10 +546,20 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         const i32x4 rqc = live_rsrc(rq, c < nst), rsc = live_rsrc(rs, c < nst);
 #pragma unroll
         // weights non-temporal: each is used once, which keeps the activations in L2
-        for (int k = 0; k < C::kQPer; ++k) lds_copy<16, true>(rqc, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
+        for (int k = 0; k < C::kQPer; ++k) {
+            if (Q4)  // one copy a wave carries the stage's nibbles; the rest are empty
+                lds_copy<16, true>(k == 0 ? rqc : live_rsrc(rqc, false), oq[k] + (uint32_t)(c * KB) * 16u,
+                                   laddr(wslot + (C::kQPer * w + k) * 64));
+            else
+                lds_copy<16, true>(rqc, oq[k] + sq, laddr(wslot + (C::kQPer * w + k) * 64));
+        }
 #pragma unroll
-        for (int k = 0; k < C::kSPer; ++k)
-            lds_copy<4>(rsc, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
+        for (int k = 0; k < C::kSPer; ++k) {
+            if (Q4)
+                lds_copy<4>(rsc, code_off(c), laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
+            else
+                lds_copy<4>(rsc, os[k] + ss, laddr(wslot + C::kWq + (C::kSPer * w + k) * 16));
+        }
     };
 
     // Prologue: W(0), X(0), X(1 .. NX - 2), W(1 .. NW - 2).
@@ -517,13 +571,23 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     for (int k = 0; k < 4 * C::kBPer; ++k) copy_b(0, (4 * w + k / C::kBPer) * C::kBPer + k % C::kBPer);
     // Stage 0 only: the copies issued after X(0) (the other prologue stages and
     // group 0's biases) may still be in flight; the stage-end waits cover them.
-    wait_vm<(NX - 2) * C::kXCopies + (NW - 2) * (C::kQPer + C::kSPer) + 4 * C::kBPer>();
+    wait_vm<(NX - 2) * C::kXCopies + (NW - 2) * (C::kQPer + C::kSPer) + (Q4 ? 0 : 4 * C::kBPer)>();
     __builtin_amdgcn_s_barrier();
 
     // ------------------------------------------------------------ compute
     const int rh = w & 1, kq = w >> 1;
     const int h = lane >> 5;
     const int ml = lane & 31;
+    // q4tp: base and step of this lane's two rows (binary16 halves of the parameter word)
+    float qb0 = 0.0f, qs0 = 0.0f, qb1 = 0.0f, qs1 = 0.0f;
+    if constexpr (Q4) {
+        const uint32_t p0 = P.params[min(r_base + 64 * rh + ml, P.rows - 1)];
+        const uint32_t p1 = P.params[min(r_base + 64 * rh + ml + 32, P.rows - 1)];
+        qb0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(p0 & 0xFFFFu));
+        qs0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(p0 >> 16));
+        qb1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(p1 & 0xFFFFu));
+        qs1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(p1 >> 16));
+    }
     f32x16 acc[2][MT];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -538,6 +602,36 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) t1[mt] = zero;
     float s1 = 0.0f;
+
+    // Bias term of group g on the calling K wave: sum over the group's blocks of
+    // bias[r][blk] * (block sum of x)[m][blk] (hi + lo on both sides); zero past kb1.
+    auto bias_mfma = [&](int g) __attribute__((always_inline)) {
+            // Bias term of the group on one K wave (in turn); zero past kb1.
+            const u32x4 *sf = lds + C::kSBase + (g & 1) * C::kSGroup + lane;
+            const float *bg = reinterpret_cast<const float *>(lds + C::kBBase + (g & 1) * C::kBGroup);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int row = 64 * rh + 32 * rt + ml;
+                const float4 b0 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h);
+                const float4 b1 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h + 4);
+                const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                bf16x8 bh, bl;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float v = kb0 + 16 * g + 8 * h + i < kb1 ? bv[i] : 0.0f;
+                    const __bf16 vh = to_bf16(v);
+                    bh[i] = vh;
+                    bl[i] = to_bf16(v - (float)vh);
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 sh = as_bf16x8(sf[mt * 64]), sl = as_bf16x8(sf[(MT + mt) * 64]);
+                    acc[rt][mt] = mfma_bf16(sh, bh, acc[rt][mt]);
+                    acc[rt][mt] = mfma_bf16(sl, bh, acc[rt][mt]);
+                    acc[rt][mt] = mfma_bf16(sh, bl, acc[rt][mt]);
+                }
+            }
+    };
 
     for (int c = 0; c < nst; ++c) {
         const int u = c % C::kStagesPerGroup;
@@ -561,8 +655,28 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
             for (int fi = 0; fi < 4; ++fi) a[mt][fi] = xst[((kbl * MT + mt) * 4 + fi) * 64];
         const int row0 = 64 * rh + ml, row1 = row0 + 32;
-        const u32x4 q0 = wst[wq_slot(row0, 2 * kbl + h)];
-        const u32x4 q1 = wst[wq_slot(row1, 2 * kbl + h)];
+        u32x4 q0, q1;
+        if constexpr (Q4) {
+            // 8 bytes (columns 16 h .. 16 h + 15 of block kbl) of each row's nibbles
+            const uint8_t *wb = reinterpret_cast<const uint8_t *>(wst);
+            auto nslot = [&](int r) __attribute__((always_inline)) {
+                return 128 * (r >> 4) + 4 * (r & 15) + (kbl ^ ((r >> 2) & 3));
+            };
+            const uint2 v0 = *reinterpret_cast<const uint2 *>(wb + 16 * nslot(row0) + 8 * h);
+            const uint2 v1 = *reinterpret_cast<const uint2 *>(wb + 16 * nslot(row1) + 8 * h);
+            q0 = u32x4{v0.x, v0.y, 0u, 0u};
+            q1 = u32x4{v1.x, v1.y, 0u, 0u};
+        } else {
+            q0 = wst[wq_slot(row0, 2 * kbl + h)];
+            q1 = wst[wq_slot(row1, 2 * kbl + h)];
+        }
+        auto to_b = [&](const u32x4 q, bf16x8 &k0, bf16x8 &k1) __attribute__((always_inline)) {
+            if constexpr (Q4) {
+                nib16_to_bf16(q.x, q.y, k0, k1);
+            } else {
+                q16_to_bf16(q, k0, k1);
+            }
+        };
         bf16x8 b00, b01, b10, b11;
         if constexpr (Q82) {
             // q8_2f: no block factors, so both tiles accumulate straight into
@@ -585,9 +699,41 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
                 acc[1][mt] = mfma_bf16(as_bf16x8(a[mt][3]), b11, acc[1][mt]);
             }
         } else {
-        const float sl0 = sst[4 * row0 + kbl], sl1 = sst[4 * row1 + kbl];
+        float sl0, sl1;
+        if constexpr (Q4) {
+            // group scale 2^(base + code step) from the row's 16-byte code window
+            const uint32_t bit0 = 5u * (uint32_t)(kb0 + c * KB);
+            auto q4_scale = [&](int r, float base, float step) __attribute__((always_inline)) {
+                // first code byte of the stage in the row, and the aligned dword the copy started at
+                const uint32_t at = (uint32_t)(r_base + r) * (uint32_t)P.code_stride + (bit0 >> 3);
+                const uint32_t a4 = at & ~3u;
+                uint64_t win;
+                if (a4 + 8u <= P.code_bytes) {
+                    const uint32_t *cw = reinterpret_cast<const uint32_t *>(wst + C::kWq) + 4 * r;
+                    win = (uint64_t)cw[0] | ((uint64_t)cw[1] << 32);
+                } else {
+                    // the buffer's last bytes: a copied dword that ran past the end
+                    // came back as zero, so read the bytes that exist directly
+                    win = 0;
+                    for (uint32_t k = 0; k < 8u; ++k)
+                        if (a4 + k < P.code_bytes) win |= (uint64_t)P.codes[a4 + k] << (8u * k);
+                }
+                const uint32_t sh = 8u * (at & 3u) + (bit0 & 7u) + 5u * (uint32_t)kbl;
+                const uint32_t code = (uint32_t)(win >> sh) & 31u;
+                return __builtin_amdgcn_exp2f(fmaf((float)code, step, base));
+            };
+            sl0 = q4_scale(row0, qb0, qs0);
+            sl1 = q4_scale(row1, qb1, qs1);
+            // this block's bias (-8 scale) into the group's bias slot: row0 from
+            // the lanes of half 0, row1 from half 1
+            float *bgw = reinterpret_cast<float *>(lds + C::kBBase + (it & 1) * C::kBGroup);
+            bgw[16 * (h ? row1 : row0) + 4 * u + kq] = live ? -8.0f * (h ? sl1 : sl0) : 0.0f;
+        } else {
+            sl0 = sst[4 * row0 + kbl];
+            sl1 = sst[4 * row1 + kbl];
+        }
         const float s0 = live ? sl0 : 0.0f;
-        q16_to_bf16(q0, b00, b01);
+        to_b(q0, b00, b01);
         // tile 0 chain; previous tile 1 scale step; tile 1 weights converted
         f32x16 t0[MT];
         // the position tiles' chains interleaved: no matrix-core instruction
@@ -604,7 +750,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[1][mt][v] = fmaf(s1, t1[mt][v], acc[1][mt][v]);
-        q16_to_bf16(q1, b10, b11);
+        to_b(q1, b10, b11);
         // tile 1 chain; tile 0 scale step
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) t1[mt] = mfma_bf16(as_bf16x8(a[mt][0]), b10, zero);
@@ -636,39 +782,19 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        if (!Q82 && u == C::kStagesPerGroup - 1 && kq == it % NK) {
-            // Bias term of the group on one K wave (in turn); zero past kb1.
-            const u32x4 *sf = lds + C::kSBase + (it & 1) * C::kSGroup + lane;
-            const float *bg = reinterpret_cast<const float *>(lds + C::kBBase + (it & 1) * C::kBGroup);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int row = 64 * rh + 32 * rt + ml;
-                const float4 b0 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h);
-                const float4 b1 = *reinterpret_cast<const float4 *>(bg + 16 * row + 8 * h + 4);
-                const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                bf16x8 bh, bl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float v = kb0 + 16 * it + 8 * h + i < kb1 ? bv[i] : 0.0f;
-                    const __bf16 vh = to_bf16(v);
-                    bh[i] = vh;
-                    bl[i] = to_bf16(v - (float)vh);
-                }
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 sh = as_bf16x8(sf[mt * 64]), sl = as_bf16x8(sf[(MT + mt) * 64]);
-                    acc[rt][mt] = mfma_bf16(sh, bh, acc[rt][mt]);
-                    acc[rt][mt] = mfma_bf16(sl, bh, acc[rt][mt]);
-                    acc[rt][mt] = mfma_bf16(sh, bl, acc[rt][mt]);
-                }
-            }
-        }
+        if (!Q82 && !Q4 && u == C::kStagesPerGroup - 1 && kq == it % NK) bias_mfma(it);
+        // q4tp: the group's biases are complete one barrier after its last stage
+        if (Q4 && u == 0 && it > 0 && kq == (it - 1) % NK) bias_mfma(it - 1);
 
         // Stage c + 1's copies must have landed before the barrier.
-        wait_vm<C::kWait>();
+        wait_vm<kWaitF>();
         __builtin_amdgcn_s_barrier();
     }
 
+    if (Q4 && nst > 0) {  // the last group's bias term (its biases are complete after the last barrier)
+        const int g = (nst - 1) / C::kStagesPerGroup;
+        if (kq == g % NK) bias_mfma(g);
+    }
     if (!Q82) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -747,7 +873,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
         }
     }
     if (direct) return;
-    dense_finish<MT, NK, NX, NW, Q82>(P, r_base, lds);
+    dense_finish<MT, NK, NX, NW, FMT>(P, r_base, lds);
 }
 
 }  // namespace pg

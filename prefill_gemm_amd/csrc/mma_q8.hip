@@ -139,7 +139,7 @@ constexpr int kDNK = 4, kDNX = 2, kDNW = 4;
 template <int MT>
 using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
 
-template <int MT, bool Q82>
+template <int MT, int FMT>
 __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int bps) {
     extern __shared__ u32x4 dlds[];
     const int id = blockIdx.x;
@@ -149,16 +149,16 @@ __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, 
     const int kb1 = min(nb, kb0 + bps);
     P.split = split;
     if (!dense_resolve_meta(P)) return;
-    dense_panel<MT, kDNK, kDNX, kDNW, Q82>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
+    dense_panel<MT, kDNK, kDNX, kDNW, FMT>(P, panel * DCfg<MT>::kRows, kb0, kb1, dlds);
 }
 
-template <int MT, bool Q82>
+template <int MT, int FMT>
 static int launch_dense(const DenseArgs &P, int grid, int bps, hipStream_t s) {
     constexpr size_t lds = (size_t)DCfg<MT>::kLdsU4 * sizeof(u32x4);
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT, Q82>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(dense_kernel<MT, FMT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL((dense_kernel<MT, Q82>), dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
+    hipLaunchKernelGGL((dense_kernel<MT, FMT>), dim3(grid), dim3(DCfg<MT>::kThreads), lds, s, P, bps);
     return launch_status();
 }
 
@@ -233,10 +233,10 @@ static int launch_stage_frag(const float *X, int n, int cols, void *xp, void *xs
 
 // The dense pass over one product whose activations are staged at (xp, xs);
 // the epilogue fields of P are the caller's.  Split partials and tickets at
-// (parts, tickets); the tickets must be zero.  q82: the weight is in the q8_2f
+// (parts, tickets); the tickets must be zero.  fmt: the weight format (kFmtQ82:
 // format (P.rs row scales; the column field is already in the staged activations).
 static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, unsigned *tickets, hipStream_t s,
-                     bool q82 = false) {
+                     int fmt = kFmtQ8) {
     P.xp = reinterpret_cast<const u32x4 *>(xp);
     P.xs = reinterpret_cast<const u32x4 *>(xs);
     P.mts = ceil_div(P.n, 32);
@@ -247,8 +247,11 @@ static int run_dense(DenseArgs P, const void *xp, const void *xs, float *parts, 
     P.parts = parts;
     P.tickets = tickets;
     const int grid = dense_panels(P.rows) * P.splits;
-    if (q82) return P.mts == 2 ? launch_dense<2, true>(P, grid, bps, s) : launch_dense<1, true>(P, grid, bps, s);
-    return P.mts == 2 ? launch_dense<2, false>(P, grid, bps, s) : launch_dense<1, false>(P, grid, bps, s);
+    if (fmt == kFmtQ82)
+        return P.mts == 2 ? launch_dense<2, kFmtQ82>(P, grid, bps, s) : launch_dense<1, kFmtQ82>(P, grid, bps, s);
+    if (fmt == kFmtQ4)
+        return P.mts == 2 ? launch_dense<2, kFmtQ4>(P, grid, bps, s) : launch_dense<1, kFmtQ4>(P, grid, bps, s);
+    return P.mts == 2 ? launch_dense<2, kFmtQ8>(P, grid, bps, s) : launch_dense<1, kFmtQ8>(P, grid, bps, s);
 }
 
 // Staging (plain or normed) into the workspace, then the dense matrix-core pass
@@ -410,7 +413,47 @@ extern "C" int prefill_gemm_q82(const int8_t *q, const uint16_t *row_scale, cons
     P.ldo = rows;
     P.act = act;
     P.mode = kDensePlain;
-    return run_dense(P, xp, xs, reinterpret_cast<float *>(ws + L.parts), tickets, s, true);
+    return run_dense(P, xp, xs, reinterpret_cast<float *>(ws + L.parts), tickets, s, kFmtQ82);
+}
+
+// q4tp prefill product (nemotron_prefill.rs, `pb_q4_bank` and its nibble and
+// code readers): the block format's matrix-core pass with the nibbles as
+// weights, the group scale 2^(base + code step) in place of the block scale
+// and -8 * scale as the group's bias (the nibble n enters as itself).
+extern "C" int prefill_gemm_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t rows,
+                                 int32_t cols, const float *X, int32_t n, float *Y, int32_t act, void *workspace,
+                                 size_t workspace_bytes, pg_stream_t stream) {
+    if (!nib || !params || !codes || !X || !Y) return PG_EINVAL;
+    if (rows <= 0 || cols <= 0 || n <= 0) return PG_EINVAL;
+    if (!aligned16(nib) || !aligned16(X) || !aligned16(Y) || ((uintptr_t)params & 3) || ((uintptr_t)codes & 3))
+        return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32 || n > 64) return PG_EUNSUPPORTED;
+    const size_t need = prefill_gemm_q8_workspace_bytes(rows, cols, n);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PG_EWORKSPACE;
+    const size_t yb = (size_t)n * rows * sizeof(float);
+    if (overlaps(Y, yb, workspace, need) || overlaps(Y, yb, X, (size_t)n * cols * sizeof(float))) return PG_EINVAL;
+    hipStream_t s = as_stream(stream);
+    char *ws = static_cast<char *>(workspace);
+    const OneLayout L = one_layout(rows, cols, n);
+    void *xp = ws, *xs = ws + L.xs;
+    unsigned *tickets = reinterpret_cast<unsigned *>(ws + L.tickets);
+    int rc = launch_stage_frag(X, n, cols, xp, xs, tickets, dense_panels(rows), s);
+    if (rc) return rc;
+    DenseArgs P{};
+    P.nib = nib;
+    P.params = params;
+    P.codes = codes;
+    P.code_stride = (5 * (cols / 32) + 7) / 8;
+    P.code_bytes = (uint32_t)rows * (uint32_t)P.code_stride;
+    P.rows = rows;
+    P.cols = cols;
+    P.n = n;
+    P.out = Y;
+    P.ldo = rows;
+    P.act = act;
+    P.mode = kDensePlain;
+    return run_dense(P, xp, xs, reinterpret_cast<float *>(ws + L.parts), tickets, s, kFmtQ4);
 }
 
 // ---------------------------------------------------------------- prefill frame

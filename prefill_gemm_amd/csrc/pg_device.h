@@ -77,6 +77,23 @@ __device__ __forceinline__ void q16_to_f32(const u32x4 w, float f[16]) {
     }
 }
 
+// Sixteen 4-bit codes n (two 32-bit words, columns 0..7 then 8..15: the low
+// half of byte j is column 2j, the high half column 2j + 1) as the bf16
+// values n, exact (integers below 16; unsigned byte to f32, the high half).
+__device__ __forceinline__ void nib16_to_bf16(const uint32_t w0, const uint32_t w1, bf16x8 &k0, bf16x8 &k1) {
+    const uint32_t in[2] = {w0, w1};
+    uint32_t p[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t lo = in[k] & 0x0F0F0F0Fu, hi = (in[k] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            p[4 * k + j] = pack_bf16_exact((float)((lo >> (8 * j)) & 0xFFu), (float)((hi >> (8 * j)) & 0xFFu));
+    }
+    k0 = __builtin_bit_cast(bf16x8, u32x4{p[0], p[1], p[2], p[3]});
+    k1 = __builtin_bit_cast(bf16x8, u32x4{p[4], p[5], p[6], p[7]});
+}
+
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, const f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
