@@ -381,6 +381,44 @@ def component_q82_bank(torch, pg, synth, reps=10, host_experts=16):
             "frac_hbm_peak": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def component_q4tp_bank(torch, pg, synth, reps=10, host_experts=16):
+    """The q4tp expert bank at the MoE pass's up shape: 128 experts of 1856 x 2688, the top 6
+    of the MoE component's router logits at 64 positions, relu^2; 16 experts drawn on the host,
+    the rest device copies at other addresses."""
+    import numpy as np
+    c = synth.moe(0)
+    E, n, k, H, I = 128, 64, c["top_k"], 2688, 1856
+    rng = synth.streams(29, host_experts)
+    ms = [synth.q4tp(rng[i], I, H) for i in range(host_experts)]
+    nib = torch.empty(E, I, H // 2, dtype=torch.uint8, device="cuda")
+    params = torch.empty(E, I, dtype=torch.int32, device="cuda")
+    codes = torch.empty(E, I, ms[0].codes.shape[1], dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        m = ms[e % host_experts]
+        nib[e].copy_(torch.as_tensor(m.nib))
+        params[e].copy_(torch.as_tensor(m.params.view(np.int32)))
+        codes[e].copy_(torch.as_tensor(m.codes))
+    X = to_dev(torch, c["X"])
+    logits = X @ to_dev(torch, c["Wr"]).t()
+    sel = torch.topk(logits, k, dim=1).indices.to(torch.int32).cpu().numpy()
+    counts = np.bincount(sel.reshape(-1), minlength=E).astype(np.int32)
+    lists = np.zeros((E, n), np.int32)
+    fill = np.zeros(E, np.int64)
+    for j, e in enumerate(sel.reshape(-1)):
+        lists[e, fill[e]] = j
+        fill[e] += 1
+    cnt, lst = to_dev(torch, counts), to_dev(torch, lists)
+    out = torch.empty(n * k, I, device="cuda")
+    t = time_graphs(torch, [one_graph(torch, [lambda: pg.expert_bank_q4tp(nib, params, codes, X, cnt, lst, src_div=k,
+                                                                           act=1, out=out)] * reps)], 3) / reps
+    active = int((counts > 0).sum())
+    nbytes = active * (I * H // 2 + I * 4 + I * ms[0].codes.shape[1])
+    return {"workload": "q4tp expert bank, MoE up shape: 128 experts 2688->1856, 64 positions top-6, relu^2",
+            "active_experts": active, "us": round(t * 1e3, 2), "bytes": int(nbytes),
+            "GB_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def component_attn(torch, pg, synth, reps=20):
     """Causal GQA prefill attention (32 query heads, 8 KV heads of 128) over a 64-position
     pass, first in its context and last in a 4096-position one: the KV append plus the
@@ -655,7 +693,8 @@ def main():
         print(json.dumps({"q82_gemv_frame_shapes": component_q82(torch, pg, synth),
                           "q4tp_gemv_frame_shapes": component_q4tp_argmax(torch, pg, synth),
                           "prefill_attention": component_attn(torch, pg, synth),
-                          "q82_expert_bank": component_q82_bank(torch, pg, synth)}), flush=True)
+                          "q82_expert_bank": component_q82_bank(torch, pg, synth),
+                          "q4tp_expert_bank": component_q4tp_bank(torch, pg, synth)}), flush=True)
         return
 
     log("building inputs ...")
@@ -748,6 +787,7 @@ def main():
         comp["q4tp_gemv_frame_shapes"] = component_q4tp_argmax(torch, pg, synth)
         comp["prefill_attention"] = component_attn(torch, pg, synth)
         comp["q82_expert_bank"] = component_q82_bank(torch, pg, synth)
+        comp["q4tp_expert_bank"] = component_q4tp_bank(torch, pg, synth)
         result["components"] = comp
         ceil = comp["hbm_read_ceiling"]["GB_s"]
         for e in (dense, gemv):
@@ -772,6 +812,9 @@ def main():
         bank = comp["q82_expert_bank"]
         R["expert_bank_kernel_q82"] = hbm_entry("expert_bank_kernel<AL, true> (q8_2f bank, MoE up shape)",
                                                 bank["bytes"], bank["us"], None, ceil)
+        qb = comp["q4tp_expert_bank"]
+        R["expert_bank_kernel_q4tp"] = hbm_entry("expert_bank_kernel<1, kExpQ4> (q4tp bank, MoE up shape)",
+                                                 qb["bytes"], qb["us"], None, ceil)
         att = comp["prefill_attention"]
         R["attn_prefill_kernel"] = {"kernel": "attn_prefill_kernel + merge (context 4096, f32 matrix cores)",
                                     "bound": "mfma", "achieved": att["ctx4096_TFLOP_s"], "peak": 157.3,

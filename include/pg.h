@@ -529,6 +529,25 @@ int expert_bank_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *
                     int32_t act, pg_stream_t stream);
 
 /*
+ * expert_bank_q4tp — the grouped expert product on the q4tp format
+ * (nemotron_prefill.rs, `pb_q4_bank` over the experts of a pass): for expert
+ * e < E and each of its listed entries j = lists[e][m], m < counts[e]:
+ *     out[j][r] = act( sum_c 2^(base_er + code_{e,r,c/32} step_er) (nib_er(c) - 8) x[j / src_div][c] )
+ * each expert's weights read once for all of its entries.  Layout per expert
+ * as gemv_q4tp: nib [E][rows][cols/2] (16-byte aligned), params [E][rows] u32
+ * (4-byte aligned), codes [E][rows][ceil(5 cols/32 / 8)]; x rows ldx floats
+ * apart (16-byte aligned, ldx % 4 == 0), out rows ldo floats apart; counts,
+ * lists and cap (<= 64) as expert_bank_q82.  The nibble n enters the matrix
+ * cores as itself (bf16, exact) and the - 8 as a per-block term -8 * scale
+ * times the block's sum of x; x as bf16 hi + lo.
+ * PG_EUNSUPPORTED: cols % 32 != 0, cap > 64, E > 1024, a code buffer under 4
+ * bytes.  PG_EINVAL: null or misaligned pointers, sizes < 1, act not 0/1.
+ */
+int expert_bank_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t E, int32_t rows,
+                     int32_t cols, const float *x, int64_t ldx, int32_t src_div, const int32_t *counts,
+                     const int32_t *lists, int32_t cap, float *out, int64_t ldo, int32_t act, pg_stream_t stream);
+
+/*
  * attn_kv_append — the pass's K and V rows into the caches (nemotron_prefill.rs,
  * `pb_kv_append`): kc[pos0 * width + i] = k[i], vc[...] = v[i] for i < n * width.
  *   k, v [n][width] f32, kc, vc [cap][width] f32 (width = nkv * hd, a multiple of 4;

@@ -92,6 +92,8 @@ def _declare(L):
     L.argmax_rows.argtypes = [_P, _i32, _i32, _P, _P]
     L.expert_bank_q82.argtypes = [_P, _P, _P, _i32, _i32, _i32, _P, ctypes.c_int64, _i32, _P, _P, _i32, _P,
                                   ctypes.c_int64, _i32, _P]
+    L.expert_bank_q4tp.argtypes = [_P, _P, _P, _i32, _i32, _i32, _P, ctypes.c_int64, _i32, _P, _P, _i32, _P,
+                                   ctypes.c_int64, _i32, _P]
     L.attn_kv_append.argtypes = [_P, _P, _i32, _i32, _i32, _P, _P, _i32, _P]
     L.attn_prefill.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _f, _P, _P, _sz, _P]
     L.attn_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
@@ -99,7 +101,7 @@ def _declare(L):
     L.moe_route_sigmoid.argtypes = [_P, _P, _i32, _i32, _i32, _i32, _f, _P, _P, _P]
     L.moe_grouped_sigmoid.argtypes = [_P, _i32, _i32, _P, _i32, _i32, _P, _i32, _f, _P, _P, _P, _i32, _P, _P, _P,
                                       _P, _P, _P, _f, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
-    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "prefill_gemm_q4tp", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
+    for name in ("gemv_q8", "gemv_f16", "gemv_q82", "prefill_gemm_q82", "prefill_gemm_q4tp", "gemv_q4tp", "argmax_rows", "moe_route_sigmoid", "moe_grouped_sigmoid", "attn_kv_append", "attn_prefill", "expert_bank_q82", "expert_bank_q4tp", "prefill_gemm_q8", "prefill_gemm_q8_noalloc", "add_rmsnorm", "moe_grouped",
                  "gemv_q8_addnorm", "prefill_gemm_q8_addnorm", "gemv_q8_residual", "gemv_q8_normed",
                  "decode_frame_q8_workspace_init", "decode_frame_q8_status", "pg_stream_read", "decode_frame_q8", "prefill_frame_q8", "prefill_frame_q8_meta"):
         getattr(L, name).restype = ctypes.c_int
@@ -600,6 +602,33 @@ def expert_bank_q82(q: torch.Tensor, rs: torch.Tensor, cf: torch.Tensor, x: torc
     _check("expert_bank_q82", lib().expert_bank_q82(_ptr(q), _ptr(rs), _ptr(cf), E, rows, cols, _ptr(x), cols,
                                                     src_div, _ptr(counts), _ptr(lists), lists.shape[1], _ptr(out),
                                                     rows, act, _stream(stream)))
+    return out
+
+
+def expert_bank_q4tp(nib: torch.Tensor, params: torch.Tensor, codes: torch.Tensor, x: torch.Tensor,
+                     counts: torch.Tensor, lists: torch.Tensor, src_div: int = 1, act: int = 0,
+                     out: torch.Tensor | None = None, n_out: int | None = None, stream=None):
+    """Grouped q4tp expert product: nib uint8 [E][rows][cols/2], params int32 [E][rows] (binary16
+    base low, step high), codes uint8 [E][rows][ceil(5 cols/32 / 8)], x f32 [*][cols], counts
+    int32 [E], lists int32 [E][cap]; out f32 [n_out][rows] (rows of listed entries are written)."""
+    _dev(nib, torch.uint8, "nib")
+    _dev(params, torch.int32, "params")
+    _dev(codes, torch.uint8, "codes")
+    _dev(x, torch.float32, "x")
+    _dev(counts, torch.int32, "counts")
+    _dev(lists, torch.int32, "lists")
+    E, rows, half = nib.shape
+    cols = 2 * half
+    if (params.shape != (E, rows) or codes.shape != (E, rows, (5 * (cols // 32) + 7) // 8) or x.shape[-1] != cols
+            or lists.shape[0] != E):
+        raise ValueError("nib [E][rows][cols/2], params [E][rows], codes [E][rows][ceil(5 cols/32 / 8)], "
+                         "x [*][cols], lists [E][cap]")
+    if out is None:
+        out = torch.zeros(n_out if n_out is not None else lists.shape[1], rows, dtype=torch.float32, device=x.device)
+    _dev(out, torch.float32, "out")
+    _check("expert_bank_q4tp", lib().expert_bank_q4tp(_ptr(nib), _ptr(params), _ptr(codes), E, rows, cols, _ptr(x),
+                                                      cols, src_div, _ptr(counts), _ptr(lists), lists.shape[1],
+                                                      _ptr(out), rows, act, _stream(stream)))
     return out
 
 

@@ -32,6 +32,13 @@ struct ExpertBank {
     const uint16_t *rs;
     const uint16_t *cf;
     long long rs_stride, cf_stride;
+    // q4tp banks (q, scale, bias unused): nibbles [E][rows][cols/2], parameter
+    // words [E][rows] (binary16 base low, step high), 5-bit group codes
+    // [E][rows][code_stride]; NULL nib: not q4tp.
+    const uint8_t *nib;
+    const uint32_t *params;
+    const uint8_t *codes;
+    int code_stride;
 };
 
 // Experts [0, experts); those with no entries are skipped.

@@ -68,6 +68,24 @@ static_assert(kExpLds + kExpMaxExperts * 4 + 16 <= 160 * 1024, "LDS of a compute
 
 constexpr int kExpNT = 0;  // weight load cache policy (2: non-temporal)
 
+// Bank formats (template argument FMT): the block format, q8_2f, and q4tp,
+// whose nibble n enters the matrix cores as the exact bf16 n while the - 8
+// rides in the per-block bias term as bias = -8 * group scale.
+enum ExpFmt { kExpQ8 = 0, kExpQ82 = 1, kExpQ4 = 2 };
+
+// Eight 4-bit codes (one dword, the low half of byte j is column 2j, the high
+// half column 2j + 1) as a bf16x8 operand of the exact values n.
+__device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t w) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint32_t p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        p[j] = pack_bf16_exact((float)((lo >> (8 * j)) & 0xFFu), (float)((hi >> (8 * j)) & 0xFFu));
+    bf16x8 r;
+    __builtin_memcpy(&r, p, 16);
+    return r;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t exp_rsrc(const void *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
@@ -178,7 +196,59 @@ struct ExpTgt {
     const float *s, *b;
     int vq[kExpTiles], vs[kExpTiles];
     bool live;
+    // q4tp: the expert's group codes and parameter words, and this lane's row
+    const uint8_t *c;
+    const uint32_t *pm;
+    int row[kExpTiles];
 };
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// q4tp: the raw material of a window's group scales for one lane: the 4-byte
+// code window holding the codes of its V blocks (moved back to end inside the
+// code buffer), the row's parameter word, and the bit where its first code
+// starts; kept as bits in the window registers until the window is taken.
+template <int D>
+__device__ __forceinline__ void q4_win_load(const ExpertBank &P, const ExpTgt &t, int w, int k, float (&dst)[D / 2]) {
+    constexpr int V = D / 2;
+    const int g = (threadIdx.x & 63) >> 4;
+    if (!t.live) {
+#pragma unroll
+        for (int j = 0; j < V; ++j) dst[j] = 0.0f;
+        return;
+    }
+    const uint32_t fbit = 5u * (uint32_t)(2 * D * w + V * g);
+    const uint32_t total = (uint32_t)P.rows * (uint32_t)P.code_stride;
+    const uint32_t absb = (uint32_t)t.row[k] * (uint32_t)P.code_stride + (fbit >> 3);
+    const uint32_t at = min(absb, total - 4u);
+    uint32_t win;
+    __builtin_memcpy(&win, t.c + at, 4);
+    dst[0] = __builtin_bit_cast(float, win);
+    dst[1] = __builtin_bit_cast(float, t.pm[t.row[k]]);
+    dst[2] = __builtin_bit_cast(float, 8u * (absb - at) + (fbit & 7u));
+    dst[3] = __builtin_bit_cast(float, (uint32_t)(2 * D * w + V * g));  // first block of the share
+}
+
+// The group scales of a q4tp window (from q4_win_load's bits) and the block
+// biases -8 * scale: scale_j = 2^(base + code_j step) (hardware exp2 of the
+// f32 fma, as the q4tp GEMV).
+// Blocks past the row's last (nb) get scale 0: their codes are not the row's.
+template <int V>
+__device__ __forceinline__ void q4_win_take(const float (&raw)[V], int nb, float (&sw)[V], float (&bw)[V]) {
+    static_assert(V >= 4, "the window registers hold four words of raw material");
+    const uint32_t win = __builtin_bit_cast(uint32_t, raw[0]);
+    const uint32_t pw = __builtin_bit_cast(uint32_t, raw[1]);
+    const uint32_t sh = __builtin_bit_cast(uint32_t, raw[2]);
+    const int fb = (int)__builtin_bit_cast(uint32_t, raw[3]);
+    const float base = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw & 0xFFFFu));
+    const float step = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw >> 16));
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const uint32_t code = (uint32_t)(((uint64_t)win >> (sh + 5u * j)) & 31u);
+        sw[j] = fb + j < nb ? __builtin_amdgcn_exp2f(fmaf((float)code, step, base)) : 0.0f;
+        bw[j] = -8.0f * sw[j];
+    }
+}
 
 // One pass over a work item (expert e, weight rows rb * kExpRows ..) for its
 // entries m0 .. m0 + cnt - 1 (at most kExpGroup): its column chunks (staged
@@ -186,12 +256,13 @@ struct ExpTgt {
 // take more than one chunk), its steps, and its outputs.  The weight ring and
 // the scale windows come in holding this pass's first steps and leave holding
 // those of the pass after it (target tn).
-template <int MT, int D, int AL, bool Q82>
+template <int MT, int D, int AL, int FMT>
 __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int cnt, int rb, bool fresh,
                                          const ExpTgt &tc, const ExpTgt &tn, u32x4 (&wq)[D][kExpTiles],
                                          float (&sw)[kExpTiles][D / 2], float (&bw)[kExpTiles][D / 2],
                                          float (&swn)[kExpTiles][D / 2], float (&bwn)[kExpTiles][D / 2],
                                          char *lds) {
+    constexpr bool Q82 = FMT == kExpQ82, Q4 = FMT == kExpQ4;
     constexpr int T = kExpTiles;
     constexpr int V = D / 2;             // blocks of a window per lane group
     constexpr int LW = AL < V ? AL : V;  // floats per scale / bias load
@@ -201,8 +272,8 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     const int nb = P.cols >> 5;
     const int np = (nb + 1) >> 1;
     const int npp = (np + D - 1) / D * D;
-    const int q_bytes = P.rows * P.cols;
-    const int s_bytes = Q82 ? 0 : P.rows * nb * 4;  // q8_2f: no block factors, the windows move nothing
+    const int q_bytes = Q4 ? P.rows * (P.cols >> 1) : P.rows * P.cols;
+    const int s_bytes = (Q82 || Q4) ? 0 : P.rows * nb * 4;  // q8_2f: no block factors, the windows move nothing
     const int32_t *list = P.lists + (long long)e * P.cap + m0;
     const int kp = exp_chunk_pairs(cnt, MT, D, np);
     const bool chunked = kp < npp;
@@ -224,13 +295,25 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     auto load = [&](const ExpTgt &t, int p, u32x4 (&w)[T]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rq = exp_rsrc(t.q, t.live && p < np ? q_bytes : 0);
 #pragma unroll
-        for (int k = 0; k < T; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 64 * p, kExpNT);
+        for (int k = 0; k < T; ++k) {
+            if constexpr (Q4) {  // 8 bytes: 16 nibbles of the lane's 16 columns
+                const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, t.vq[k], 32 * p, kExpNT));
+                w[k] = u32x4{v.x, v.y, 0u, 0u};
+            } else {
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 64 * p, kExpNT);
+            }
+        }
     };
     // Scales and biases come a window of D steps (2D blocks) at a time: lane
     // group g holds blocks V g .. V g + V - 1 of the window for its row, and
     // a step takes its two blocks from the group that holds them (a lane
     // permute), so that the four lanes of a row do not each load them.
     auto load_win = [&](const ExpTgt &t, int w) __attribute__((always_inline)) {
+        if constexpr (Q4) {
+#pragma unroll
+            for (int k = 0; k < T; ++k) q4_win_load<D>(P, t, w, k, swn[k]);
+            return;
+        }
         const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t.s, t.live ? s_bytes : 0);
         const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t.b, t.live ? s_bytes : 0);
         const int off = 8 * D * w;
@@ -294,10 +377,16 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             b[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev + 1])));
             // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
             // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
-            const auto e0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
-            const auto e1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
-            b0[k] = q8_to_bf16(e0[0], e1[0]);
-            b1[k] = q8_to_bf16(e0[1], e1[1]);
+            if constexpr (Q4) {  // the second 8 columns (dword y) move across
+                const auto e = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].y, false, false);
+                b0[k] = nib8_to_bf16(e[0]);
+                b1[k] = nib8_to_bf16(e[1]);
+            } else {
+                const auto e0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
+                const auto e1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
+                b0[k] = q8_to_bf16(e0[0], e1[0]);
+                b1[k] = q8_to_bf16(e0[1], e1[1]);
+            }
         }
         const f32x4 z{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -349,12 +438,17 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
         const int c1 = min(npp, c0 + kp);
         for (int p0 = c0; p0 < c1; p0 += D) {
 #pragma unroll
-            for (int k = 0; k < T; ++k)
+            for (int k = 0; k < T; ++k) {
+                if constexpr (Q4) {
+                    q4_win_take<V>(swn[k], nb, sw[k], bw[k]);
+                } else {
 #pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    sw[k][j] = swn[k][j];
-                    bw[k][j] = bwn[k][j];
+                    for (int j = 0; j < V; ++j) {
+                        sw[k][j] = swn[k][j];
+                        bw[k][j] = bwn[k][j];
+                    }
                 }
+            }
             const bool last = p0 + D >= npp;
             const ExpTgt &tl = last ? tn : tc;
             const int pl = last ? p0 + D - npp : p0 + D;
@@ -393,8 +487,9 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 // once for all of that expert's items in its share, and its weight stream
 // runs from one item into the next without draining.  An expert with more
 // than kExpGroup entries takes one pass per group of kExpGroup over each item.
-template <int AL, bool Q82>
+template <int AL, int FMT>
 __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
+    constexpr bool Q82 = FMT == kExpQ82, Q4 = FMT == kExpQ4;
     extern __shared__ u32x4 exp_lds[];
     __shared__ int act[kExpMaxExperts];
     __shared__ int nact_s;
@@ -431,14 +526,21 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
         const int it = t.live ? item : i1 - 1;
         const int e = __builtin_amdgcn_readfirstlane(act[it / RB]);
         const int rb = it % RB;
-        t.q = P.q + (long long)e * P.q_stride;
+        if (Q4) {
+            t.q = reinterpret_cast<const int8_t *>(P.nib + (long long)e * P.rows * (P.cols >> 1));
+            t.c = P.codes + (long long)e * P.rows * P.code_stride;
+            t.pm = P.params + (long long)e * P.rows;
+        } else {
+            t.q = P.q + (long long)e * P.q_stride;
+        }
         t.s = P.scale + (long long)e * P.s_stride;
         t.b = P.bias + (long long)e * P.s_stride;
 #pragma unroll
         for (int k = 0; k < T; ++k) {
             const int r = min(rb * kExpRows + (wave * T + k) * 16 + i16, P.rows - 1);
-            t.vq[k] = r * P.cols + 16 * g;
+            t.vq[k] = Q4 ? r * (P.cols >> 1) + 8 * g : r * P.cols + 16 * g;
             t.vs[k] = (r * nb + V * g) * 4;
+            t.row[k] = r;
         }
         return t;
     };
@@ -450,22 +552,40 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
     float sw[T][V], bw[T][V], swn[T][V], bwn[T][V];
     {
         const ExpTgt t0 = target(i0);
-        const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t0.s, Q82 ? 0 : P.rows * nb * 4);
-        const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t0.b, Q82 ? 0 : P.rows * nb * 4);
+        if constexpr (Q4) {
 #pragma unroll
-        for (int k = 0; k < T; ++k)
+            for (int k = 0; k < T; ++k) {
+                q4_win_load<D>(P, t0, 0, k, swn[k]);
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t0.vs[k], 4 * j, 0));
-                bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t0.vs[k], 4 * j, 0));
+                for (int j = 0; j < V; ++j) bwn[k][j] = 0.0f;
             }
+        } else {
+            const __amdgpu_buffer_rsrc_t rs = exp_rsrc(t0.s, Q82 ? 0 : P.rows * nb * 4);
+            const __amdgpu_buffer_rsrc_t rbs = exp_rsrc(t0.b, Q82 ? 0 : P.rows * nb * 4);
+#pragma unroll
+            for (int k = 0; k < T; ++k)
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t0.vs[k], 4 * j, 0));
+                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t0.vs[k], 4 * j, 0));
+                }
+        }
         __builtin_amdgcn_sched_barrier(kExpSched);
         const int np = (nb + 1) >> 1;
         static_for<D>([&](auto uc) __attribute__((always_inline)) {
             constexpr int u = decltype(uc)::value;
-            const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
 #pragma unroll
-            for (int k = 0; k < T; ++k) wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 64 * u, kExpNT);
+            for (int k = 0; k < T; ++k) {
+                if constexpr (Q4) {
+                    const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * (P.cols >> 1) : 0);
+                    const u32x2 v =
+                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, t0.vq[k], 32 * u, kExpNT));
+                    wq[u][k] = u32x4{v.x, v.y, 0u, 0u};
+                } else {
+                    const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
+                    wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 64 * u, kExpNT);
+                }
+            }
             __builtin_amdgcn_sched_barrier(kExpSched);
         });
     }
@@ -483,9 +603,9 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
             const bool fresh = e != prev || groups > 1;
             const ExpTgt &nx = gi + 1 < groups ? tc : tn;
             if (kExpGroup <= 16 || cg <= 16)
-                exp_item<1, D, AL, Q82>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+                exp_item<1, D, AL, FMT>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
             else
-                exp_item<2, D, AL, Q82>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
+                exp_item<2, D, AL, FMT>(P, e, m0, cg, rb, fresh, tc, nx, wq, sw, bw, swn, bwn, lds);
         }
         prev = e;
     }
@@ -502,12 +622,12 @@ static int exp_grid() {
     return cus;
 }
 
-template <int AL, bool Q82 = false>
+template <int AL, int FMT = kExpQ8>
 static int launch_bank(const ExpertBank &P, hipStream_t s) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL, Q82>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL, FMT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kExpLds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL((expert_bank_kernel<AL, Q82>), dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
+    hipLaunchKernelGGL((expert_bank_kernel<AL, FMT>), dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
     return launch_status();
 }
 
@@ -516,10 +636,14 @@ int launch_expert_bank(const ExpertBank &P, hipStream_t s) {
     if (P.experts < 1 || P.experts > kExpMaxExperts) return PG_EUNSUPPORTED;
     if ((long long)P.rows * P.cols >= (1ll << 31)) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
     const int nb = P.cols / 32;
+    if (P.nib) {  // q4tp: code windows instead of scale loads
+        if (!P.params || !P.codes || (long long)P.rows * P.code_stride < 4) return PG_EINVAL;
+        return launch_bank<1, kExpQ4>(P, s);
+    }
     if (P.rs) {  // q8_2f: the (empty) window loads take the widest form the block count allows
         if (!P.cf) return PG_EINVAL;
-        return nb % 4 == 0 ? launch_bank<4, true>(P, s) : nb % 2 == 0 ? launch_bank<2, true>(P, s)
-                                                                       : launch_bank<1, true>(P, s);
+        return nb % 4 == 0 ? launch_bank<4, kExpQ82>(P, s) : nb % 2 == 0 ? launch_bank<2, kExpQ82>(P, s)
+                                                                          : launch_bank<1, kExpQ82>(P, s);
     }
     // Widest scale / bias loads: a row's blocks must start on that boundary.
     const uintptr_t a = (uintptr_t)P.scale | (uintptr_t)P.bias;
@@ -563,5 +687,39 @@ extern "C" int expert_bank_q82(const int8_t *q, const uint16_t *row_scale, const
     P.cf = col_field;
     P.rs_stride = rows;
     P.cf_stride = cols;
+    return launch_expert_bank(P, as_stream(stream));
+}
+
+// The q4tp expert bank over a pass (nemotron_prefill.rs, `pb_q4_bank` and its
+// nibble and code readers: 4-bit codes, a binary16 base and step per row, a
+// 5-bit code per 32-column group; w = 2^(base + code step) (nib - 8)), each
+// selected expert's weights streamed once for all of its entries.
+extern "C" int expert_bank_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t E,
+                                int32_t rows, int32_t cols, const float *x, int64_t ldx, int32_t src_div,
+                                const int32_t *counts, const int32_t *lists, int32_t cap, float *out, int64_t ldo,
+                                int32_t act, pg_stream_t stream) {
+    if (!nib || !params || !codes || !x || !counts || !lists || !out) return PG_EINVAL;
+    if (E <= 0 || rows <= 0 || cols <= 0 || cap <= 0 || src_div <= 0 || ldx < cols || ldo < rows) return PG_EINVAL;
+    if (act != 0 && act != 1) return PG_EINVAL;
+    if (cols % 32) return PG_EUNSUPPORTED;
+    if (!aligned16(nib) || !aligned16(x) || ldx % 4 || ((uintptr_t)params & 3)) return PG_EINVAL;
+    ExpertBank P{};
+    P.rows = rows;
+    P.cols = cols;
+    P.x = x;
+    P.ldx = ldx;
+    P.src_div = src_div;
+    P.counts = counts;
+    P.lists = lists;
+    P.cap = cap;
+    P.experts = E;
+    P.out = out;
+    P.ldo = ldo;
+    P.act = act;
+    P.nib = nib;
+    P.params = params;
+    P.codes = codes;
+    P.code_stride = (5 * (cols / 32) + 7) / 8;
+    if ((long long)rows * P.code_stride < 4) return PG_EUNSUPPORTED;  // 4-byte code windows
     return launch_expert_bank(P, as_stream(stream));
 }
