@@ -473,9 +473,7 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     const i32x4 rx = buf_rsrc(P.xp, (uint32_t)nb * P.mts * 4096u);
     const i32x4 rxs = buf_rsrc(P.xs, (uint32_t)ng * P.mts * 2048u);
     auto live_rsrc = [](i32x4 r, bool live) __attribute__((always_inline)) {
-#ifndef PG_DENSE_NOSKIP
         r[2] = live ? r[2] : 0;
-#endif
         return r;
     };
     // LDS byte address of slot i (16 bytes) of the ring.
