@@ -671,8 +671,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU part in this build "
-              "(--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU part (one process drives "
+              "one device; --gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration:
