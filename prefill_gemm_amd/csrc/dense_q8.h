@@ -35,9 +35,11 @@
 //    banks;
 //  - scales and biases: 16 rows x 4 blocks (4 bytes a lane) per instruction;
 //  - activation fragments and block sums: as staged, 1 KB per instruction.
-// A wave waits for its own copies of stage c + 1 (memory counter) before the
-// stage barrier; copies are issued in the same order every stage, so the wait
-// is one constant.  Blocks past the range inside a stage are weighted by
+// Each stage requests the next activations at its start and the weights (and a
+// bias share) once its matrix-core work is issued, so the activations are
+// never queued behind that stage's weight requests.  A wave waits for its own
+// copies of stage c + 1 (memory counter) before the stage barrier; copies are
+// issued in the same order every stage, so the wait is one constant.  Blocks past the range inside a stage are weighted by
 // zero, and copies for stages past the end go through empty buffer
 // resources (zeros, no memory traffic), which keeps every stage one
 // branch-free stretch.
@@ -634,12 +636,11 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     for (int c = 0; c < nst; ++c) {
         const int u = c % C::kStagesPerGroup;
         const int it = c / C::kStagesPerGroup;
-        // Refill the slots stage c - 1 used (every wave is past it), and copy a
-        // share of the next group's biases (its slot was last read a group ago).
+        // Refill the activation slot stage c - 1 used (every wave is past it).
+        // The weight refill waits until this stage's matrix-core work is issued:
+        // a compute unit returns its requests in order, so activations requested
+        // ahead of weights arrive without waiting for them.
         copy_x(c + NX - 1);
-        copy_w(c + NW - 1);
-#pragma unroll
-        for (int k = 0; k < C::kBPer; ++k) copy_b(it + 1, (4 * w + u) * C::kBPer + k);
         __builtin_amdgcn_sched_barrier(0);
         const u32x4 *xst = lds + C::kXBase + (c % NX) * C::kXStage + lane;
         const u32x4 *wst = lds + C::kWBase + (c % NW) * C::kWStage;
@@ -779,6 +780,11 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // The weight slot stage c - 1 used, and a share of the next group's
+        // biases (their slot was last read a group ago).
+        copy_w(c + NW - 1);
+#pragma unroll
+        for (int k = 0; k < C::kBPer; ++k) copy_b(it + 1, (4 * w + u) * C::kBPer + k);
 
         if (!Q82 && !Q4 && u == C::kStagesPerGroup - 1 && kq == it % NK) bias_mfma(it);
         // q4tp: the group's biases are complete one barrier after its last stage
