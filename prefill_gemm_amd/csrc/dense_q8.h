@@ -809,46 +809,57 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
     // ------------------------------------------------------------ epilogue
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing refills
     __builtin_amdgcn_s_barrier();
-    // The K waves' partials meet in LDS as 16-byte pieces: piece (v / 4) of
-    // tile (rt, mt) of wave kq sits at red4[((kq - 1, rh, rt, mt), v / 4, lane)].
+    // The K waves' partials meet in LDS as 16-byte pieces, and wave kq sums
+    // piece v4 == kq of every tile (rt, mt) over the K waves in K order (the
+    // same order for every piece).  Piece v4 of tile (rt, mt) from wave
+    // k != v4 sits at red4[((j, rh, rt, mt), v4, lane)], j = k - (k > v4).
+    // Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h + (v %
+    // 4), row 64 rh + 32 rt + ml of the panel.
     u32x4 *red4 = lds;
     auto red_at = [&](int k, int rt, int mt, int v4) __attribute__((always_inline)) {
-        return (((((k - 1) * 2 + rh) * 2 + rt) * MT + mt) * 4 + v4) * 64 + lane;
+        const int j = k - (k > v4 ? 1 : 0);
+        return ((((j * 2 + rh) * 2 + rt) * MT + mt) * 4 + v4) * 64 + lane;
     };
-    if (kq > 0) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
+            for (int v4 = 0; v4 < 4; ++v4)
+                if (v4 != kq)
                     red4[red_at(kq, rt, mt, v4)] =
                         u32x4{__float_as_uint(acc[rt][mt][4 * v4]), __float_as_uint(acc[rt][mt][4 * v4 + 1]),
                               __float_as_uint(acc[rt][mt][4 * v4 + 2]), __float_as_uint(acc[rt][mt][4 * v4 + 3])};
-    }
     __syncthreads();
-    // On the kq == 0 waves: add the other K waves' partials (in order).
-    // Element v of tile (rt, mt) is position 32 mt + 8 (v / 4) + 4 h + (v %
-    // 4), row 64 rh + 32 rt + ml of the panel.
-    if (kq == 0) {
+    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);  // [m][128]
+    const bool direct = P.splits == 1 && P.mode == kDensePlain;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+        if (v4 != kq) continue;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt) {
+                float sum[4];
 #pragma unroll
-                for (int k = 1; k < NK; ++k)
+                for (int k = 0; k < NK; ++k) {
+                    float pk[4];
+                    if (k == v4) {
 #pragma unroll
-                    for (int v4 = 0; v4 < 4; ++v4) {
+                        for (int i = 0; i < 4; ++i) pk[i] = acc[rt][mt][4 * v4 + i];
+                    } else {
                         const u32x4 r = red4[red_at(k, rt, mt, v4)];
-                        acc[rt][mt][4 * v4] += __uint_as_float(r.x);
-                        acc[rt][mt][4 * v4 + 1] += __uint_as_float(r.y);
-                        acc[rt][mt][4 * v4 + 2] += __uint_as_float(r.z);
-                        acc[rt][mt][4 * v4 + 3] += __uint_as_float(r.w);
+                        pk[0] = __uint_as_float(r.x);
+                        pk[1] = __uint_as_float(r.y);
+                        pk[2] = __uint_as_float(r.z);
+                        pk[3] = __uint_as_float(r.w);
                     }
-    }
-    float *tile = reinterpret_cast<float *>(lds + C::kTileBase);  // [m][128]
-    const bool direct = P.splits == 1 && P.mode == kDensePlain;
-    if (kq == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sum[i] = k == 0 ? pk[i] : sum[i] + pk[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[rt][mt][4 * v4 + i] = sum[i];
+            }
         if (direct) {
             // Plain, unsplit: straight to the output (bounds by predication).
 #pragma unroll
@@ -858,9 +869,9 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-                        const float y = apply_act(P.act, Q82 ? acc[rt][mt][v] * rsc : acc[rt][mt][v]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 32 * mt + 8 * v4 + 4 * h + i;
+                        const float y = apply_act(P.act, Q82 ? acc[rt][mt][4 * v4 + i] * rsc : acc[rt][mt][4 * v4 + i]);
                         if (r < P.rows && m < P.n) P.out[m * P.ldo + r] = y;
                     }
             }
@@ -871,8 +882,8 @@ __device__ __forceinline__ void dense_panel(const DenseArgs &P, const int r_base
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        tile[(32 * mt + 8 * (v >> 2) + 4 * h + (v & 3)) * 128 + rl] = acc[rt][mt][v];
+                    for (int i = 0; i < 4; ++i)
+                        tile[(32 * mt + 8 * v4 + 4 * h + i) * 128 + rl] = acc[rt][mt][4 * v4 + i];
             }
         }
     }
