@@ -20,8 +20,11 @@
 //    to about 2^-17), staged once per workgroup in LDS from the f32 rows,
 //    together with the f32 block sums that the bias multiplies.
 // Each wave owns kExpTiles tiles of 16 weight rows over all columns, with
-// kExpDepth steps of weights in flight; the block scales and biases arrive a
-// window of steps at a time, spread over the four lanes of a row.  When the
+// kExpDepth steps of weights in flight, requested kExpBurst at a time (a
+// burst reads 512 contiguous bytes of each of its 16 rows, which HBM serves
+// better than the same bytes spread over single steps); the block scales
+// and biases arrive a window of steps at a time, spread over the four lanes
+// of a row.  When the
 // entries' staged rows exceed the LDS budget, the columns are taken in
 // chunks, each staged between two barriers.
 #include "expert_q8.h"
@@ -39,7 +42,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kExpSched = 0;
 constexpr int kExpThreads = 512;
 constexpr int kExpWaves = kExpThreads / kWave;
-constexpr int kExpDepth = 8;
+constexpr int kExpDepth = 16;  // q4tp: 8 (exp_depth)
+constexpr int kExpBurst = 8;   // ring slots refilled together
 constexpr int kExpTiles = 1;                    // 16-row weight tiles per wave
 constexpr int kExpRows = kExpWaves * 16 * kExpTiles;   // weight rows of one work item
 constexpr int kExpGroup = 16;                // entries per pass over an item
@@ -65,6 +69,7 @@ __device__ __forceinline__ int exp_chunk_pairs(int cnt, int mt, int d, int np) {
 // One ring of steps must fit the LDS budget at the largest entry count.
 static_assert(exp_chunk_bytes(kExpDepth, kExpGroup, kExpGroup / 16) <= kExpLds, "LDS budget");
 static_assert(kExpLds + kExpMaxExperts * 4 + 16 <= 160 * 1024, "LDS of a compute unit");
+static_assert(kExpDepth % kExpBurst == 0, "the ring refills in whole bursts");
 
 constexpr int kExpNT = 0;  // weight load cache policy (2: non-temporal)
 
@@ -211,6 +216,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int D>
 __device__ __forceinline__ void q4_win_load(const ExpertBank &P, const ExpTgt &t, int w, int k, float (&dst)[D / 2]) {
     constexpr int V = D / 2;
+    static_assert(5 * V + 7 <= 32, "a window's codes fit one 4-byte code window");
     const int g = (threadIdx.x & 63) >> 4;
     if (!t.live) {
 #pragma unroll
@@ -458,7 +464,11 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                 constexpr int u = decltype(uc)::value;
                 const int p = p0 + u;
                 if (p < np) compute(uc, p, 2 * c0, wq[u]);
-                load(tl, pl + u, wq[u]);
+                // after the last step of a burst, its slots are refilled together
+                if constexpr (u % kExpBurst == kExpBurst - 1) {
+#pragma unroll
+                    for (int j = u + 1 - kExpBurst; j <= u; ++j) load(tl, pl + j, wq[j]);
+                }
                 __builtin_amdgcn_sched_barrier(kExpSched);
             });
         }
@@ -487,13 +497,18 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 // once for all of that expert's items in its share, and its weight stream
 // runs from one item into the next without draining.  An expert with more
 // than kExpGroup entries takes one pass per group of kExpGroup over each item.
+// Ring depth of a format: q4tp's scale window reads the codes of its blocks
+// from one 4-byte window, which holds those of 8 steps at most.
+template <int FMT>
+constexpr int exp_depth() { return FMT == kExpQ4 ? 8 : kExpDepth; }
+
 template <int AL, int FMT>
 __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
     constexpr bool Q82 = FMT == kExpQ82, Q4 = FMT == kExpQ4;
     extern __shared__ u32x4 exp_lds[];
     __shared__ int act[kExpMaxExperts];
     __shared__ int nact_s;
-    constexpr int D = kExpDepth, T = kExpTiles, V = D / 2;
+    constexpr int D = exp_depth<FMT>(), T = kExpTiles, V = D / 2;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int i16 = lane & 15, g = lane >> 4;
