@@ -142,8 +142,14 @@ using DCfg = DenseCfg<MT, kDNK, kDNX, kDNW>;
 template <int MT, int FMT>
 __global__ __launch_bounds__(DCfg<MT>::kThreads) void dense_kernel(DenseArgs P, int bps) {
     extern __shared__ u32x4 dlds[];
-    const int id = blockIdx.x;
-    const int split = id % P.splits, panel = id / P.splits;
+    // Workgroups go to the 8 chiplets in turn (id % 8), and each chiplet has
+    // its own L2: chiplet x takes a contiguous run of items in split-major
+    // order, so that its workgroups share the staged activations of one or
+    // two K ranges.
+    const int G = gridDim.x, x = blockIdx.x % 8;
+    const int id = (x * (G / 8) + min(x, G % 8)) + blockIdx.x / 8;
+    const int panels = (P.rows + DCfg<MT>::kRows - 1) / DCfg<MT>::kRows;
+    const int split = id / panels, panel = id % panels;
     const int nb = P.cols >> 5;
     const int kb0 = split * bps;
     const int kb1 = min(nb, kb0 + bps);
