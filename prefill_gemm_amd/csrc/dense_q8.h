@@ -20,10 +20,13 @@
 // Work of one workgroup: 128 weight rows x a range of blocks x all positions,
 // 2 NK waves.  Wave (rh, kq) owns rows 64 rh .. 64 rh + 63 (two matrix-core
 // row tiles, so every activation fragment read from LDS feeds two weight
-// tiles) and blocks kq * 4/NK .. of every stage of four blocks; the NK
-// partial sums of a row half meet in LDS at the end.  With NK = 4 two waves
-// share every SIMD, so one wave's matrix-core chain overlaps the other's
-// vector work.
+// tiles) and blocks kq * 4/NK .. of every stage of four blocks; at the end
+// the NK partial sums of a row half meet in LDS, every K wave adding one
+// quarter of each tile.  With NK = 4 two waves share every SIMD, so one
+// wave's matrix-core chain overlaps the other's vector work.  Workgroup ids
+// go to the chiplets in turn; the kernel maps them so that each chiplet takes
+// a contiguous run of (split, panel) items and its L2 holds the staged
+// activations of one or two K ranges.
 //
 // Memory path.  Every byte moves from global memory straight into LDS
 // (buffer loads to LDS, no registers), shared out over all waves, NX - 1
