@@ -538,9 +538,10 @@ int expert_bank_q82(const int8_t *q, const uint16_t *row_scale, const uint16_t *
  * (4-byte aligned), codes [E][rows][ceil(5 cols/32 / 8)]; x rows ldx floats
  * apart (16-byte aligned, ldx % 4 == 0), out rows ldo floats apart; counts,
  * lists and cap (<= 64) as expert_bank_q82.  The nibble n enters the matrix
- * cores as itself (bf16, exact) and the - 8 as a per-block term -8 * scale
- * times the block's sum of x; x as bf16 hi + lo.
- * PG_EUNSUPPORTED: cols % 32 != 0, cap > 64, E > 1024, a code buffer under 4
+ * cores as 128 + n (bf16, exact) and the - (128 + 8) as a per-block term
+ * -136 * scale times the block's sum of the activations as the products see
+ * them (bf16 hi + lo).
+ * PG_EUNSUPPORTED: cols % 32 != 0, cap > 64, E > 1024, a code buffer under 8
  * bytes.  PG_EINVAL: null or misaligned pointers, sizes < 1, act not 0/1.
  */
 int expert_bank_q4tp(const uint8_t *nib, const uint32_t *params, const uint8_t *codes, int32_t E, int32_t rows,

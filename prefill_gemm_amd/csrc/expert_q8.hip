@@ -16,6 +16,10 @@
 //  - lanes l and l + 32 trade the upper 8 bytes of their load
 //    (v_permlane32_swap), so that each matrix-core product sees 32 columns of
 //    one block and the block scale can multiply its result;
+//  - q4tp: a lane's 16 bytes cover one block of a pair of steps, and the four
+//    lane groups of a row transpose them (two lane-half swaps, two row swaps)
+//    to 8 columns of each block; a nibble n enters as the bf16 bit pattern of
+//    128 + n (one and-or for two), which the block term corrects;
 //  - A operand = the entries' activations as bf16 hi + lo (two products, exact
 //    to about 2^-17), staged once per workgroup in LDS from the f32 rows,
 //    together with the f32 block sums that the bias multiplies.
@@ -42,7 +46,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kExpSched = 0;
 constexpr int kExpThreads = 512;
 constexpr int kExpWaves = kExpThreads / kWave;
-constexpr int kExpDepth = 16;  // q4tp: 8 (exp_depth)
+constexpr int kExpDepth = 16;
 constexpr int kExpBurst = 8;   // ring slots refilled together
 constexpr int kExpTiles = 1;                    // 16-row weight tiles per wave
 constexpr int kExpRows = kExpWaves * 16 * kExpTiles;   // weight rows of one work item
@@ -74,18 +78,26 @@ static_assert(kExpDepth % kExpBurst == 0, "the ring refills in whole bursts");
 constexpr int kExpNT = 0;  // weight load cache policy (2: non-temporal)
 
 // Bank formats (template argument FMT): the block format, q8_2f, and q4tp,
-// whose nibble n enters the matrix cores as the exact bf16 n while the - 8
-// rides in the per-block bias term as bias = -8 * group scale.
+// whose nibble n enters the matrix cores as the exact bf16 128 + n while the
+// - (128 + 8) rides in the per-block term: group scale times the block's sum
+// of the staged activations times -136 (staged with them).
 enum ExpFmt { kExpQ8 = 0, kExpQ82 = 1, kExpQ4 = 2 };
 
+// (x & m) | c in one instruction (m a scalar, c a vector register).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
 // Eight 4-bit codes (one dword, the low half of byte j is column 2j, the high
-// half column 2j + 1) as a bf16x8 operand of the exact values n.
-__device__ __forceinline__ bf16x8 nib8_to_bf16(uint32_t w) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+// half column 2j + 1) as a bf16x8 operand of the exact values 128 + n, in the
+// column order 0 4 1 5 2 6 3 7 (dword j = columns j and j + 4).
+__device__ __forceinline__ bf16x8 nib8_to_bf16_off(uint32_t w) {
+    // 0x4300 | n is the bf16 of 128 + n (n < 128 fits the 7 fraction bits at 2^7)
     uint32_t p[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        p[j] = pack_bf16_exact((float)((lo >> (8 * j)) & 0xFFu), (float)((hi >> (8 * j)) & 0xFFu));
+    for (int j = 0; j < 4; ++j) p[j] = and_or(w >> (4 * j), 0x000F000Fu, 0x43004300u);
     bf16x8 r;
     __builtin_memcpy(&r, p, 16);
     return r;
@@ -124,7 +136,7 @@ constexpr int kStageBatch = 6;
 
 // cf: the expert's binary16 column field (q8_2f), multiplied into the staged
 // activations; NULL for the block format.
-template <int MT>
+template <int MT, bool NIB>
 __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *list, int cnt, int cb0,
                                           int kp, char *lds, const uint16_t *cf) {
     const int nb = P.cols >> 5;
@@ -169,11 +181,17 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] *= (float)c[j];
             }
+            if constexpr (NIB) {  // the nibble operand's column order 0 4 1 5 2 6 3 7
+                const float t[8] = {v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = t[j];
+            }
             __bf16 hi[8], lo[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 hi[j] = to_bf16(v[j]);
                 lo[j] = to_bf16(v[j] - (float)hi[j]);
+                if constexpr (NIB) v[j] = (float)hi[j] + (float)lo[j];  // the block sum of what the products see
             }
             u32x4 h4, l4;
             __builtin_memcpy(&h4, hi, 16);
@@ -186,6 +204,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
             float sum = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
             sum += __shfl_xor(sum, 1, kWave);
             sum += __shfl_xor(sum, 2, kWave);
+            if constexpr (NIB) sum *= -136.0f;
             if (in && i == 0 && r < 16 * MT) xsum[bl * 16 * MT + r] = sum;
         }
     }
@@ -209,14 +228,14 @@ struct ExpTgt {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// q4tp: the raw material of a window's group scales for one lane: the 4-byte
+// q4tp: the raw material of a window's group scales for one lane: the 8-byte
 // code window holding the codes of its V blocks (moved back to end inside the
 // code buffer), the row's parameter word, and the bit where its first code
 // starts; kept as bits in the window registers until the window is taken.
 template <int D>
 __device__ __forceinline__ void q4_win_load(const ExpertBank &P, const ExpTgt &t, int w, int k, float (&dst)[D / 2]) {
     constexpr int V = D / 2;
-    static_assert(5 * V + 7 <= 32, "a window's codes fit one 4-byte code window");
+    static_assert(5 * V + 7 <= 64 && V >= 5, "a window's codes fit one 8-byte code window");
     const int g = (threadIdx.x & 63) >> 4;
     if (!t.live) {
 #pragma unroll
@@ -226,13 +245,14 @@ __device__ __forceinline__ void q4_win_load(const ExpertBank &P, const ExpTgt &t
     const uint32_t fbit = 5u * (uint32_t)(2 * D * w + V * g);
     const uint32_t total = (uint32_t)P.rows * (uint32_t)P.code_stride;
     const uint32_t absb = (uint32_t)t.row[k] * (uint32_t)P.code_stride + (fbit >> 3);
-    const uint32_t at = min(absb, total - 4u);
-    uint32_t win;
-    __builtin_memcpy(&win, t.c + at, 4);
-    dst[0] = __builtin_bit_cast(float, win);
-    dst[1] = __builtin_bit_cast(float, t.pm[t.row[k]]);
-    dst[2] = __builtin_bit_cast(float, 8u * (absb - at) + (fbit & 7u));
-    dst[3] = __builtin_bit_cast(float, (uint32_t)(2 * D * w + V * g));  // first block of the share
+    const uint32_t at = min(absb, total - 8u);
+    uint32_t win[2];
+    __builtin_memcpy(win, t.c + at, 8);
+    dst[0] = __builtin_bit_cast(float, win[0]);
+    dst[1] = __builtin_bit_cast(float, win[1]);
+    dst[2] = __builtin_bit_cast(float, t.pm[t.row[k]]);
+    dst[3] = __builtin_bit_cast(float, 8u * (absb - at) + (fbit & 7u));
+    dst[4] = __builtin_bit_cast(float, (uint32_t)(2 * D * w + V * g));  // first block of the share
 }
 
 // The group scales of a q4tp window (from q4_win_load's bits) and the block
@@ -241,18 +261,19 @@ __device__ __forceinline__ void q4_win_load(const ExpertBank &P, const ExpTgt &t
 // Blocks past the row's last (nb) get scale 0: their codes are not the row's.
 template <int V>
 __device__ __forceinline__ void q4_win_take(const float (&raw)[V], int nb, float (&sw)[V], float (&bw)[V]) {
-    static_assert(V >= 4, "the window registers hold four words of raw material");
-    const uint32_t win = __builtin_bit_cast(uint32_t, raw[0]);
-    const uint32_t pw = __builtin_bit_cast(uint32_t, raw[1]);
-    const uint32_t sh = __builtin_bit_cast(uint32_t, raw[2]);
-    const int fb = (int)__builtin_bit_cast(uint32_t, raw[3]);
+    static_assert(V >= 5, "the window registers hold five words of raw material");
+    const uint64_t win = (uint64_t)__builtin_bit_cast(uint32_t, raw[1]) << 32 | __builtin_bit_cast(uint32_t, raw[0]);
+    const uint32_t pw = __builtin_bit_cast(uint32_t, raw[2]);
+    const uint64_t wv = win >> (__builtin_bit_cast(uint32_t, raw[3]) & 63u);  // the first code at bit 0
+    const int fb = (int)__builtin_bit_cast(uint32_t, raw[4]);
     const float base = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw & 0xFFFFu));
     const float step = (float)__builtin_bit_cast(_Float16, (uint16_t)(pw >> 16));
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const uint32_t code = (uint32_t)(((uint64_t)win >> (sh + 5u * j)) & 31u);
+        // a valid block's code ends inside the window (sh + 5 j + 5 <= 64)
+        const uint32_t code = (uint32_t)(wv >> (5 * j)) & 31u;
         sw[j] = fb + j < nb ? __builtin_amdgcn_exp2f(fmaf((float)code, step, base)) : 0.0f;
-        bw[j] = -8.0f * sw[j];
+        bw[j] = sw[j];  // the staged block sums carry the -(128 + 8)
     }
 }
 
@@ -302,9 +323,8 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
         const __amdgpu_buffer_rsrc_t rq = exp_rsrc(t.q, t.live && p < np ? q_bytes : 0);
 #pragma unroll
         for (int k = 0; k < T; ++k) {
-            if constexpr (Q4) {  // 8 bytes: 16 nibbles of the lane's 16 columns
-                const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, t.vq[k], 32 * p, kExpNT));
-                w[k] = u32x4{v.x, v.y, 0u, 0u};
+            if constexpr (Q4) {  // 16 bytes: block 2 p + g of the lane's row (p even)
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 32 * p, kExpNT);
             } else {
                 w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 64 * p, kExpNT);
             }
@@ -358,7 +378,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     // A operand of lane (i16, g): entry 16 mt + i16 (the zero row past cnt),
     // columns 16 (g & 1) + 8 (g >> 1) .. + 7 of the block, matching the
     // weight columns this lane group holds after the exchange.
-    const int a_col = 2 * (16 * (g & 1) + 8 * (g >> 1));
+    const int a_col = Q4 ? 16 * g : 2 * (16 * (g & 1) + 8 * (g >> 1));
     int a_row[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -368,7 +388,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 
     // Step u of a window: blocks 2u, 2u + 1 sit in lane group 2u / V at
     // entries 2u % V and 2u % V + 1.
-    auto compute = [&](auto uc, int p, int cb0, const u32x4 (&w)[T]) __attribute__((always_inline)) {
+    auto compute = [&](auto uc, int p, int cb0, u32x4 (&w)[T]) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr int gs = 2 * u / V, ev = 2 * u % V;
         const int src = (i16 + 16 * gs) * 4;
@@ -383,10 +403,20 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             b[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev + 1])));
             // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
             // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
-            if constexpr (Q4) {  // the second 8 columns (dword y) move across
-                const auto e = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].y, false, false);
-                b0[k] = nib8_to_bf16(e[0]);
-                b1[k] = nib8_to_bf16(e[1]);
+            if constexpr (Q4) {
+                // The slot of a step pair holds block 4P + g in lane group g
+                // (dword j: its columns 8 j .. 8 j + 7); the even step
+                // transposes it in place (lane-half swaps, then row swaps) to
+                // dword j = block 4P + j, columns 8 g .. 8 g + 7.
+                if constexpr (u % 2 == 0) {
+                    const auto h0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
+                    const auto h1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
+                    const auto r0 = __builtin_amdgcn_permlane16_swap(h0[0], h1[0], false, false);
+                    const auto r1 = __builtin_amdgcn_permlane16_swap(h0[1], h1[1], false, false);
+                    w[k] = u32x4{r0[0], r0[1], r1[0], r1[1]};
+                }
+                b0[k] = nib8_to_bf16_off(u % 2 ? w[k].z : w[k].x);
+                b1[k] = nib8_to_bf16_off(u % 2 ? w[k].w : w[k].y);
             } else {
                 const auto e0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
                 const auto e1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
@@ -438,7 +468,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     for (int c0 = 0; c0 < npp; c0 += kp) {
         if (c0 > 0 || chunked || fresh) {
             __syncthreads();
-            exp_stage<MT>(P, list, cnt, 2 * c0, kp, lds, Q82 ? P.cf + (long long)e * P.cf_stride : nullptr);
+            exp_stage<MT, Q4>(P, list, cnt, 2 * c0, kp, lds, Q82 ? P.cf + (long long)e * P.cf_stride : nullptr);
             __syncthreads();
         }
         const int c1 = min(npp, c0 + kp);
@@ -463,11 +493,11 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             static_for<D>([&](auto uc) __attribute__((always_inline)) {
                 constexpr int u = decltype(uc)::value;
                 const int p = p0 + u;
-                if (p < np) compute(uc, p, 2 * c0, wq[u]);
+                if (p < np) compute(uc, p, 2 * c0, wq[Q4 ? u & ~1 : u]);
                 // after the last step of a burst, its slots are refilled together
                 if constexpr (u % kExpBurst == kExpBurst - 1) {
 #pragma unroll
-                    for (int j = u + 1 - kExpBurst; j <= u; ++j) load(tl, pl + j, wq[j]);
+                    for (int j = u + 1 - kExpBurst; j <= u; j += Q4 ? 2 : 1) load(tl, pl + j, wq[j]);
                 }
                 __builtin_amdgcn_sched_barrier(kExpSched);
             });
@@ -497,10 +527,10 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 // once for all of that expert's items in its share, and its weight stream
 // runs from one item into the next without draining.  An expert with more
 // than kExpGroup entries takes one pass per group of kExpGroup over each item.
-// Ring depth of a format: q4tp's scale window reads the codes of its blocks
-// from one 4-byte window, which holds those of 8 steps at most.
+// Ring depth of a format (the same for all: q4tp's scale window reads the
+// codes of its 2 D blocks from one 8-byte window).
 template <int FMT>
-constexpr int exp_depth() { return FMT == kExpQ4 ? 8 : kExpDepth; }
+constexpr int exp_depth() { return kExpDepth; }
 
 template <int AL, int FMT>
 __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
@@ -553,7 +583,7 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
 #pragma unroll
         for (int k = 0; k < T; ++k) {
             const int r = min(rb * kExpRows + (wave * T + k) * 16 + i16, P.rows - 1);
-            t.vq[k] = Q4 ? r * (P.cols >> 1) + 8 * g : r * P.cols + 16 * g;
+            t.vq[k] = Q4 ? r * (P.cols >> 1) + 16 * g : r * P.cols + 16 * g;
             t.vs[k] = (r * nb + V * g) * 4;
             t.row[k] = r;
         }
@@ -592,10 +622,10 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
 #pragma unroll
             for (int k = 0; k < T; ++k) {
                 if constexpr (Q4) {
-                    const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * (P.cols >> 1) : 0);
-                    const u32x2 v =
-                        __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, t0.vq[k], 32 * u, kExpNT));
-                    wq[u][k] = u32x4{v.x, v.y, 0u, 0u};
+                    if constexpr (u % 2 == 0) {
+                        const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * (P.cols >> 1) : 0);
+                        wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 32 * u, kExpNT);
+                    }
                 } else {
                     const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
                     wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 64 * u, kExpNT);
@@ -652,7 +682,7 @@ int launch_expert_bank(const ExpertBank &P, hipStream_t s) {
     if ((long long)P.rows * P.cols >= (1ll << 31)) return PG_EUNSUPPORTED;  // 32-bit buffer offsets
     const int nb = P.cols / 32;
     if (P.nib) {  // q4tp: code windows instead of scale loads
-        if (!P.params || !P.codes || (long long)P.rows * P.code_stride < 4) return PG_EINVAL;
+        if (!P.params || !P.codes || (long long)P.rows * P.code_stride < 8) return PG_EINVAL;
         return launch_bank<1, kExpQ4>(P, s);
     }
     if (P.rs) {  // q8_2f: the (empty) window loads take the widest form the block count allows
@@ -735,6 +765,6 @@ extern "C" int expert_bank_q4tp(const uint8_t *nib, const uint32_t *params, cons
     P.params = params;
     P.codes = codes;
     P.code_stride = (5 * (cols / 32) + 7) / 8;
-    if ((long long)rows * P.code_stride < 4) return PG_EUNSUPPORTED;  // 4-byte code windows
+    if ((long long)rows * P.code_stride < 8) return PG_EUNSUPPORTED;  // 8-byte code windows
     return launch_expert_bank(P, as_stream(stream));
 }
