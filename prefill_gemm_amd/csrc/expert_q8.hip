@@ -103,6 +103,11 @@ __device__ __forceinline__ bf16x8 nib8_to_bf16_off(uint32_t w) {
     return r;
 }
 
+// A buffer resource over `bytes` bytes.  Every load below puts its whole
+// offset in the per-lane (vector) offset, which the hardware checks against
+// the resource's size (bytes past it read as zero); the scalar offset, which
+// it does not check, stays 0.  So a row's last step or window, which may run
+// past the row, never reads past the tensor.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t exp_rsrc(const void *p, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
@@ -324,9 +329,9 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 #pragma unroll
         for (int k = 0; k < T; ++k) {
             if constexpr (Q4) {  // 16 bytes: block 2 p + g of the lane's row (p even)
-                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 32 * p, kExpNT);
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 32 * p, 0, kExpNT);
             } else {
-                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k], 64 * p, kExpNT);
+                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 64 * p, 0, kExpNT);
             }
         }
     };
@@ -348,23 +353,23 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 #pragma unroll
             for (int j = 0; j < V; j += LW) {
                 if (LW == 4) {
-                    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, t.vs[k], off + 4 * j, 0));
-                    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbs, t.vs[k], off + 4 * j, 0));
+                    const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, t.vs[k] + off + 4 * j, 0, 0));
+                    const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rbs, t.vs[k] + off + 4 * j, 0, 0));
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         swn[k][j + i] = a[i];
                         bwn[k][j + i] = b[i];
                     }
                 } else if (LW == 2) {
-                    const f32x2 a = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, t.vs[k], off + 4 * j, 0));
-                    const f32x2 b = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rbs, t.vs[k], off + 4 * j, 0));
+                    const f32x2 a = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, t.vs[k] + off + 4 * j, 0, 0));
+                    const f32x2 b = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rbs, t.vs[k] + off + 4 * j, 0, 0));
                     swn[k][j] = a[0];
                     swn[k][j + 1] = a[1];
                     bwn[k][j] = b[0];
                     bwn[k][j + 1] = b[1];
                 } else {
-                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t.vs[k], off + 4 * j, 0));
-                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t.vs[k], off + 4 * j, 0));
+                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t.vs[k] + off + 4 * j, 0, 0));
+                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t.vs[k] + off + 4 * j, 0, 0));
                 }
             }
     };
@@ -611,8 +616,8 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
             for (int k = 0; k < T; ++k)
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t0.vs[k], 4 * j, 0));
-                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t0.vs[k], 4 * j, 0));
+                    swn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, t0.vs[k] + 4 * j, 0, 0));
+                    bwn[k][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rbs, t0.vs[k] + 4 * j, 0, 0));
                 }
         }
         __builtin_amdgcn_sched_barrier(kExpSched);
@@ -624,11 +629,11 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
                 if constexpr (Q4) {
                     if constexpr (u % 2 == 0) {
                         const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * (P.cols >> 1) : 0);
-                        wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 32 * u, kExpNT);
+                        wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k] + 32 * u, 0, kExpNT);
                     }
                 } else {
                     const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
-                    wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k], 64 * u, kExpNT);
+                    wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k] + 64 * u, 0, kExpNT);
                 }
             }
             __builtin_amdgcn_sched_barrier(kExpSched);
