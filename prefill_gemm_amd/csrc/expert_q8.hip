@@ -46,10 +46,13 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kExpSched = 0;
 constexpr int kExpThreads = 512;
 constexpr int kExpWaves = kExpThreads / kWave;
+// Threads of a workgroup by format: q4tp's registers leave room for three
+// waves a SIMD.
+template <int FMT>
+constexpr int exp_threads() { return FMT == 2 ? 768 : kExpThreads; }  // 2: kExpQ4
 constexpr int kExpDepth = 16;
 constexpr int kExpBurst = 8;   // ring slots refilled together
 constexpr int kExpTiles = 1;                    // 16-row weight tiles per wave
-constexpr int kExpRows = kExpWaves * 16 * kExpTiles;   // weight rows of one work item
 constexpr int kExpGroup = 16;                // entries per pass over an item
 constexpr int kExpLds = (148 * 1024);
 constexpr int kExpMaxCnt = 64;
@@ -141,7 +144,7 @@ constexpr int kStageBatch = 6;
 
 // cf: the expert's binary16 column field (q8_2f), multiplied into the staged
 // activations; NULL for the block format.
-template <int MT, bool NIB>
+template <int MT, bool NIB, int NTH>
 __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *list, int cnt, int cb0,
                                           int kp, char *lds, const uint16_t *cf) {
     const int nb = P.cols >> 5;
@@ -150,12 +153,12 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
     char *lo_base = lds + (cnt + 1) * pitch;
     float *xsum = reinterpret_cast<float *>(lds + 2 * (cnt + 1) * pitch);
     const int total = (cnt + 1) * 4 * kc;
-    for (int base = 0; base < total; base += kStageBatch * kExpThreads) {
+    for (int base = 0; base < total; base += kStageBatch * NTH) {
         float4 xa[kStageBatch][2];
         u32x4 ca[kStageBatch];
 #pragma unroll
         for (int k = 0; k < kStageBatch; ++k) {
-            const int it = base + k * kExpThreads + threadIdx.x;
+            const int it = base + k * NTH + threadIdx.x;
             const int r = it / (4 * kc);
             const int qb = it - r * 4 * kc;
             const int blk = cb0 + (qb >> 2);
@@ -173,7 +176,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
         for (int k = 0; k < kStageBatch; ++k) {
             // Every requested item is consumed (stores only for items in range),
             // so no load of the batch is left pending past the staging.
-            const int it = base + k * kExpThreads + threadIdx.x;
+            const int it = base + k * NTH + threadIdx.x;
             const bool in = it < total;
             const int r = it / (4 * kc);
             const int qb = it - r * 4 * kc;
@@ -214,7 +217,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
         }
     }
     // Block sums of the padding rows past the zero row.
-    for (int it = threadIdx.x; it < kc * 16 * MT; it += kExpThreads)
+    for (int it = threadIdx.x; it < kc * 16 * MT; it += NTH)
         if (it % (16 * MT) > cnt) xsum[it] = 0.0f;
 }
 
@@ -282,12 +285,12 @@ __device__ __forceinline__ void q4_win_take(const float (&raw)[V], int nb, float
     }
 }
 
-// One pass over a work item (expert e, weight rows rb * kExpRows ..) for its
-// entries m0 .. m0 + cnt - 1 (at most kExpGroup): its column chunks (staged
-// when the expert or the entry group changes, or every time when the entries
-// take more than one chunk), its steps, and its outputs.  The weight ring and
-// the scale windows come in holding this pass's first steps and leave holding
-// those of the pass after it (target tn).
+// One pass over a work item (expert e, weight rows rb * R .., R = 16 rows a
+// wave) for its entries m0 .. m0 + cnt - 1 (at most kExpGroup): its column
+// chunks (staged when the expert or the entry group changes, or every time
+// when the entries take more than one chunk), its steps, and its outputs.
+// The weight ring and the scale windows come in holding this pass's first
+// steps and leave holding those of the pass after it (target tn).
 template <int MT, int D, int AL, int FMT>
 __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int cnt, int rb, bool fresh,
                                          const ExpTgt &tc, const ExpTgt &tn, u32x4 (&wq)[D][kExpTiles],
@@ -473,7 +476,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     for (int c0 = 0; c0 < npp; c0 += kp) {
         if (c0 > 0 || chunked || fresh) {
             __syncthreads();
-            exp_stage<MT, Q4>(P, list, cnt, 2 * c0, kp, lds, Q82 ? P.cf + (long long)e * P.cf_stride : nullptr);
+            exp_stage<MT, Q4, exp_threads<FMT>()>(P, list, cnt, 2 * c0, kp, lds, Q82 ? P.cf + (long long)e * P.cf_stride : nullptr);
             __syncthreads();
         }
         const int c1 = min(npp, c0 + kp);
@@ -510,10 +513,10 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     }
 
     // Output element v of tile (k, mt): entry 16 mt + 4 g + v, weight row
-    // rb * kExpRows + (wave T + k) * 16 + i16.
+    // rb * R + (wave T + k) * 16 + i16.
 #pragma unroll
     for (int k = 0; k < T; ++k) {
-        const int r = rb * kExpRows + (wave * T + k) * 16 + i16;
+        const int r = rb * (exp_threads<FMT>() / 4) + (wave * T + k) * 16 + i16;
         if (r >= P.rows) continue;
         // q8_2f: the row scale multiplies the finished sum.
         const float rsc = Q82 ? (float)__builtin_bit_cast(_Float16, P.rs[(long long)e * P.rs_stride + r]) : 1.0f;
@@ -526,19 +529,20 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     }
 }
 
-// Persistent workgroups, one per compute unit.  The work items are (active
-// expert, block of kExpRows weight rows), experts in ascending order; each
-// workgroup takes one contiguous share, so that it stages an expert's entries
-// once for all of that expert's items in its share, and its weight stream
-// runs from one item into the next without draining.  An expert with more
-// than kExpGroup entries takes one pass per group of kExpGroup over each item.
+// Persistent workgroups, one per compute unit (8 waves; 12 for q4tp).  The
+// work items are (active expert, block of 16 rows a wave), experts in
+// ascending order; each workgroup takes one contiguous share, so that it
+// stages an expert's entries once for all of that expert's items in its
+// share, and its weight stream runs from one item into the next without
+// draining.  An expert with more than kExpGroup entries takes one pass per
+// group of kExpGroup over each item.
 // Ring depth of a format (the same for all: q4tp's scale window reads the
 // codes of its 2 D blocks from one 8-byte window).
 template <int FMT>
 constexpr int exp_depth() { return kExpDepth; }
 
 template <int AL, int FMT>
-__global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank P) {
+__global__ __launch_bounds__(exp_threads<FMT>(), 1) void expert_bank_kernel(ExpertBank P) {
     constexpr bool Q82 = FMT == kExpQ82, Q4 = FMT == kExpQ4;
     extern __shared__ u32x4 exp_lds[];
     __shared__ int act[kExpMaxExperts];
@@ -563,7 +567,8 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
         if (lane == 0) nact_s = base;
     }
     __syncthreads();
-    const int RB = (P.rows + kExpRows - 1) / kExpRows;
+    constexpr int kRows = exp_threads<FMT>() / 4 * kExpTiles;  // weight rows of one work item
+    const int RB = (P.rows + kRows - 1) / kRows;
     const long long N = (long long)nact_s * RB;
     const int i0 = (int)(N * blockIdx.x / gridDim.x);
     const int i1 = (int)(N * (blockIdx.x + 1) / gridDim.x);
@@ -587,7 +592,7 @@ __global__ __launch_bounds__(kExpThreads, 1) void expert_bank_kernel(ExpertBank 
         t.b = P.bias + (long long)e * P.s_stride;
 #pragma unroll
         for (int k = 0; k < T; ++k) {
-            const int r = min(rb * kExpRows + (wave * T + k) * 16 + i16, P.rows - 1);
+            const int r = min(rb * kRows + (wave * T + k) * 16 + i16, P.rows - 1);
             t.vq[k] = Q4 ? r * (P.cols >> 1) + 16 * g : r * P.cols + 16 * g;
             t.vs[k] = (r * nb + V * g) * 4;
             t.row[k] = r;
@@ -677,7 +682,7 @@ static int launch_bank(const ExpertBank &P, hipStream_t s) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(expert_bank_kernel<AL, FMT>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kExpLds);
     if (attr != hipSuccess) return PG_ELAUNCH;
-    hipLaunchKernelGGL((expert_bank_kernel<AL, FMT>), dim3(exp_grid()), dim3(kExpThreads), kExpLds, s, P);
+    hipLaunchKernelGGL((expert_bank_kernel<AL, FMT>), dim3(exp_grid()), dim3(exp_threads<FMT>()), kExpLds, s, P);
     return launch_status();
 }
 
