@@ -445,9 +445,10 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             const f32x4 xs1 = *reinterpret_cast<const f32x4 *>(xs + 16 * MT);
 #pragma unroll
             for (int k = 0; k < T; ++k) {
-                f32x4 d0 = mfma16(ah0, b0[k], z);
+                // q4tp: the chains start from the staged block sums (times -136)
+                f32x4 d0 = mfma16(ah0, b0[k], Q4 ? xs0 : z);
                 d0 = mfma16(al0, b0[k], d0);
-                f32x4 d1 = mfma16(ah1, b1[k], z);
+                f32x4 d1 = mfma16(ah1, b1[k], Q4 ? xs1 : z);
                 d1 = mfma16(al1, b1[k], d1);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -457,6 +458,9 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                         (void)xs1;
                         x += d0[v];
                         x += d1[v];
+                    } else if constexpr (Q4) {
+                        x = fmaf(s[k].x, d0[v], x);
+                        x = fmaf(s[k].y, d1[v], x);
                     } else {
                         x = fmaf(s[k].x, d0[v], x);
                         x = fmaf(s[k].y, d1[v], x);
