@@ -61,8 +61,8 @@ template <int HD>
 struct AttnCfg {
     static constexpr int kKStride = HD + 4;        // floats per staged K row (padding spreads banks)
     static constexpr int kKFloats = kAttnKT * kKStride;
-    static constexpr int kVStride = kAttnKT + 4;   // V staged transposed: [dim][key]
-    static constexpr int kVFloats = HD * kVStride;
+    static constexpr int kVStride = HD + 4;        // V staged as K: [key][dim]
+    static constexpr int kVFloats = kAttnKT * kVStride;
     static constexpr int kPStride = kAttnKT + 4;   // p of a wave: [16 queries][key]
     static constexpr int kPFloats = kAttnWaves * kAttnQW * kPStride;
     static_assert(kPFloats <= kKFloats, "p reuses the K tile's space");
@@ -77,7 +77,9 @@ struct AttnCfg {
 // 16c + 4k + u (k = lane group l / 16), so a lane reads its q row and its key's
 // K row as float4 at dims 16c + 4k; q stays in registers.  p . V: step 4c + u
 // contracts keys 16c + 4k + u, p read back from LDS as float4 of its row and V
-// from its transposed copy as float4 of its dim.  The softmax runs in the D
+// (staged as K is, a row per key) as four single values of its dim, one per
+// key: a transposed copy would need 4-byte writes that meet 16-way LDS bank
+// conflicts, the single reads meet none.  The softmax runs in the D
 // layout: a row's 16 keys of a 16-key block sit in the 16 lanes of one DPP row.
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
@@ -148,16 +150,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
 
     for (int t0 = j0; t0 < j1; t0 += kAttnKT) {
         __syncthreads();  // the previous tile's K and V are no longer read
-        // Stage keys t0 .. t0 + 63: K rows as they are, V transposed.
+        // Stage keys t0 .. t0 + 63: K and V rows as they are.
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int t = threadIdx.x + r * kAttnThreads;
             const int kk = t / kRow4, d4 = t % kRow4;
             *reinterpret_cast<float4 *>(sk + kk * C::kKStride + 4 * d4) = ka[r];
-            sv[(4 * d4 + 0) * C::kVStride + kk] = va[r].x;
-            sv[(4 * d4 + 1) * C::kVStride + kk] = va[r].y;
-            sv[(4 * d4 + 2) * C::kVStride + kk] = va[r].z;
-            sv[(4 * d4 + 3) * C::kVStride + kk] = va[r].w;
+            *reinterpret_cast<float4 *>(sv + kk * C::kVStride + 4 * d4) = va[r];
         }
         __syncthreads();
         if (t0 + kAttnKT < j1) fetch(t0 + kAttnKT);
@@ -208,7 +207,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
             const f32x4 pf = *reinterpret_cast<const f32x4 *>(pw + r16 * C::kPStride + 16 * c2 + 4 * kg);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const f32x4 vf = *reinterpret_cast<const f32x4 *>(sv + (16 * c + r16) * C::kVStride + 16 * c2 + 4 * kg);
+                const float *vcol = sv + (16 * c2 + 4 * kg) * C::kVStride + 16 * c + r16;
+                const f32x4 vf{vcol[0], vcol[C::kVStride], vcol[2 * C::kVStride], vcol[3 * C::kVStride]};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o[c] = mfma_f32_16x16x4(pf[u], vf[u], o[c]);
             }
