@@ -60,15 +60,16 @@ constexpr int kExpMaxExperts = 1024;
 
 // LDS bytes of a chunk of `kp` block pairs for cnt entries in MT tiles of 16:
 // hi and lo arrays of cnt + 1 rows (the last all zero) of 64 bytes a block
-// plus 16 bytes of padding a row, and the block sums [block][16 MT] f32.
+// plus 48 bytes of padding a row (of the 16-byte multiples tried, the one
+// the q4tp bank runs fastest with), and the block sums [block][16 MT] f32.
 __host__ __device__ constexpr int exp_chunk_bytes(int kp, int cnt, int mt) {
-    return 2 * (cnt + 1) * (128 * kp + 16) + 2 * kp * 16 * mt * 4;
+    return 2 * (cnt + 1) * (128 * kp + 48) + 2 * kp * 16 * mt * 4;
 }
 
 // Block pairs per chunk: the most that fit, a multiple of the ring depth D.
 __device__ __forceinline__ int exp_chunk_pairs(int cnt, int mt, int d, int np) {
     const int per = 2 * (cnt + 1) * 128 + 2 * 16 * mt * 4;
-    int kp = (kExpLds - 32 * (cnt + 1)) / per;
+    int kp = (kExpLds - 2 * 48 * (cnt + 1)) / per;
     kp -= kp % d;
     const int need = (np + d - 1) / d * d;
     return kp < need ? kp : need;
@@ -149,7 +150,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
                                           int kp, char *lds, const uint16_t *cf) {
     const int nb = P.cols >> 5;
     const int kc = 2 * kp;
-    const int pitch = 64 * kc + 16;
+    const int pitch = 64 * kc + 48;
     char *lo_base = lds + (cnt + 1) * pitch;
     float *xsum = reinterpret_cast<float *>(lds + 2 * (cnt + 1) * pitch);
     const int total = (cnt + 1) * 4 * kc;
@@ -312,7 +313,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     const int32_t *list = P.lists + (long long)e * P.cap + m0;
     const int kp = exp_chunk_pairs(cnt, MT, D, np);
     const bool chunked = kp < npp;
-    const int pitch = 128 * kp + 16;
+    const int pitch = 128 * kp + 48;
     const int lo_off = (cnt + 1) * pitch;
     const int xs_off = 2 * (cnt + 1) * pitch;
 
