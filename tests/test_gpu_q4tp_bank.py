@@ -139,7 +139,7 @@ def test_expert_bank_q4tp_errors(pg):
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
 
-    def call(cols=cols, cap=cap, np_=None, pp=None, xp=None, act=0, ldx=cols):
+    def call(cols=cols, cap=cap, np_=None, pp=None, xp=None, act=0, ldx=cols, rows=rows):
         return L.expert_bank_q4tp(np_ or P(nib), pp or P(params), P(codes), E, rows, cols, xp or P(x), ldx, 1,
                                   P(counts), P(lists), cap, P(out), rows, act, s)
 
@@ -147,6 +147,8 @@ def test_expert_bank_q4tp_errors(pg):
     torch.cuda.synchronize()
     assert call(cols=240) == pg.PG_EUNSUPPORTED
     assert call(cap=65) == pg.PG_EUNSUPPORTED
+    # a code buffer under 8 bytes (one row of one group: one code byte) cannot hold a code window
+    assert call(rows=1, cols=32, ldx=32) == pg.PG_EUNSUPPORTED
     assert call(act=2) == pg.PG_EINVAL
     assert call(np_=P(nib, 8)) == pg.PG_EINVAL
     assert call(pp=P(params, 2)) == pg.PG_EINVAL
