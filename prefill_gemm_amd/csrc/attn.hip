@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
 // One wave per (position, query head): the splits rescaled to their common
 // maximum and added in split order.  Lane s fetches split s's maximum and sum
 // (splits <= 64), so the maximum and the denominator are one wave reduction
-// each; the partial rows are requested eight splits at a time.
+// each; the partial rows are requested sixteen splits at a time, the first
+// sixteen together with the maxima and sums (one round trip for up to 16 splits).
 template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *__restrict__ part, int n, int nh,
                                                                   int splits, float *__restrict__ o) {
@@ -249,9 +250,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *_
     const int i = blockIdx.x * kAttnWaves + (threadIdx.x >> 6);  // b * nh + h
     if (i >= n * nh) return;
     constexpr int DL = HD / 64;
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const long long stride = (long long)n * nh * (HD + 2);
     const float *p0 = part + (long long)i * (HD + 2);
+    float a[kBatch][DL];
+    auto fetch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int sk = min(s0 + k, splits - 1);
+#pragma unroll
+            for (int e = 0; e < DL; ++e) a[k][e] = p0[sk * stride + lane * DL + e];
+        }
+    };
+    fetch(0);  // requested together with the maxima and sums below: one round trip
     const bool mine = lane < splits;
     const float ms = mine ? p0[lane * stride + HD] : kAttnNoMax;
     const float ls = mine ? p0[lane * stride + HD + 1] : 0.0f;
@@ -261,13 +272,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *_
 #pragma unroll
     for (int e = 0; e < DL; ++e) num[e] = 0.0f;
     for (int s0 = 0; s0 < splits; s0 += kBatch) {
-        float a[kBatch][DL];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int sk = min(s0 + k, splits - 1);
-#pragma unroll
-            for (int e = 0; e < DL; ++e) a[k][e] = p0[sk * stride + lane * DL + e];
-        }
+        if (s0 > 0) fetch(s0);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             if (s0 + k >= splits) break;
