@@ -11,9 +11,11 @@
 // per expert, so this is a matrix product with a very short side.  It runs on
 // the 16 x 16 x 32 bf16 matrix cores (v_mfma_f32_16x16x32_bf16), which pad the
 // entries only to 16:
-//  - B operand = weights, exact bf16 integers; a lane streams 16 bytes of one
-//    weight row per step (a step = 16 rows x 2 blocks, 1 KB a wave);
-//  - lanes l and l + 32 trade the upper 8 bytes of their load
+//  - B operand = weights, exact bf16 integers; a step is 16 rows x 2 blocks
+//    (1 KB a wave), and a pair of steps comes as two loads of 8 rows x 128
+//    bytes (whole lines, non-temporal), from which a step's pieces are
+//    gathered to 16 bytes of one row a lane (a half-row rotation, a select);
+//  - lanes l and l + 32 trade the upper 8 bytes of those 16
 //    (v_permlane32_swap), so that each matrix-core product sees 32 columns of
 //    one block and the block scale can multiply its result;
 //  - q4tp: a lane's 16 bytes cover one block of a pair of steps, and the four
@@ -79,7 +81,8 @@ static_assert(exp_chunk_bytes(kExpDepth, kExpGroup, kExpGroup / 16) <= kExpLds, 
 static_assert(kExpLds + kExpMaxExperts * 4 + 16 <= 160 * 1024, "LDS of a compute unit");
 static_assert(kExpDepth % kExpBurst == 0, "the ring refills in whole bursts");
 
-constexpr int kExpNT = 0;  // weight load cache policy (2: non-temporal)
+constexpr int kExpNT = 0;      // q4tp weight loads: normal cache policy
+constexpr int kExpNTPair = 2;  // q8 / q8_2f pair loads: non-temporal (each byte is used once)
 
 // Bank formats (template argument FMT): the block format, q8_2f, and q4tp,
 // whose nibble n enters the matrix cores as the exact bf16 128 + n while the
@@ -227,7 +230,7 @@ __device__ __forceinline__ void exp_stage(const ExpertBank &P, const int32_t *li
 struct ExpTgt {
     const int8_t *q;
     const float *s, *b;
-    int vq[kExpTiles], vs[kExpTiles];
+    int vq[kExpTiles], vb[kExpTiles], vs[kExpTiles];  // vb: the second slot of a pair (8-bit formats)
     bool live;
     // q4tp: the expert's group codes and parameter words, and this lane's row
     const uint8_t *c;
@@ -328,14 +331,20 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             orow[mt][v] = m < cnt ? list[m] : -1;
         }
 
-    auto load = [&](const ExpTgt &t, int p, u32x4 (&w)[T]) __attribute__((always_inline)) {
+    // The ring slots of a step pair (p even).  q4tp: one slot, 16 bytes a lane
+    // (block 2 p + g of the lane's row).  The 8-bit formats: two slots, each one
+    // instruction over 8 rows x 128 bytes (both steps of rows 0-7, then of rows
+    // 8-15; lane (g, i) reads piece g of step i / 8 of row i % 8), the pattern
+    // HBM serves best; compute gathers a step's pieces from the two.
+    auto load = [&](const ExpTgt &t, int p, u32x4 (&wa)[T], u32x4 (&wb)[T]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rq = exp_rsrc(t.q, t.live && p < np ? q_bytes : 0);
 #pragma unroll
         for (int k = 0; k < T; ++k) {
-            if constexpr (Q4) {  // 16 bytes: block 2 p + g of the lane's row (p even)
-                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 32 * p, 0, kExpNT);
+            if constexpr (Q4) {
+                wa[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 32 * p, 0, kExpNT);
             } else {
-                w[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 64 * p, 0, kExpNT);
+                wa[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vq[k] + 64 * p, 0, kExpNTPair);
+                wb[k] = __builtin_amdgcn_raw_buffer_load_b128(rq, t.vb[k] + 64 * p, 0, kExpNTPair);
             }
         }
     };
@@ -397,7 +406,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 
     // Step u of a window: blocks 2u, 2u + 1 sit in lane group 2u / V at
     // entries 2u % V and 2u % V + 1.
-    auto compute = [&](auto uc, int p, int cb0, u32x4 (&w)[T]) __attribute__((always_inline)) {
+    auto compute = [&](auto uc, int p, int cb0, u32x4 (&w)[T], const u32x4 (&w2)[T]) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr int gs = 2 * u / V, ev = 2 * u % V;
         const int src = (i16 + 16 * gs) * 4;
@@ -427,8 +436,19 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                 b0[k] = nib8_to_bf16_off(u % 2 ? w[k].z : w[k].x);
                 b1[k] = nib8_to_bf16_off(u % 2 ? w[k].w : w[k].y);
             } else {
-                const auto e0 = __builtin_amdgcn_permlane32_swap(w[k].x, w[k].z, false, false);
-                const auto e1 = __builtin_amdgcn_permlane32_swap(w[k].y, w[k].w, false, false);
+                // The pair's slots: w holds rows 0-7, w2 rows 8-15, lane (g, i)
+                // carrying piece g of row i % 8 (+ 8) for step i / 8.  Step 0 keeps
+                // w's first half-rows and w2's moved up; step 1 w's second
+                // half-rows moved down and w2's.
+                constexpr bool S1 = u & 1;
+                auto pick = [&](uint32_t a, uint32_t b) __attribute__((always_inline)) {
+                    const uint32_t lo = S1 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x128, 0xF, 0xF, false) : a;
+                    const uint32_t hi = S1 ? b : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x128, 0xF, 0xF, false);
+                    return i16 < 8 ? lo : hi;
+                };
+                const u32x4 q{pick(w[k].x, w2[k].x), pick(w[k].y, w2[k].y), pick(w[k].z, w2[k].z), pick(w[k].w, w2[k].w)};
+                const auto e0 = __builtin_amdgcn_permlane32_swap(q.x, q.z, false, false);
+                const auto e1 = __builtin_amdgcn_permlane32_swap(q.y, q.w, false, false);
                 b0[k] = q8_to_bf16(e0[0], e1[0]);
                 b1[k] = q8_to_bf16(e0[1], e1[1]);
             }
@@ -506,11 +526,11 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             static_for<D>([&](auto uc) __attribute__((always_inline)) {
                 constexpr int u = decltype(uc)::value;
                 const int p = p0 + u;
-                if (p < np) compute(uc, p, 2 * c0, wq[Q4 ? u & ~1 : u]);
+                if (p < np) compute(uc, p, 2 * c0, wq[u & ~1], wq[(u & ~1) + (Q4 ? 0 : 1)]);
                 // after the last step of a burst, its slots are refilled together
                 if constexpr (u % kExpBurst == kExpBurst - 1) {
 #pragma unroll
-                    for (int j = u + 1 - kExpBurst; j <= u; j += Q4 ? 2 : 1) load(tl, pl + j, wq[j]);
+                    for (int j = u + 1 - kExpBurst; j <= u; j += 2) load(tl, pl + j, wq[j], wq[j + 1]);
                 }
                 __builtin_amdgcn_sched_barrier(kExpSched);
             });
@@ -598,7 +618,9 @@ __global__ __launch_bounds__(exp_threads<FMT>(), 1) void expert_bank_kernel(Expe
 #pragma unroll
         for (int k = 0; k < T; ++k) {
             const int r = min(rb * kRows + (wave * T + k) * 16 + i16, P.rows - 1);
-            t.vq[k] = Q4 ? r * (P.cols >> 1) + 16 * g : r * P.cols + 16 * g;
+            const int r8 = rb * kRows + (wave * T + k) * 16 + (i16 & 7);
+            t.vq[k] = Q4 ? r * (P.cols >> 1) + 16 * g : min(r8, P.rows - 1) * P.cols + 64 * (i16 >> 3) + 16 * g;
+            t.vb[k] = Q4 ? 0 : min(r8 + 8, P.rows - 1) * P.cols + 64 * (i16 >> 3) + 16 * g;
             t.vs[k] = (r * nb + V * g) * 4;
             t.row[k] = r;
         }
@@ -641,9 +663,10 @@ __global__ __launch_bounds__(exp_threads<FMT>(), 1) void expert_bank_kernel(Expe
                         const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * (P.cols >> 1) : 0);
                         wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k] + 32 * u, 0, kExpNT);
                     }
-                } else {
+                } else if constexpr (u % 2 == 0) {
                     const __amdgpu_buffer_rsrc_t r = exp_rsrc(t0.q, u < np ? P.rows * P.cols : 0);
-                    wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k] + 64 * u, 0, kExpNT);
+                    wq[u][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vq[k] + 64 * u, 0, kExpNTPair);
+                    wq[u + 1][k] = __builtin_amdgcn_raw_buffer_load_b128(r, t0.vb[k] + 64 * u, 0, kExpNTPair);
                 }
             }
             __builtin_amdgcn_sched_barrier(kExpSched);
