@@ -334,8 +334,9 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     // The ring slots of a step pair (p even).  q4tp: one slot, 16 bytes a lane
     // (block 2 p + g of the lane's row).  The 8-bit formats: two slots, each one
     // instruction over 8 rows x 128 bytes (both steps of rows 0-7, then of rows
-    // 8-15; lane (g, i) reads piece g of step i / 8 of row i % 8), the pattern
-    // HBM serves best; compute gathers a step's pieces from the two.
+    // 8-15), the pattern HBM serves best: lane (g, i) reads piece g of row i % 8
+    // for step i / 8 in the first, of row 8 + i % 8 for step 1 - i / 8 in the
+    // second, so that a step's operand is a lane-wise select of the two.
     auto load = [&](const ExpTgt &t, int p, u32x4 (&wa)[T], u32x4 (&wb)[T]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rq = exp_rsrc(t.q, t.live && p < np ? q_bytes : 0);
 #pragma unroll
@@ -387,11 +388,13 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             }
     };
 
-    f32x4 acc[T][MT];
+    // acc: the even steps; acc1: the odd steps of the 8-bit formats, whose
+    // column n is row n ^ 8.
+    f32x4 acc[T][MT], acc1[T][MT];
 #pragma unroll
     for (int k = 0; k < T; ++k)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[k][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mt = 0; mt < MT; ++mt) acc[k][mt] = acc1[k][mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // A operand of lane (i16, g): entry 16 mt + i16 (the zero row past cnt),
     // columns 16 (g & 1) + 8 (g >> 1) .. + 7 of the block, matching the
@@ -409,7 +412,8 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
     auto compute = [&](auto uc, int p, int cb0, u32x4 (&w)[T], const u32x4 (&w2)[T]) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr int gs = 2 * u / V, ev = 2 * u % V;
-        const int src = (i16 + 16 * gs) * 4;
+        constexpr bool ODD = !Q4 && (u & 1);  // this step's column n holds row n ^ 8
+        const int src = ((ODD ? i16 ^ 8 : i16) + 16 * gs) * 4;
         const int bl = 2 * p - cb0;
         f32x2 s[T], b[T];
         bf16x8 b0[T], b1[T];
@@ -436,15 +440,13 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                 b0[k] = nib8_to_bf16_off(u % 2 ? w[k].z : w[k].x);
                 b1[k] = nib8_to_bf16_off(u % 2 ? w[k].w : w[k].y);
             } else {
-                // The pair's slots: w holds rows 0-7, w2 rows 8-15, lane (g, i)
-                // carrying piece g of row i % 8 (+ 8) for step i / 8.  Step 0 keeps
-                // w's first half-rows and w2's moved up; step 1 w's second
-                // half-rows moved down and w2's.
-                constexpr bool S1 = u & 1;
+                // The pair's slots: w holds rows 0-7 (lane (g, i): piece g of row
+                // i % 8 for step i / 8), w2 rows 8-15 the other way round (step
+                // 1 - i / 8).  Step 0 takes w's first half-rows and w2's second
+                // (column n = row n); step 1 w2's first and w's second (column
+                // n = row n ^ 8).
                 auto pick = [&](uint32_t a, uint32_t b) __attribute__((always_inline)) {
-                    const uint32_t lo = S1 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x128, 0xF, 0xF, false) : a;
-                    const uint32_t hi = S1 ? b : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0x128, 0xF, 0xF, false);
-                    return i16 < 8 ? lo : hi;
+                    return (i16 < 8) != ODD ? a : b;
                 };
                 const u32x4 q{pick(w[k].x, w2[k].x), pick(w[k].y, w2[k].y), pick(w[k].z, w2[k].z), pick(w[k].w, w2[k].w)};
                 const auto e0 = __builtin_amdgcn_permlane32_swap(q.x, q.z, false, false);
@@ -473,7 +475,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                 d1 = mfma16(al1, b1[k], d1);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    float x = acc[k][mt][v];
+                    float x = ODD ? acc1[k][mt][v] : acc[k][mt][v];
                     if constexpr (Q82) {
                         (void)xs0;
                         (void)xs1;
@@ -488,7 +490,8 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                         x = fmaf(b[k].x, xs0[v], x);
                         x = fmaf(b[k].y, xs1[v], x);
                     }
-                    acc[k][mt][v] = x;
+                    if constexpr (ODD) acc1[k][mt][v] = x;
+                    else acc[k][mt][v] = x;
                 }
             }
         }
@@ -537,6 +540,17 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
         }
     }
 
+    if constexpr (!Q4) {  // the odd steps' sums: column n held row n ^ 8 (all lanes take part)
+#pragma unroll
+        for (int k = 0; k < T; ++k)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float o = acc1[k][mt][v];  // a copy: bit_cast of a vector element read element 0
+                    acc[k][mt][v] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, o), 0x128, 0xF, 0xF, false));
+                }
+    }
     // Output element v of tile (k, mt): entry 16 mt + 4 g + v, weight row
     // rb * R + (wave T + k) * 16 + i16.
 #pragma unroll
@@ -620,7 +634,7 @@ __global__ __launch_bounds__(exp_threads<FMT>(), 1) void expert_bank_kernel(Expe
             const int r = min(rb * kRows + (wave * T + k) * 16 + i16, P.rows - 1);
             const int r8 = rb * kRows + (wave * T + k) * 16 + (i16 & 7);
             t.vq[k] = Q4 ? r * (P.cols >> 1) + 16 * g : min(r8, P.rows - 1) * P.cols + 64 * (i16 >> 3) + 16 * g;
-            t.vb[k] = Q4 ? 0 : min(r8 + 8, P.rows - 1) * P.cols + 64 * (i16 >> 3) + 16 * g;
+            t.vb[k] = Q4 ? 0 : min(r8 + 8, P.rows - 1) * P.cols + 64 * (1 - (i16 >> 3)) + 16 * g;
             t.vs[k] = (r * nb + V * g) * 4;
             t.row[k] = r;
         }
