@@ -468,6 +468,14 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
             const f32x4 xs1 = *reinterpret_cast<const f32x4 *>(xs + 16 * MT);
 #pragma unroll
             for (int k = 0; k < T; ++k) {
+                if constexpr (Q82) {  // no block factors: one chain through the accumulator
+                    f32x4 &A = ODD ? acc1[k][mt] : acc[k][mt];
+                    A = mfma16(ah0, b0[k], A);
+                    A = mfma16(al0, b0[k], A);
+                    A = mfma16(ah1, b1[k], A);
+                    A = mfma16(al1, b1[k], A);
+                    continue;
+                }
                 // q4tp: the chains start from the staged block sums (times -136)
                 f32x4 d0 = mfma16(ah0, b0[k], Q4 ? xs0 : z);
                 d0 = mfma16(al0, b0[k], d0);
@@ -476,12 +484,7 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float x = ODD ? acc1[k][mt][v] : acc[k][mt][v];
-                    if constexpr (Q82) {
-                        (void)xs0;
-                        (void)xs1;
-                        x += d0[v];
-                        x += d1[v];
-                    } else if constexpr (Q4) {
+                    if constexpr (Q4) {
                         x = fmaf(s[k].x, d0[v], x);
                         x = fmaf(s[k].y, d1[v], x);
                     } else {
