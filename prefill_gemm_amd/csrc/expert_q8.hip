@@ -24,7 +24,9 @@
 //    128 + n (one and-or for two), which the block term corrects;
 //  - A operand = the entries' activations as bf16 hi + lo (two products, exact
 //    to about 2^-17), staged once per workgroup in LDS from the f32 rows,
-//    together with the f32 block sums that the bias multiplies.
+//    together with the f32 block sums that the bias multiplies (the block
+//    format's bias term runs once a window of 2 D blocks, block sums times
+//    biases on the f32 matrix cores).
 // Each wave owns kExpTiles tiles of 16 weight rows over all columns, with
 // kExpDepth steps of weights in flight, requested kExpBurst at a time (a
 // burst reads 512 contiguous bytes of each of its 16 rows, which HBM serves
@@ -121,6 +123,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t exp_rsrc(const void *p, int by
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 a, const bf16x8 b, const f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_f32(float a, float b, const f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Eight int8 (two dwords, column order) as a bf16x8 operand; integers in
@@ -415,14 +420,12 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
         constexpr bool ODD = !Q4 && (u & 1);  // this step's column n holds row n ^ 8
         const int src = ((ODD ? i16 ^ 8 : i16) + 16 * gs) * 4;
         const int bl = 2 * p - cb0;
-        f32x2 s[T], b[T];
+        f32x2 s[T];
         bf16x8 b0[T], b1[T];
 #pragma unroll
         for (int k = 0; k < T; ++k) {
             s[k].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[k][ev])));
             s[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, sw[k][ev + 1])));
-            b[k].x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev])));
-            b[k].y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, bw[k][ev + 1])));
             // Lanes 0-31 hold block 2p, lanes 32-63 block 2p + 1; after the
             // exchange operand 0 carries block 2p on every lane, operand 1 block 2p + 1.
             if constexpr (Q4) {
@@ -484,15 +487,8 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float x = ODD ? acc1[k][mt][v] : acc[k][mt][v];
-                    if constexpr (Q4) {
-                        x = fmaf(s[k].x, d0[v], x);
-                        x = fmaf(s[k].y, d1[v], x);
-                    } else {
-                        x = fmaf(s[k].x, d0[v], x);
-                        x = fmaf(s[k].y, d1[v], x);
-                        x = fmaf(b[k].x, xs0[v], x);
-                        x = fmaf(b[k].y, xs1[v], x);
-                    }
+                    x = fmaf(s[k].x, d0[v], x);
+                    x = fmaf(s[k].y, d1[v], x);
                     if constexpr (ODD) acc1[k][mt][v] = x;
                     else acc[k][mt][v] = x;
                 }
@@ -522,6 +518,23 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
                         sw[k][j] = swn[k][j];
                         bw[k][j] = bwn[k][j];
                     }
+                }
+            }
+            if constexpr (!Q4 && !Q82) {
+                // The window's bias term, sum over its 2 D blocks of bias x block
+                // sum, on the f32 matrix cores: lane group g holds the biases of
+                // blocks V g .. V g + V - 1 of its row (the B operand as loaded)
+                // and reads the matching block sums of entry 16 mt + i16.
+                const float *xw = reinterpret_cast<const float *>(lds + xs_off) + (2 * (p0 - c0) + V * g) * 16 * MT + i16;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    float a[V];
+#pragma unroll
+                    for (int j = 0; j < V; ++j) a[j] = xw[j * 16 * MT + 16 * mt];
+#pragma unroll
+                    for (int k = 0; k < T; ++k)
+#pragma unroll
+                        for (int j = 0; j < V; ++j) acc[k][mt] = mfma16_f32(a[j], bw[k][j], acc[k][mt]);
                 }
             }
             const bool last = p0 + D >= npp;
