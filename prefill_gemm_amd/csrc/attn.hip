@@ -13,7 +13,8 @@
 // forms their scores and p . V on the matrix cores in f32
 // (v_mfma_f32_16x16x4f32: products and sums in f32, as the pages' arithmetic),
 // and keeps an online softmax per query (running max m and sum l) on the vector
-// ALU in between.  A split writes (m, l, acc) per query; the merge kernel
+// ALU in between.  q enters scaled by scale * log2 e, so the scores are in
+// base-2 units and every softmax weight is one hardware exp2 (v_exp_f32).  A split writes (m, l, acc) per query; the merge kernel
 // rescales the splits to a common maximum and adds them in split order.
 #include <stdint.h>
 
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
 
     // A fragments of q . k: query 16 wave + r16 (position b0 + i / rep, head g rep + i % rep), scaled.
     f32x4 qf[NC];
+    const float sl = scale * 1.44269504088896341f;  // base-2 scores: exp(x) = exp2(x log2 e)
     {
         const int i = kAttnQW * wave + r16;
         const int b = b0 + i / rep, h = g * rep + i % rep;
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
         for (int c = 0; c < NC; ++c) {
             float4 v = make_float4(0, 0, 0, 0);
             if (b < n) v = *reinterpret_cast<const float4 *>(q + ((long long)b * nh + h) * HD + 16 * c + 4 * kg);
-            qf[c] = f32x4{v.x * scale, v.y * scale, v.z * scale, v.w * scale};
+            qf[c] = f32x4{v.x * sl, v.y * sl, v.z * sl, v.w * sl};
         }
     }
     // The lane's D rows: queries 16 wave + 4 kg + v; their key limits.
@@ -186,11 +188,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
                 mx = fmaxf(mx, s[kb]);
             }
             const float mn = fmaxf(m[v], row16_reduce<true>(mx));
-            const float al = expf(m[v] - mn);
+            const float al = __builtin_amdgcn_exp2f(m[v] - mn);
             float ps = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const float p = s[kb] == -INFINITY ? 0.0f : expf(s[kb] - mn);
+                const float p = s[kb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[kb] - mn);
                 ps += p;
                 pw[(4 * kg + v) * C::kPStride + 16 * kb + r16] = p;
             }
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_merge_kernel(const float *_
     const float ms = mine ? p0[lane * stride + HD] : kAttnNoMax;
     const float ls = mine ? p0[lane * stride + HD + 1] : 0.0f;
     const float mx = wave_max(ms);
-    const float f = mine ? expf(ms - mx) : 0.0f;  // split `lane`'s factor
+    const float f = mine ? __builtin_amdgcn_exp2f(ms - mx) : 0.0f;  // split `lane`'s factor
     float den = 0.0f, num[DL];
 #pragma unroll
     for (int e = 0; e < DL; ++e) num[e] = 0.0f;
