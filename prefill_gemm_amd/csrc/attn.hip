@@ -178,28 +178,43 @@ __global__ __launch_bounds__(kAttnThreads) void attn_prefill_kernel(
         }
         __syncthreads();  // every wave is done with K: its space takes p
         // Online softmax per row; masked keys weigh exactly 0.  Sums stay per lane.
+        // The reference maximum m moves only when a row's tile maximum exceeds it
+        // by more than 8 (weights up to 2^8), so most tiles rescale nothing.
+        float s[4][NKB], mxr[4];
+        bool need = false;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float s[NKB], mx = -INFINITY;
+            float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const int j = t0 + 16 * kb + r16;
-                s[kb] = (j < j1 && j <= lim[v]) ? sc[kb][v] : -INFINITY;
-                mx = fmaxf(mx, s[kb]);
+                s[v][kb] = (j < j1 && j <= lim[v]) ? sc[kb][v] : -INFINITY;
+                mx = fmaxf(mx, s[v][kb]);
             }
-            const float mn = fmaxf(m[v], row16_reduce<true>(mx));
-            const float al = __builtin_amdgcn_exp2f(m[v] - mn);
+            mxr[v] = row16_reduce<true>(mx);
+            need |= mxr[v] > m[v] + 8.0f;
+        }
+        if (__ballot(need)) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float mn = fmaxf(m[v], mxr[v]);
+                const float al = __builtin_amdgcn_exp2f(m[v] - mn);
+                l[v] *= al;
+                m[v] = mn;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) o[c][v] *= al;
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
             float ps = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const float p = s[kb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[kb] - mn);
+                const float p = s[v][kb] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s[v][kb] - m[v]);
                 ps += p;
                 pw[(4 * kg + v) * C::kPStride + 16 * kb + r16] = p;
             }
-            l[v] = l[v] * al + ps;
-            m[v] = mn;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) o[c][v] *= al;
+            l[v] += ps;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's p writes land before its reads (lgkmcnt 0)
         __builtin_amdgcn_wave_barrier();
