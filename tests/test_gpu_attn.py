@@ -52,6 +52,30 @@ def test_attn_parity(pg, oracle, n, pos0, nh, nkv, hd):
     assert err <= TOL_ATTN
 
 
+def test_attn_rising_and_jumping_scores(pg, oracle):
+    """Scores that climb in a sawtooth over the context (up by about 6 in base-2 units a 64-key
+    tile, falling back every 320 keys) and jump by about 17 at one key: each split's running
+    maximum moves by steps below and above the softmax's rescaling threshold, and the merge
+    meets splits of different maxima.  q has one nonzero dim, so the f32 scores carry no
+    long sums and the test measures the softmax, not the scores' rounding."""
+    _case("attn rising and jumping scores")
+    n, pos0 = 64, 4032
+    c = synth.attn_pass(17, n, pos0)
+    j = np.arange(pos0 + n)
+    saw = (18.0 * ((j % 320) / 320.0)).astype(np.float32)   # scores rise by 16 over 320 keys
+    c["kc"][:pos0, :, 0] += saw[:pos0, None]
+    c["k"][:, :, 0] += saw[pos0:, None]
+    c["kc"][2000, :, 0] += 13.5
+    c["q"][:] = 0.0
+    c["q"][:, :, 0] = 10.0
+    o, kc, vc = _run(pg, c)
+    kc_ref, vc_ref = oracle.kv_append(c["kc"], c["vc"], c["k"], c["v"], pos0)
+    ref = oracle.attn_prefill(c["q"], kc_ref, vc_ref, pos0, c["scale"])
+    err = oracle.rel_err(o, ref)
+    print(f"[info] rel err {err:.2e}", flush=True)
+    assert err <= TOL_ATTN
+
+
 def test_attn_closed_forms(pg, oracle):
     """The first position of a first pass sees only its own key: o = its v.  A zero query
     weighs all visible keys equally: o is the mean of their v rows."""
