@@ -355,9 +355,10 @@ __device__ __forceinline__ void exp_item(const ExpertBank &P, int e, int m0, int
         }
     };
     // Scales and biases come a window of D steps (2D blocks) at a time: lane
-    // group g holds blocks V g .. V g + V - 1 of the window for its row, and
-    // a step takes its two blocks from the group that holds them (a lane
-    // permute), so that the four lanes of a row do not each load them.
+    // group g holds blocks V g .. V g + V - 1 of the window for its row; a
+    // step takes its two blocks' scales from the group that holds them (a lane
+    // permute), so that the four lanes of a row do not each load them, and the
+    // biases serve the window's bias term where they lie.
     auto load_win = [&](const ExpTgt &t, int w) __attribute__((always_inline)) {
         if constexpr (Q4) {
 #pragma unroll
