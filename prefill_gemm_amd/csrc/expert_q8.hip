@@ -29,7 +29,7 @@
 //    biases on the f32 matrix cores).
 // Each wave owns kExpTiles tiles of 16 weight rows over all columns, with
 // kExpDepth steps of weights in flight, requested kExpBurst at a time (a
-// burst reads 512 contiguous bytes of each of its 16 rows, which HBM serves
+// burst reads 256 contiguous bytes of each of its 16 rows, which HBM serves
 // better than the same bytes spread over single steps); the block scales
 // and biases arrive a window of steps at a time, spread over the four lanes
 // of a row.  When the
@@ -55,7 +55,7 @@ constexpr int kExpWaves = kExpThreads / kWave;
 template <int FMT>
 constexpr int exp_threads() { return FMT == 2 ? 768 : kExpThreads; }  // 2: kExpQ4
 constexpr int kExpDepth = 16;
-constexpr int kExpBurst = 8;   // ring slots refilled together
+constexpr int kExpBurst = 4;   // ring slots refilled together
 constexpr int kExpTiles = 1;                    // 16-row weight tiles per wave
 constexpr int kExpGroup = 16;                // entries per pass over an item
 constexpr int kExpLds = (148 * 1024);
